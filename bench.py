@@ -1,0 +1,340 @@
+"""Throughput of the InfLLM v2 block-sparse attention path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload N]
+
+Default workload (2): the final 8192-query chunk of a 131072-token context
+(bf16, 32 query heads / 2 KV heads, d=128, 64-token blocks, 32/16 kernels,
+top-64, dense_len 8192) -- the long-context prefill the pages quote 128K
+throughput for.  One step = compress the windows this chunk completes ->
+block scores -> top-k -> sparse attention, i.e. every stage of the path.
+Other workloads (for reports): 1 = 32K decode, 3 = 128K tree verification
+with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode.
+
+Prints one JSON line: tokens/s over K timed steps, per-stage times from HIP
+events recorded on the library's stream, the dominant kernel's roofline
+fraction, and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "InfLLMv2 attn tokens/s at 128K (decode, prefill); % of HBM/MFMA roofline"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0           # MI355X HBM3E peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def _n_windows(n, ks, s):
+    return 0 if n < ks else (n - ks) // s + 1
+
+
+def _visible_selected_keys(pos, p, n_sel_blocks):
+    """Keys attended by a sparse query at `pos` that keeps n_sel_blocks blocks,
+    its own (partial) block among them: full blocks + the own block's prefix."""
+    B = p.block_size
+    return (n_sel_blocks - 1) * B + (pos % B) + 1
+
+
+def _kernel_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel_name, src_file):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
+    were taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_sha") != _kernel_sha(src_file):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------
+class Workload:
+    """Builds inputs on the GPU and exposes step() plus algorithmic work."""
+
+    def __init__(self, wid, torch, seed=0):
+        from block_sparse_long_infllmv2_amd import binding as B
+        from block_sparse_long_infllmv2_amd import pipeline as PL
+        from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, config
+        self.torch, self.B, self.PL = torch, B, PL
+        self.wid = wid
+        dev = torch.device("cuda:0")
+        self.dev = dev
+        if wid == 5:
+            self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
+            self.name = "decode_bf16_128k"
+        else:
+            self.case = config(wid, seed=seed)
+            self.name = CONFIG_NAMES[wid]
+        c = self.case
+        p = c.params
+        self.p = p
+        bf = torch.bfloat16
+        up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, bf)
+        if wid == 2:
+            self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
+            h_kv, n_k, d = c.k.shape
+            self.plan = PL.PrefillPlan(c.n_q, n_k, c.q.shape[1], h_kv, d, bf, p, device=dev)
+            nc = _n_windows(n_k, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((h_kv, nc, d), dtype=bf, device=dev)
+            # compressed keys of the context before this chunk already exist
+            self.plan.compress(self.k, self.ck, m_begin=0)
+            torch.cuda.synchronize()
+            self.tokens = c.n_q
+            self.kind = "prefill"
+        elif wid in (1, 4, 5):
+            lens = np.asarray(c.seqlens)
+            bsz = len(lens)
+            h_kv, _, d = c.k[0].shape
+            cap = int(((lens.max() + 63) // 64) * 64)
+            self.k = torch.zeros((bsz, h_kv, cap, d), dtype=bf, device=dev)
+            self.v = torch.zeros_like(self.k)
+            for i, L in enumerate(lens):
+                self.k[i, :, :L] = up(c.k[i])
+                self.v[i, :, :L] = up(c.v[i])
+            self.q = up(c.q)
+            self.seqlens = torch.from_numpy(lens.astype(np.int32)).to(dev)
+            nc = _n_windows(cap, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((bsz, h_kv, nc, d), dtype=bf, device=dev)
+            B.infllmv2_compress_keys(self.k, self.seqlens, 0, nc, self.ck, p)
+            self.plan = PL.DecodePlan(bsz, int(lens.max()), c.q.shape[1], h_kv, d, bf, p,
+                                      device=dev)
+            torch.cuda.synchronize()
+            self.tokens = bsz
+            self.kind = "decode"
+        elif wid == 3:
+            self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
+            self.kd, self.vd = up(c.k_draft), up(c.v_draft)
+            self.mask = torch.from_numpy(c.mask.astype(np.int64)).to(dev)
+            h_kv, n_ctx, d = c.k.shape
+            nc = _n_windows(n_ctx, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((h_kv, nc, d), dtype=bf, device=dev)
+            B.infllmv2_compress_keys(self.k.unsqueeze(0),
+                                     torch.tensor([n_ctx], dtype=torch.int32, device=dev), 0,
+                                     nc, self.ck.unsqueeze(0), p)
+            self.plan = PL.TreePlan(c.q.shape[0], n_ctx, c.q.shape[1], h_kv, d, bf, p,
+                                    device=dev)
+            torch.cuda.synchronize()
+            self.tokens = c.q.shape[0]
+            self.kind = "tree"
+        else:
+            raise SystemExit(f"workload {wid} is a parity case, not a bench workload")
+
+    # one step, with optional per-stage event recording
+    def step(self, ev=None):
+        def mark(name):
+            if ev is not None:
+                e = self.torch.cuda.Event(enable_timing=True)
+                e.record()
+                ev.append((name, e))
+        pl = self.plan
+        if self.kind == "prefill":
+            mark("start")
+            pl.compress(self.k, self.ck)
+            mark("compress_keys")
+            pl.select(self.q, self.ck)      # block_scores + select_topk
+            mark("scores_topk")
+            pl.attend(self.q, self.k, self.v)
+            mark("sparse_attn_prefill")
+        elif self.kind == "decode":
+            mark("start")
+            pl.select(self.q, self.ck, self.seqlens)
+            mark("scores_topk")
+            pl.attend(self.q, self.k, self.v, self.seqlens)
+            mark("sparse_attn_decode")
+        else:
+            mark("start")
+            pl.select(self.q, self.ck)
+            mark("scores_topk")
+            pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
+            mark("tree_verify")
+
+    # ---- algorithmic work (what the method must touch / compute) ----------
+    def work(self):
+        c, p = self.case, self.p
+        if self.kind == "prefill":
+            h_kv, n_k, d = c.k.shape
+            h_q = c.q.shape[1]
+            pos = np.arange(n_k - c.n_q, n_k)
+            keys = sum(_visible_selected_keys(int(x), p, p.topk) for x in pos)
+            attn_flop = 4.0 * d * h_q * keys
+            nvis = np.array([_n_windows(int(x) + 1, p.kernel_size, p.kernel_stride)
+                             for x in pos])
+            score_flop = 2.0 * d * h_kv * float(nvis.sum())
+            return {"dominant": "sparse_attn_prefill", "bound": "mfma",
+                    "flop": attn_flop, "score_flop": score_flop,
+                    "src": "attn_bf16.hip"}
+        d = c.q.shape[2]
+        h_q = c.q.shape[1]
+        if self.kind == "decode":
+            total = 0.0
+            for L in c.seqlens:
+                L = int(L)
+                h_kv = c.k[0].shape[0]
+                if L < p.dense_len:
+                    kv = h_kv * L * d * 2 * 2
+                    ckb = 0
+                else:
+                    kv = h_kv * _visible_selected_keys(L - 1, p, p.topk) * d * 2 * 2
+                    ckb = h_kv * _n_windows(L, p.kernel_size, p.kernel_stride) * d * 2
+                total += kv + ckb + h_q * d * 2 * 2
+            return {"dominant": "sparse_attn_decode", "bound": "hbm", "bytes": total,
+                    "src": "attn_bf16.hip"}
+        # tree: CK once + union of kept blocks per KV head + drafts + Q/O
+        h_kv, n_ctx, _ = c.k.shape
+        sel = self.plan.block_idx.cpu().numpy()
+        union = sum(len(np.unique(sel[:, g][sel[:, g] >= 0])) for g in range(h_kv))
+        T = c.q.shape[0]
+        total = (h_kv * _n_windows(n_ctx, p.kernel_size, p.kernel_stride) * d * 2 +
+                 union * p.block_size * d * 2 * 2 + T * h_q * d * 2 * 2 +
+                 2 * h_kv * T * d * 2 + T * 8)
+        return {"dominant": "tree_verify", "bound": "hbm", "bytes": float(total),
+                "union_blocks": int(union), "src": "attn_bf16.hip"}
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """The CPU oracle as it stands, single-threaded, on a bounded sample."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    c, p = wl.case, wl.p
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        if wl.kind == "prefill":
+            ck = O.compress_keys(c.k, p, "bf16")
+            rows, i = [], 0
+            step = max(1, c.n_q // 256)
+            while time.perf_counter() - t0 < budget_s and i < c.n_q:
+                O.prefill(c.q, c.k, c.v, p, "bf16", rows=[i], ck=ck)
+                rows.append(i)
+                i += step
+            dt = time.perf_counter() - t0
+            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{len(rows)} of {c.n_q} chunk queries (every {step}th) incl. "
+                              f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
+        if wl.kind == "decode":
+            n = 0
+            while time.perf_counter() - t0 < budget_s and n < len(c.seqlens):
+                O.decode(c.q[n:n + 1], [c.k[n]], [c.v[n]], [c.seqlens[n]], p, "bf16")
+                n += 1
+            dt = time.perf_counter() - t0
+            return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{n} of {len(c.seqlens)} sequences, float64 numpy, 1 thread"}
+        T = c.q.shape[0]
+        n = 0
+        ck = O.compress_keys(c.k, p, "bf16")
+        while time.perf_counter() - t0 < budget_s and n < T:
+            O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, "bf16", ck=ck,
+                          drafts=[n])
+            n += 1
+        dt = time.perf_counter() - t0
+        return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"{n} of {T} drafts, float64 numpy, 1 thread"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path is "
+              "single-GPU and sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = Workload(args.workload, torch)
+    print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+
+    evs = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = []
+        wl.step(ev)
+        evs.append(ev)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    print(f"[bench] {args.steps} steps in {wall:.4f} s", file=sys.stderr, flush=True)
+
+    stages = {}
+    for ev in evs:
+        for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:]):
+            stages.setdefault(n1, []).append(e0.elapsed_time(e1))
+    stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.tokens / (ms_per_step / 1e3)
+
+    w = wl.work()
+    dom = w["dominant"]
+    dom_ms = stage_ms[dom]
+    src = os.path.join(ROOT, "block_sparse_long_infllmv2_amd", "csrc", w["src"])
+    if w["bound"] == "mfma":
+        achieved = w["flop"] / (dom_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": _traffic(dom, src), "kernel": dom,
+                "algorithmic_gflop_per_launch": round(w["flop"] / 1e9, 2),
+                "kernel_ms": round(dom_ms, 4)}
+    else:
+        achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "traffic": _traffic(dom, src), "kernel": dom,
+                "algorithmic_mb_per_launch": round(w["bytes"] / 1e6, 3),
+                "kernel_ms": round(dom_ms, 4)}
+
+    cfg = {"workload": wl.name}
+    c = wl.case
+    if wl.kind == "prefill":
+        cfg.update({"context": int(c.k.shape[1]), "chunk_queries": int(c.n_q)})
+    elif wl.kind == "decode":
+        cfg.update({"batch": int(len(c.seqlens)), "seqlens": [int(x) for x in c.seqlens]})
+    else:
+        cfg.update({"context": int(c.k.shape[1]), "drafts": int(c.q.shape[0])})
+    cfg.update({"h_q": int(c.q.shape[1]), "h_kv": 2, "head_dim": int(c.q.shape[2]),
+                "block_size": wl.p.block_size, "kernel_size": wl.p.kernel_size,
+                "kernel_stride": wl.p.kernel_stride, "topk": wl.p.topk,
+                "init_blocks": wl.p.init_blocks, "local_blocks": wl.p.local_blocks,
+                "dense_len": wl.p.dense_len})
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": cfg, "roofline": roof,
+           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+    if w["bound"] == "mfma":
+        out["scoring_gflop"] = round(w["score_flop"] / 1e9, 2)
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

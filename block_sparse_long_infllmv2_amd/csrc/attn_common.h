@@ -1,0 +1,44 @@
+// Arguments shared by the attention kernels (bf16 matrix-core path and the
+// float32 vector path) and the host launchers.
+#pragma once
+
+#include "device_common.h"
+#include "host_common.h"
+
+namespace infllmv2 {
+
+enum Mode { kPrefill = 0, kDecode = 1, kTree = 2 };
+
+constexpr int kChunk = 64;                  // keys per staged unit
+constexpr int kSortCap = 128;               // max topk handled by the union sort
+constexpr int kEmptyBlock = 0x7fffffff;
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* block_idx;   // [rows][h_kv][topk] or NULL (dense)
+  const uint16_t* k_draft;    // tree: [h_kv][n_draft][D]
+  const uint16_t* v_draft;
+  const uint64_t* tree_mask;  // tree: [n_draft]
+  const int32_t* seqlens;     // decode: [batch]
+  const int32_t* union_blk;   // tree: [h_kv][union_cap] (from the planner)
+  const uint64_t* union_mask; // tree: [h_kv][union_cap], bit = draft index
+  const int32_t* union_len;   // tree: [h_kv]
+  uint16_t* out;
+  float* lse;
+  float* ws;                  // split partials [rows][h_q][n_split][D+2]
+  int64_t cap;                // tokens per (sequence, KV head) in the cache
+  int64_t n_k;                // prefill: keys; tree: context length
+  int n_rows;                 // prefill: n_q; decode: batch; tree: n_draft
+  int h_q, h_kv, topk, B, dense_len, n_split, entries_per_split, n_tiles, union_cap;
+  float scale_log2;           // softmax scale * log2(e)
+};
+
+
+// float32 (vector ALU) attention: exact-precision path for float32 inputs.
+int prefill_f32(const AttnArgs& a, int d, hipStream_t st);
+int decode_f32(const AttnArgs& a, int d, hipStream_t st);
+int tree_f32(const AttnArgs& a, int d, hipStream_t st);
+
+}  // namespace infllmv2

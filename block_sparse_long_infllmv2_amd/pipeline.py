@@ -1,0 +1,150 @@
+"""Pre-planned call sequences over the C ABI: chunked prefill, ragged decode
+and tree verification.
+
+A plan allocates (through torch, once) every buffer a step needs -- positions,
+block scores, selections, workspaces, outputs -- and `run` issues the library
+calls on the current stream.  The plans perform no arithmetic of their own.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+def _windows(n: int, ks: int, s: int) -> int:
+    return 0 if n < ks else (n - ks) // s + 1
+
+
+class PrefillPlan:
+    """The final n_q queries of an n_k-token sequence (chunked prefill).
+
+    Calls: compress_keys (windows completed by this chunk) -> block_scores ->
+    select_topk -> sparse_attn_prefill.  Dense (n_k < dense_len): attention only.
+    """
+
+    def __init__(self, n_q, n_k, h_q, h_kv, d, dtype, params, device="cuda"):
+        self.p = B.to_params(params)
+        self.n_q, self.n_k, self.h_q, self.h_kv, self.d = n_q, n_k, h_q, h_kv, d
+        self.dtype = dtype
+        self.dense = n_k < self.p.dense_len
+        self.nb = (n_k + self.p.block_size - 1) // self.p.block_size
+        dev = torch.device(device)
+        self.seqlens = torch.tensor([n_k], dtype=torch.int32, device=dev)
+        self.row_pos = torch.arange(n_k - n_q, n_k, dtype=torch.int32, device=dev)
+        self.scores = None if self.dense else torch.empty(
+            (n_q, h_kv, self.nb), dtype=torch.float32, device=dev)
+        self.block_idx = None if self.dense else torch.empty(
+            (n_q, h_kv, self.p.topk), dtype=torch.int32, device=dev)
+        self.out = torch.empty((n_q, h_q, d), dtype=dtype, device=dev)
+        self.lse = torch.empty((n_q, h_q), dtype=torch.float32, device=dev)
+        # windows completed by this chunk: all windows not complete before it
+        self.m_begin = _windows(n_k - n_q, self.p.kernel_size, self.p.kernel_stride)
+        self.m_end = _windows(n_k, self.p.kernel_size, self.p.kernel_stride)
+
+    def compress(self, k_cache, ck_cache, m_begin=None):
+        """k_cache [h_kv][cap][d] -> ck_cache [h_kv][nc_cap][d], windows
+        [m_begin, m_end)."""
+        mb = self.m_begin if m_begin is None else m_begin
+        B.infllmv2_compress_keys(k_cache.unsqueeze(0), self.seqlens, mb, self.m_end,
+                                 ck_cache.unsqueeze(0), self.p)
+
+    def select(self, q, ck_cache):
+        B.infllmv2_block_scores(q, None, self.row_pos, ck_cache.unsqueeze(0), self.seqlens,
+                                self.scores, self.n_k - 1, self.p)
+        B.infllmv2_select_topk(self.scores, None, self.row_pos, self.seqlens, self.block_idx,
+                               self.p)
+
+    def attend(self, q, k_cache, v_cache):
+        B.infllmv2_sparse_attn_prefill(q, k_cache, v_cache, self.n_k, self.block_idx, self.out,
+                                       self.lse, self.p)
+
+    def run(self, q, k_cache, v_cache, ck_cache, m_begin=None):
+        if not self.dense:
+            self.compress(k_cache, ck_cache, m_begin)
+            self.select(q, ck_cache)
+        self.attend(q, k_cache, v_cache)
+        return self.out
+
+
+class DecodePlan:
+    """One new query per sequence of a ragged batch (its K/V already cached).
+
+    Calls: block_scores -> select_topk -> sparse_attn_decode (split-KV +
+    combine).  Compressed keys are assumed current (append windows with
+    compress_keys as the caches grow).
+    """
+
+    def __init__(self, batch, max_seqlen, h_q, h_kv, d, dtype, params, device="cuda"):
+        self.p = B.to_params(params)
+        self.batch, self.max_seqlen = batch, max_seqlen
+        self.h_q, self.h_kv, self.d, self.dtype = h_q, h_kv, d, dtype
+        dev = torch.device(device)
+        self.nb = (max_seqlen + self.p.block_size - 1) // self.p.block_size
+        self.row_seq = torch.arange(batch, dtype=torch.int32, device=dev)
+        self.scores = torch.empty((batch, h_kv, self.nb), dtype=torch.float32, device=dev)
+        self.block_idx = torch.empty((batch, h_kv, self.p.topk), dtype=torch.int32, device=dev)
+        ws = B.infllmv2_workspace_size(B.OP_DECODE, batch, h_q, h_kv, d, max_seqlen, self.p)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((batch, h_q, d), dtype=dtype, device=dev)
+        self.lse = torch.empty((batch, h_q), dtype=torch.float32, device=dev)
+
+    def select(self, q, ck_cache, seqlens):
+        if self.max_seqlen < self.p.dense_len:
+            return
+        B.infllmv2_block_scores(q, self.row_seq, None, ck_cache, seqlens, self.scores,
+                                self.max_seqlen - 1, self.p)
+        B.infllmv2_select_topk(self.scores, self.row_seq, None, seqlens, self.block_idx,
+                               self.p)
+
+    def attend(self, q, k_cache, v_cache, seqlens):
+        B.infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, self.max_seqlen,
+                                      self.block_idx, self.out, self.lse, self.ws, self.p)
+
+    def run(self, q, k_cache, v_cache, ck_cache, seqlens):
+        self.select(q, ck_cache, seqlens)
+        self.attend(q, k_cache, v_cache, seqlens)
+        return self.out
+
+
+class TreePlan:
+    """n_draft tree-shaped draft tokens after an n_ctx-token context.
+
+    Calls: block_scores (every draft at the context's last position) ->
+    select_topk -> tree_verify (union planner, split-KV, combine).
+    """
+
+    def __init__(self, n_draft, n_ctx, h_q, h_kv, d, dtype, params, device="cuda"):
+        self.p = B.to_params(params)
+        self.n_draft, self.n_ctx = n_draft, n_ctx
+        self.h_q, self.h_kv, self.d, self.dtype = h_q, h_kv, d, dtype
+        self.dense = n_ctx < self.p.dense_len
+        dev = torch.device(device)
+        self.nb = (n_ctx + self.p.block_size - 1) // self.p.block_size
+        self.seqlens = torch.tensor([n_ctx], dtype=torch.int32, device=dev)
+        self.row_pos = torch.full((n_draft,), n_ctx - 1, dtype=torch.int32, device=dev)
+        self.scores = None if self.dense else torch.empty(
+            (n_draft, h_kv, self.nb), dtype=torch.float32, device=dev)
+        self.block_idx = None if self.dense else torch.empty(
+            (n_draft, h_kv, self.p.topk), dtype=torch.int32, device=dev)
+        ws = B.infllmv2_workspace_size(B.OP_TREE, n_draft, h_q, h_kv, d, n_ctx, self.p)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device=dev)
+        self.out = torch.empty((n_draft, h_q, d), dtype=dtype, device=dev)
+        self.lse = torch.empty((n_draft, h_q), dtype=torch.float32, device=dev)
+
+    def select(self, q, ck_cache):
+        if self.dense:
+            return
+        B.infllmv2_block_scores(q, None, self.row_pos, ck_cache.unsqueeze(0), self.seqlens,
+                                self.scores, self.n_ctx - 1, self.p)
+        B.infllmv2_select_topk(self.scores, None, self.row_pos, self.seqlens, self.block_idx,
+                               self.p)
+
+    def attend(self, q, k_cache, v_cache, k_draft, v_draft, tree_mask):
+        B.infllmv2_tree_verify(q, k_cache, v_cache, self.n_ctx, k_draft, v_draft, tree_mask,
+                               self.block_idx, self.out, self.lse, self.ws, self.p)
+
+    def run(self, q, k_cache, v_cache, ck_cache, k_draft, v_draft, tree_mask):
+        self.select(q, ck_cache)
+        self.attend(q, k_cache, v_cache, k_draft, v_draft, tree_mask)
+        return self.out

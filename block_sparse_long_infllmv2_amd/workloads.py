@@ -106,18 +106,25 @@ class TreeCase:
         return self.k.shape[1]
 
 
-def round_to_bf16(x: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bfloat16 value (ties to even), returned as float32."""
+def round_to_bf16(x: np.ndarray, inplace: bool = False) -> np.ndarray:
+    """float32 -> nearest bfloat16 value (ties to even), returned as float32.
+    Inputs are finite, so the 32-bit sum below cannot wrap."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    bits = x.view(np.uint32).astype(np.uint64)
-    bias = 0x7FFF + ((bits >> 16) & 1)
-    out = ((bits + bias) & 0xFFFF0000).astype(np.uint32)
-    return out.view(np.float32)
+    if not inplace:
+        x = x.copy()
+    bits = x.view(np.uint32)
+    tmp = bits >> np.uint32(16)
+    tmp &= np.uint32(1)
+    tmp += np.uint32(0x7FFF)
+    bits += tmp
+    bits &= np.uint32(0xFFFF0000)
+    return x
 
 
 def _to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
-    x = x.astype(np.float32, copy=False)
-    return round_to_bf16(x) if dtype == "bf16" else np.ascontiguousarray(x)
+    """Round a freshly drawn float32 array (owned here) to the dtype in place."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    return round_to_bf16(x, inplace=True) if dtype == "bf16" else x
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:

@@ -1,0 +1,244 @@
+/*
+ * infllmv2.h -- C ABI of an MI355X (gfx950) implementation of InfLLM v2
+ * trainable block-sparse attention.
+ *
+ * What the method computes (sources are web pages about CPM.cu / MiniCPM4):
+ *   - the KV context is split into fixed-size blocks of tokens (64 on the page
+ *     "MiniCPM 4.0 ..." (shadowrocket9.top), section on native sparsity /
+ *     InfLLM v2; 128 on "MiniCPM4: running LLMs on phones and PCs"
+ *     (xugj520.cn), section 1.1 and the CPM_cu class sketch in section 2.1);
+ *   - keys are compressed into parameter-free "semantic kernels": overlapping
+ *     32-token units with stride 16 (xugj520.cn, section 1.1);
+ *   - each query scores the kernels, the scores are pooled to blocks and the
+ *     query keeps its top-k blocks (top-64 on shadowrocket9.top, top-6 on
+ *     xugj520.cn), always including the initial tokens and a sliding local
+ *     window (xugj520.cn, section 1.1);
+ *   - attention then runs over the kept blocks only;
+ *   - contexts shorter than dense_len = 8192 use dense attention
+ *     (shadowrocket9.top, InfLLM v2 section; the sparse_config dict in its
+ *     deployment section holds topk / block_size / dense_len);
+ *   - the attention mask for tree speculative decoding is packed in uint64
+ *     words (xugj520.cn, section 1.1 technical notes; pomoai.com CPM.cu
+ *     article, section 2).
+ * Where the pages disagree (block 64 vs 128, top-64 vs top-6) the value is a
+ * run-time parameter.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are DEVICE pointers unless a comment says "host".  The caller
+ *     allocates and owns every buffer (inputs, outputs, workspaces); the
+ *     library never allocates, frees or synchronises, so every call can be
+ *     captured into a HIP graph.  Buffers must stay alive until the work
+ *     queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Work is queued asynchronously.  Arguments are validated on the host
+ *     before anything is launched; an invalid call returns a non-zero status
+ *     and queues nothing.  A failed launch returns INFLLMV2_ERR_HIP.  Faults
+ *     inside queued work surface at the caller's next synchronisation.
+ *   - Nothing aborts, throws or prints.  The library is stateless and
+ *     reentrant.
+ *   - dtype selects the element type of q, k, v, compressed keys and outputs:
+ *     INFLLMV2_F32 (float) or INFLLMV2_BF16 (bfloat16, stored as uint16).
+ *     Accumulation is float32 in both cases.
+ *   - Layouts (row-major, innermost last):
+ *       queries      q        [rows][h_q][d]
+ *       KV caches    k, v     [batch][h_kv][cap][d]   (batch = 1 for prefill
+ *                                                      and tree verification)
+ *       compressed   ck       [batch][h_kv][nc_cap][d] (dtype of k)
+ *       block scores scores   [rows][h_kv][nb_cap]  float32
+ *       selections   block_idx[rows][h_kv][topk]    int32, ascending, -1 pad
+ *       outputs      out      [rows][h_q][d]; lse [rows][h_q] float32 (ln)
+ *   - Query head h reads KV head floor(h * h_kv / h_q) (GQA groups of
+ *     G = h_q / h_kv consecutive heads).
+ *   - Supported: d in {64, 128}; h_q % h_kv == 0; for bf16 attention
+ *     G in {1, 2, 4, 8, 16, 32}; block_size a multiple of 32 up to 256;
+ *     kernel_stride <= kernel_size; 1 <= topk <= 128;
+ *     init_blocks + local_blocks <= topk; n_draft <= 64.
+ */
+#ifndef INFLLMV2_H
+#define INFLLMV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  INFLLMV2_OK = 0,
+  INFLLMV2_ERR_INVALID_ARG = 1,   /* NULL pointer, bad size, inconsistent args */
+  INFLLMV2_ERR_UNSUPPORTED = 2,   /* valid but outside the supported range    */
+  INFLLMV2_ERR_WORKSPACE = 3,     /* workspace missing or too small           */
+  INFLLMV2_ERR_HIP = 4            /* a kernel launch failed                   */
+} infllmv2_status;
+
+typedef enum { INFLLMV2_F32 = 0, INFLLMV2_BF16 = 1 } infllmv2_dtype;
+
+/* Sparse-attention parameters.  Names of topk / block_size / dense_len follow
+ * the sparse_config dict on shadowrocket9.top (deployment section). */
+typedef struct {
+  int32_t block_size;     /* B: tokens per KV block (default 64)                 */
+  int32_t kernel_size;    /* ks: tokens per semantic kernel (default 32)         */
+  int32_t kernel_stride;  /* s: token stride between kernels (default 16)        */
+  int32_t topk;           /* blocks kept per (query, KV head), forced ones
+                             included (default 64)                                */
+  int32_t init_blocks;    /* leading blocks always kept (default 1)              */
+  int32_t local_blocks;   /* the query's own block and the local_blocks-1 before
+                             it are always kept (default 2)                       */
+  int32_t dense_len;      /* a sequence with fewer than dense_len keys uses dense
+                             causal attention (default 8192)                      */
+  float scale;            /* softmax scale; 0 selects 1/sqrt(d)                  */
+} infllmv2_params;
+
+/* host: fill *p with the defaults 64 / 32 / 16 / 64 / 1 / 2 / 8192 / 0. */
+void infllmv2_default_params(infllmv2_params* p);
+
+/* host: static string for a status code (never NULL). */
+const char* infllmv2_status_string(int status);
+
+/* host: library ABI version (major * 100 + minor). */
+int infllmv2_version(void);
+
+/*
+ * Semantic-kernel key compression (xugj520.cn, section 1.1: 32-token units,
+ * stride 16, no parameters; pooling = arithmetic mean).
+ *
+ *   ck[b][g][m][:] = round_to_dtype( mean_{t = m*s .. m*s+ks-1} k[b][g][t][:] )
+ *
+ * for every sequence b < batch, KV head g < h_kv and window m in
+ * [m_begin, m_end) whose tokens all lie inside the sequence
+ * (m*s + ks <= seqlens[b]).  Other windows are left untouched, so a decode
+ * loop can append new windows as the cache grows.  Sum in float32, one
+ * rounding (to nearest, ties to even) to the storage dtype.
+ *   k        [batch][h_kv][cap][d]     seqlens  int32 [batch]
+ *   ck       [batch][h_kv][nc_cap][d]  requires m_end <= nc_cap and
+ *            (m_end-1)*s + ks <= cap.
+ */
+int infllmv2_compress_keys(int dtype, const void* k, int32_t batch, int32_t h_kv,
+                           int64_t cap, int32_t d, const int32_t* seqlens,
+                           int64_t m_begin, int64_t m_end, void* ck, int64_t nc_cap,
+                           const infllmv2_params* p, void* stream);
+
+/*
+ * Block relevance scores (xugj520.cn, section 1.1: each query is scored
+ * against semantic kernels, blocks are picked from them).  For query row r
+ * (sequence row_seq[r], absolute position row_pos[r]) and KV head g:
+ *
+ *   sigma[m] = scale * sum_{h in group g} q[r][h] . ck[seq][g][m]
+ *              for windows that end at or before row_pos[r]
+ *   scores[r][g][b] = max of sigma[m] over the visible windows m whose token
+ *              span overlaps block b, or -inf if there is none,
+ *
+ * written for the eligible blocks b = 0 .. floor(row_pos[r] / B); entries
+ * beyond are left untouched.  Rows whose sequence is dense
+ * (seqlens[seq] < dense_len) are skipped.
+ *   q        [rows][h_q][d]            row_seq int32 [rows] or NULL (all 0)
+ *   row_pos  int32 [rows], each < seqlens[row's sequence]; NULL means the
+ *            decode position seqlens[row's sequence] - 1
+ *   ck       [batch][h_kv][nc_cap][d]  holding every window visible to the rows
+ *   seqlens  int32 [batch]
+ *   scores   float32 [rows][h_kv][nb_cap], nb_cap >= floor(max_pos / B) + 1
+ *   max_pos  host: an upper bound of row_pos (sizes the launch)
+ */
+int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
+                          const int32_t* row_seq, const int32_t* row_pos,
+                          int32_t h_q, int32_t h_kv, int32_t d, const void* ck,
+                          int32_t batch, int64_t nc_cap, const int32_t* seqlens,
+                          float* scores, int64_t nb_cap, int32_t max_pos,
+                          const infllmv2_params* p, void* stream);
+
+/*
+ * Top-k block selection (shadowrocket9.top, InfLLM v2 section: top-k blocks
+ * per query; xugj520.cn, section 1.1: initial and sliding-window tokens are
+ * always kept).  For row r at position pos with own block b_r = pos / B:
+ *   eligible  E = {0 .. b_r}
+ *   forced    F = ({0 .. init_blocks-1} U {b_r-local_blocks+1 .. b_r}) n E
+ *   kept      F plus the best blocks of E \ F by (score descending, block
+ *             index ascending) until min(topk, |E|) blocks are kept.
+ * block_idx[r][g][:] receives the kept blocks in ascending order, padded with
+ * -1.  Rows whose sequence is dense receive -1 only.  row_seq / row_pos
+ * follow infllmv2_block_scores (NULL row_pos = decode positions).
+ *   scores   float32 [rows][h_kv][nb_cap] as written by infllmv2_block_scores
+ *   block_idx int32  [rows][h_kv][topk]
+ */
+int infllmv2_select_topk(const float* scores, int32_t rows, const int32_t* row_seq,
+                         const int32_t* row_pos, int32_t h_kv, int64_t nb_cap,
+                         const int32_t* seqlens, int32_t batch, int32_t* block_idx,
+                         const infllmv2_params* p, void* stream);
+
+/*
+ * Block-sparse causal attention for a prefill chunk (xugj520.cn, section 1.1:
+ * attention computed on the selected blocks only; pomoai.com, section 4:
+ * chunked prefill).  One sequence; query i sits at position n_k - n_q + i and
+ * attends the keys j <= its position inside its kept blocks.  If
+ * n_k < dense_len the attention is dense causal and block_idx is ignored (may
+ * be NULL); otherwise block_idx [n_q][h_kv][topk] is required.
+ *   q    [n_q][h_q][d]          k, v [h_kv][cap][d], n_k <= cap
+ *   out  [n_q][h_q][d] (dtype)  lse  float32 [n_q][h_q] natural log, or NULL
+ * No workspace.
+ */
+int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_q,
+                                 const void* k, const void* v, int64_t cap,
+                                 int64_t n_k, int32_t h_q, int32_t h_kv, int32_t d,
+                                 const int32_t* block_idx, void* out, float* lse,
+                                 const infllmv2_params* p, void* stream);
+
+/*
+ * Block-sparse decode attention, ragged batch (one new query per sequence,
+ * at position seqlens[b]-1, its own K/V already in the cache).  Each sequence
+ * is dense or sparse on its own length.  Split-KV: partial results go to the
+ * workspace and a second kernel merges them.
+ *   q    [batch][h_q][d]        k, v [batch][h_kv][cap][d]
+ *   seqlens int32 [batch], 1 <= seqlens[b] <= cap
+ *   max_seqlen host: upper bound of seqlens (sizes launch and workspace)
+ *   block_idx int32 [batch][h_kv][topk] (ignored for dense sequences; may be
+ *            NULL when max_seqlen < dense_len)
+ *   out  [batch][h_q][d]        lse float32 [batch][h_q] or NULL
+ *   ws   >= infllmv2_workspace_size(INFLLMV2_OP_DECODE, batch, h_q, h_kv, d,
+ *            max_seqlen, p) bytes, 256-byte aligned
+ */
+int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t batch,
+                                const void* k, const void* v, int64_t cap,
+                                const int32_t* seqlens, int32_t max_seqlen,
+                                int32_t h_q, int32_t h_kv, int32_t d,
+                                const int32_t* block_idx, void* out, float* lse,
+                                void* ws, size_t ws_bytes,
+                                const infllmv2_params* p, void* stream);
+
+/*
+ * Tree speculative verification (pomoai.com, section 2: tree verification in
+ * the attention kernel; xugj520.cn, section 1.1: uint64-packed mask for tree
+ * speculative decoding).  n_draft draft tokens follow an n_ctx-token context.
+ * Draft i keeps its own blocks (block_idx row i, selected over the context as
+ * seen from position n_ctx-1) and attends, in one softmax, the context keys of
+ * those blocks and every draft j whose bit j is set in tree_mask[i] (bit 0 =
+ * least significant).  A draft always attends itself; bits >= n_draft are
+ * ignored.  If n_ctx < dense_len the context part is dense.
+ *   q          [n_draft][h_q][d]       k, v [h_kv][cap][d] (context)
+ *   k_draft, v_draft [h_kv][n_draft][d] tree_mask uint64 [n_draft]
+ *   block_idx  int32 [n_draft][h_kv][topk] (may be NULL when dense)
+ *   out        [n_draft][h_q][d]       lse float32 [n_draft][h_q] or NULL
+ *   ws >= infllmv2_workspace_size(INFLLMV2_OP_TREE, n_draft, h_q, h_kv, d,
+ *         n_ctx, p) bytes, 256-byte aligned
+ */
+int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* k,
+                         const void* v, int64_t cap, int64_t n_ctx,
+                         const void* k_draft, const void* v_draft,
+                         const uint64_t* tree_mask, int32_t h_q, int32_t h_kv,
+                         int32_t d, const int32_t* block_idx, void* out, float* lse,
+                         void* ws, size_t ws_bytes, const infllmv2_params* p,
+                         void* stream);
+
+enum { INFLLMV2_OP_DECODE = 0, INFLLMV2_OP_TREE = 1 };
+
+/* host: workspace bytes needed by infllmv2_sparse_attn_decode (op DECODE,
+ * n = batch, max_len = max_seqlen) or infllmv2_tree_verify (op TREE,
+ * n = n_draft, max_len = n_ctx).  0 on invalid arguments. */
+size_t infllmv2_workspace_size(int op, int32_t n, int32_t h_q, int32_t h_kv,
+                               int32_t d, int64_t max_len, const infllmv2_params* p);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFLLMV2_H */

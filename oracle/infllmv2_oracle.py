@@ -58,7 +58,8 @@ import numpy as np
 __all__ = [
     "bf16_round", "store_round", "num_windows", "compress_keys",
     "windows_of_block", "kernel_scores", "block_scores", "select_blocks",
-    "attend", "dense_attend", "prefill", "decode", "tree_verify",
+    "attend", "attend_selected", "dense_attend", "forced_blocks", "prefill",
+    "decode", "tree_verify",
 ]
 
 
@@ -241,16 +242,17 @@ def dense_attend(q_row, k, v, pos: int, params):
 # --------------------------------------------------------------------------
 # Whole-path drivers
 # --------------------------------------------------------------------------
-def _sparse_row(q_row, k, v, ck, pos, params, extra=None):
-    """Steps 3-6 for one query token.  `extra` = (k_x, v_x) [h_kv][n][d]
-    additional keys attended densely (tree drafts)."""
+def attend_selected(q_row, k, v, sel, pos, params, extra=None):
+    """Step 6 for one query token given its kept blocks per KV head:
+    attention over the keys j <= pos of those blocks, plus `extra` =
+    (k_x, v_x) [h_kv][n][d] keys attended in the same softmax (tree drafts).
+    Returns (o [h_q][d], lse [h_q])."""
     q_row = np.asarray(q_row, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
     h_q, d = q_row.shape
     h_kv = k.shape[0]
     scale = _scale(params, d)
-    sigma = kernel_scores(q_row, ck, pos, params, h_kv)
-    S = block_scores(sigma, pos, params)
-    sel = [select_blocks(S[g], pos, params) for g in range(h_kv)]
     o = np.zeros((h_q, d))
     lse = np.zeros(h_q)
     for h in range(h_q):
@@ -258,9 +260,21 @@ def _sparse_row(q_row, k, v, ck, pos, params, extra=None):
         toks = _block_tokens(sel[g], pos, params.block_size)
         keys, vals = k[g, toks], v[g, toks]
         if extra is not None:
-            keys = np.concatenate([keys, extra[0][g]], axis=0)
-            vals = np.concatenate([vals, extra[1][g]], axis=0)
+            keys = np.concatenate([keys, np.asarray(extra[0][g], np.float64)], axis=0)
+            vals = np.concatenate([vals, np.asarray(extra[1][g], np.float64)], axis=0)
         o[h], lse[h] = attend(q_row[h], keys, vals, scale)
+    return o, lse
+
+
+def _sparse_row(q_row, k, v, ck, pos, params, extra=None):
+    """Steps 3-6 for one query token.  `extra` = (k_x, v_x) [h_kv][n][d]
+    additional keys attended densely (tree drafts)."""
+    q_row = np.asarray(q_row, np.float64)
+    h_kv = k.shape[0]
+    sigma = kernel_scores(q_row, ck, pos, params, h_kv)
+    S = block_scores(sigma, pos, params)
+    sel = [select_blocks(S[g], pos, params) for g in range(h_kv)]
+    o, lse = attend_selected(q_row, k, v, sel, pos, params, extra)
     return o, lse, S, sel
 
 

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+the header declares, and rejects invalid calls on the host before launching
+anything (only argument validation runs; no kernel is queued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infllmv2.h")
+LIBPATH = os.path.join(ROOT, "block_sparse_long_infllmv2_amd", "libinfllmv2.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(infllmv2_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIBPATH):
+        pytest.fail(f"{LIBPATH} not built (run __graft_entry__.build())")
+    lib = ctypes.CDLL(LIBPATH)
+    from block_sparse_long_infllmv2_amd.binding import Params
+    P = ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    PP = ctypes.POINTER(Params)
+    lib.infllmv2_default_params.argtypes = [PP]
+    lib.infllmv2_status_string.restype = ctypes.c_char_p
+    lib.infllmv2_workspace_size.restype = sz
+    lib.infllmv2_workspace_size.argtypes = [ctypes.c_int, i32, i32, i32, i32, i64, PP]
+    lib.infllmv2_compress_keys.argtypes = [ctypes.c_int, P, i32, i32, i64, i32, P, i64, i64, P,
+                                           i64, PP, P]
+    lib.infllmv2_block_scores.argtypes = [ctypes.c_int, P, i32, P, P, i32, i32, i32, P, i32,
+                                          i64, P, P, i64, i32, PP, P]
+    lib.infllmv2_select_topk.argtypes = [P, i32, P, P, i32, i64, P, i32, P, PP, P]
+    lib.infllmv2_sparse_attn_prefill.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, i32,
+                                                 i32, i32, P, P, P, PP, P]
+    lib.infllmv2_sparse_attn_decode.argtypes = [ctypes.c_int, P, i32, P, P, i64, P, i32, i32,
+                                                i32, i32, P, P, P, P, sz, PP, P]
+    lib.infllmv2_tree_verify.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P, i32,
+                                         i32, i32, P, P, P, P, sz, PP, P]
+    lib.Params = Params
+    return lib
+
+
+def params(lib, **kw):
+    p = lib.Params()
+    lib.infllmv2_default_params(ctypes.byref(p))
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return ctypes.byref(p)
+
+
+FAKE = ctypes.c_void_p(0x10000)     # aligned, never dereferenced by the host
+
+
+def test_header_declares_the_six_calls():
+    fns = declared_functions()
+    for name in ["infllmv2_compress_keys", "infllmv2_block_scores", "infllmv2_select_topk",
+                 "infllmv2_sparse_attn_prefill", "infllmv2_sparse_attn_decode",
+                 "infllmv2_tree_verify"]:
+        assert name in fns
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_defaults_status_version(lib):
+    p = lib.Params()
+    lib.infllmv2_default_params(ctypes.byref(p))
+    assert (p.block_size, p.kernel_size, p.kernel_stride, p.topk, p.init_blocks,
+            p.local_blocks, p.dense_len, p.scale) == (64, 32, 16, 64, 1, 2, 8192, 0.0)
+    assert lib.infllmv2_status_string(0) == b"ok"
+    assert b"workspace" in lib.infllmv2_status_string(3)
+    assert lib.infllmv2_status_string(99) == b"unknown status"
+    assert lib.infllmv2_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    ws = lib.infllmv2_workspace_size
+    dec = ws(0, 8, 32, 2, 128, 131072, params(lib))
+    # 8 rows x 32 heads x (128 blocks of a dense 8191-token sequence / 2 per
+    # split) x (128 + 2) floats: dense rows may walk more blocks than topk
+    assert dec == 8 * 32 * 64 * 130 * 4
+    dec_dense = ws(0, 1, 32, 2, 128, 4096, params(lib))
+    assert dec_dense == ((1 * 32 * 32 * 130 * 4 + 255) // 256) * 256
+    tree = ws(1, 16, 32, 2, 128, 131072, params(lib))
+    assert tree > 16 * 32 * 130 * 4
+    assert ws(1, 65, 32, 2, 128, 131072, params(lib)) == 0      # > 64 drafts
+    assert ws(0, 8, 32, 3, 128, 131072, params(lib)) == 0       # 32 % 3 != 0
+    assert ws(0, 8, 32, 2, 96, 131072, params(lib)) == 0        # head_dim 96
+    assert ws(7, 8, 32, 2, 128, 131072, params(lib)) == 0       # unknown op
+
+
+def test_compress_validation(lib):
+    f = lib.infllmv2_compress_keys
+    seq = FAKE
+    assert f(1, None, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63, params(lib), None) == INVALID
+    assert f(5, FAKE, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63, params(lib), None) == INVALID
+    assert f(1, FAKE, 1, 2, 1024, 96, seq, 0, 10, FAKE, 63, params(lib), None) == UNSUPPORTED
+    assert f(1, FAKE, 1, 2, 1024, 128, seq, 0, 64, FAKE, 63, params(lib), None) == INVALID
+    assert f(1, FAKE, 1, 2, 100, 128, seq, 0, 10, FAKE, 63, params(lib), None) == INVALID
+    assert f(1, FAKE, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63,
+             params(lib, topk=2, init_blocks=1, local_blocks=2), None) == INVALID
+    assert f(1, FAKE, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63,
+             params(lib, kernel_stride=64), None) == UNSUPPORTED
+    assert f(1, FAKE, 1, 2, 1024, 128, seq, 5, 5, FAKE, 63, params(lib), None) == OK  # empty
+
+
+def test_scores_and_topk_validation(lib):
+    s = lib.infllmv2_block_scores
+    assert s(1, FAKE, 4, None, FAKE, 32, 3, 128, FAKE, 1, 100, FAKE, FAKE, 32, 1000,
+             params(lib), None) == INVALID                           # 32 % 3
+    assert s(1, FAKE, 4, None, FAKE, 32, 2, 128, FAKE, 1, 100, FAKE, FAKE, 8, 1000,
+             params(lib), None) == INVALID                           # nb_cap too small
+    assert s(1, FAKE, 4, None, FAKE, 32, 2, 128, FAKE, 1, 50, FAKE, FAKE, 32, 1000,
+             params(lib), None) == INVALID                           # nc_cap too small
+    assert s(1, FAKE, 0, None, FAKE, 32, 2, 128, FAKE, 1, 100, FAKE, FAKE, 32, 1000,
+             params(lib), None) == OK                                # no rows
+    t = lib.infllmv2_select_topk
+    assert t(None, 4, None, FAKE, 2, 32, FAKE, 1, FAKE, params(lib), None) == INVALID
+    assert t(FAKE, 4, None, FAKE, 2, 32, FAKE, 1, FAKE, params(lib, topk=200),
+             None) == UNSUPPORTED
+    assert t(FAKE, 0, None, FAKE, 2, 32, FAKE, 1, FAKE, params(lib), None) == OK
+
+
+def test_attention_validation(lib):
+    pre = lib.infllmv2_sparse_attn_prefill
+    # sparse (n_k >= dense_len) without block_idx
+    assert pre(1, FAKE, 8, FAKE, FAKE, 10000, 10000, 32, 2, 128, None, FAKE, None,
+               params(lib), None) == INVALID
+    # group size 3 has no matrix-core tiling
+    assert pre(1, FAKE, 8, FAKE, FAKE, 10000, 10000, 6, 2, 128, FAKE, FAKE, None,
+               params(lib), None) == UNSUPPORTED
+    assert pre(1, FAKE, 8, FAKE, FAKE, 100, 1000, 32, 2, 128, FAKE, FAKE, None,
+               params(lib), None) == INVALID                         # cap < n_k
+    dec = lib.infllmv2_sparse_attn_decode
+    need = lib.infllmv2_workspace_size(0, 2, 32, 2, 128, 20000, params(lib))
+    assert dec(1, FAKE, 2, FAKE, FAKE, 20000, FAKE, 20000, 32, 2, 128, FAKE, FAKE, None,
+               FAKE, need - 1, params(lib), None) == WORKSPACE
+    assert dec(1, FAKE, 2, FAKE, FAKE, 20000, FAKE, 20000, 32, 2, 128, FAKE, FAKE, None,
+               None, need, params(lib), None) == WORKSPACE
+    assert dec(1, FAKE, 2, FAKE, FAKE, 20000, FAKE, 20000, 32, 2, 128, None, FAKE, None,
+               FAKE, need, params(lib), None) == INVALID             # sparse needs idx
+    tv = lib.infllmv2_tree_verify
+    assert tv(1, FAKE, 65, FAKE, FAKE, 20000, 20000, FAKE, FAKE, FAKE, 32, 2, 128, FAKE, FAKE,
+              None, FAKE, 1 << 30, params(lib), None) == INVALID     # > 64 drafts
+    tneed = lib.infllmv2_workspace_size(1, 16, 32, 2, 128, 20000, params(lib))
+    assert tv(1, FAKE, 16, FAKE, FAKE, 20000, 20000, FAKE, FAKE, FAKE, 32, 2, 128, FAKE,
+              FAKE, None, FAKE, tneed - 256, params(lib), None) == WORKSPACE
+    assert tv(1, FAKE, 16, FAKE, FAKE, 20000, 20000, FAKE, None, FAKE, 32, 2, 128, FAKE,
+              FAKE, None, FAKE, tneed, params(lib), None) == INVALID  # no draft V

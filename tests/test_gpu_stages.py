@@ -1,0 +1,337 @@
+"""GPU parity, stage by stage and end to end, at sizes the oracle finishes in
+seconds (several tiles, ragged tails, dense/sparse mixes).  Every case calls
+the HIP library through its C ABI (ctypes binding) and compares with the CPU
+oracle on the same seeded inputs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from block_sparse_long_infllmv2_amd.workloads import Params, config, make_decode, \
+    make_prefill, make_tree
+from parity import check_close, check_selection
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def B():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from block_sparse_long_infllmv2_amd import binding
+    return binding
+
+
+@pytest.fixture(scope="module")
+def PL():
+    from block_sparse_long_infllmv2_amd import pipeline
+    return pipeline
+
+
+def dev(x, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16 if dtype == "bf16" else torch.float32).cuda()
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def tdt(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+# ------------------------------------------------------------- compress ----
+def _check_ck(got, ref, dtype, where):
+    """bf16: the float32 sum of 32 bf16 keys is exact, so the stored mean must
+    match the oracle's rounding except for rare double-rounding cases.
+    float32: the sum itself rounds; allow a few float32 ulps."""
+    if dtype == "bf16":
+        mism = np.count_nonzero(got != ref)
+        assert mism <= max(1, ref.size // 10000), f"{where}: {mism} of {ref.size} differ"
+        np.testing.assert_allclose(got, ref, rtol=2 ** -7, atol=1e-30)
+    else:
+        np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
+def test_compress_keys(B, dtype, d):
+    _say(f"compress {dtype} d={d}")
+    p = Params()
+    rng = np.random.default_rng(1)
+    lens = [1000, 333, 31]
+    cap = 1024
+    h_kv = 2
+    k = np.zeros((3, h_kv, cap, d), np.float32)
+    for i, L in enumerate(lens):
+        k[i, :, :L] = rng.standard_normal((h_kv, L, d))
+    kk = dev(k, dtype)
+    host_k = host(kk)
+    nc_cap = O.num_windows(cap, 32, 16)
+    ck = torch.full((3, h_kv, nc_cap, d), 7.0, dtype=tdt(dtype), device="cuda")
+    B.infllmv2_compress_keys(kk, torch.tensor(lens, dtype=torch.int32, device="cuda"), 0,
+                             nc_cap, ck, p)
+    torch.cuda.synchronize()
+    got = host(ck)
+    for i, L in enumerate(lens):
+        ref = O.compress_keys(host_k[i, :, :L], p, dtype)
+        n_c = ref.shape[1]
+        _check_ck(got[i, :, :n_c], ref, dtype, f"seq {i}")
+        assert np.all(got[i, :, n_c:] == 7.0), "windows past the sequence were written"
+
+
+# --------------------------------------------------------------- scores ----
+@pytest.mark.parametrize("dtype,d,h_q,h_kv", [("bf16", 128, 32, 2), ("f32", 64, 2, 1),
+                                              ("bf16", 64, 8, 2)])
+def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv):
+    _say(f"scores {dtype} d={d} h_q={h_q} h_kv={h_kv}")
+    p = Params(dense_len=0)
+    n_k = 5000
+    c = make_prefill(3, n_k=n_k, n_q=1, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
+                     n_planted=5, alpha=1.5, beta=1.5)
+    ck = O.compress_keys(c.k, p, dtype)
+    rng = np.random.default_rng(2)
+    pos = np.array([0, 15, 30, 31, 63, 64, 78, 79, 200, 4095, 4999, 2500], np.int32)
+    q = dev(rng.standard_normal((len(pos), h_q, d)), dtype)
+    nb = n_k // 64 + 1
+    scores = torch.full((len(pos), h_kv, nb), 123.0, dtype=torch.float32, device="cuda")
+    B.infllmv2_block_scores(q, None, torch.from_numpy(pos).cuda(), dev(ck[None], dtype),
+                            torch.tensor([n_k], dtype=torch.int32, device="cuda"), scores,
+                            int(pos.max()), p)
+    torch.cuda.synchronize()
+    got = scores.cpu().numpy()
+    qh = host(q)
+    for r, ps in enumerate(pos):
+        sig = O.kernel_scores(qh[r], ck, int(ps), p, h_kv)
+        S = O.block_scores(sig, int(ps), p)
+        ne = S.shape[1]
+        g = got[r, :, :ne]
+        inf = np.isinf(S)
+        assert np.array_equal(np.isinf(g), inf), f"row {r}: -inf pattern differs"
+        np.testing.assert_allclose(g[~inf], S[~inf], rtol=2e-5, atol=2e-5)
+        assert np.all(got[r, :, ne:] == 123.0), "scores beyond eligible blocks written"
+
+
+# ----------------------------------------------------------------- topk ----
+def test_select_topk_matches_oracle_exactly(B):
+    _say("topk exact")
+    rng = np.random.default_rng(4)
+    cases = []
+    for topk, init, local, nb, ties in [(8, 1, 2, 40, True), (64, 1, 2, 2048, False),
+                                        (64, 1, 2, 2048, True), (6, 0, 0, 30, True),
+                                        (16, 2, 3, 700, False), (64, 1, 2, 65, False),
+                                        (64, 1, 2, 10000, False)]:
+        cases.append((Params(topk=topk, init_blocks=init, local_blocks=local, dense_len=0),
+                      nb, ties))
+    for p, nb, ties in cases:
+        rows = 24
+        n_k = nb * 64
+        pos = rng.integers(0, n_k, rows).astype(np.int32)
+        pos[0] = n_k - 1
+        pos[1] = 0
+        S = rng.standard_normal((rows, 2, nb)).astype(np.float32)
+        if ties:
+            S = np.round(S * 2).astype(np.float32)
+        S[rng.random(S.shape) < 0.05] = -np.inf
+        s_t = torch.from_numpy(S).cuda()
+        idx = torch.full((rows, 2, p.topk), -7, dtype=torch.int32, device="cuda")
+        B.infllmv2_select_topk(s_t, None, torch.from_numpy(pos).cuda(),
+                               torch.tensor([n_k], dtype=torch.int32, device="cuda"), idx, p)
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        for r in range(rows):
+            for g in range(2):
+                ne = pos[r] // 64 + 1
+                want = O.select_blocks(S[r, g, :ne].astype(np.float64), int(pos[r]), p)
+                row = got[r, g]
+                assert list(row[:len(want)]) == list(want), (p, r, g)
+                assert np.all(row[len(want):] == -1)
+
+
+def test_select_topk_dense_rows_get_minus_one(B):
+    _say("topk dense rows")
+    p = Params()
+    S = torch.zeros((3, 2, 200), dtype=torch.float32, device="cuda")
+    idx = torch.zeros((3, 2, 64), dtype=torch.int32, device="cuda")
+    seqlens = torch.tensor([8191, 8192, 12000], dtype=torch.int32, device="cuda")
+    row_seq = torch.tensor([0, 1, 2], dtype=torch.int32, device="cuda")
+    B.infllmv2_select_topk(S, row_seq, None, seqlens, idx, p)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert np.all(got[0] == -1)
+    assert np.all(got[1] >= 0) and np.all(got[2] >= 0)
+
+
+# -------------------------------------------------------------- prefill ----
+def _run_prefill(B, PL, c, rows_check=None):
+    p = c.params
+    h_kv, n_k, d = c.k.shape
+    n_q, h_q, _ = c.q.shape
+    q = dev(c.q, c.dtype)
+    k = dev(c.k, c.dtype)
+    v = dev(c.v, c.dtype)
+    nc = max(1, O.num_windows(n_k, p.kernel_size, p.kernel_stride))
+    ck = torch.zeros((h_kv, nc, d), dtype=tdt(c.dtype), device="cuda")
+    plan = PL.PrefillPlan(n_q, n_k, h_q, h_kv, d, tdt(c.dtype), p)
+    plan.run(q, k, v, ck, m_begin=0)
+    torch.cuda.synchronize()
+    return plan, ck
+
+
+def _check_prefill(plan, ck_gpu, c, rows):
+    p = c.params
+    n_q = c.n_q
+    res = O.prefill(c.q, c.k, c.v, p, c.dtype, rows=rows)
+    out = host(plan.out)
+    lse = plan.lse.cpu().numpy()
+    if not res["dense"]:
+        _check_ck(host(ck_gpu), res["ck"], c.dtype, "compressed keys")
+        sel = plan.block_idx.cpu().numpy()
+    for i in rows:
+        pos = c.n_k - n_q + i
+        if res["dense"]:
+            ref_o, ref_l = res["o"][i], res["lse"][i]
+        else:
+            P = [check_selection(sel[i, g], res["S"][i][g], res["sel"][i][g], pos, p,
+                                 f"row {i} g {g}") for g in range(c.k.shape[0])]
+            ref_o, ref_l = O.attend_selected(c.q[i], c.k, c.v, P, pos, p)
+        check_close(out[i], ref_o, c.dtype, f"row {i}")
+        np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if c.dtype == "bf16" else 1e-4)
+
+
+def test_prefill_tiny_f32_config(B, PL):
+    """The tiny float32 workload at full size: N=2048, 2 q heads / 1 KV head."""
+    _say("prefill cfg0 f32 n=2048")
+    c = config(0)
+    plan, ck = _run_prefill(B, PL, c)
+    _check_prefill(plan, ck, c, rows=list(range(0, 2048, 7)) + [2047, 2046, 64, 63])
+
+
+@pytest.mark.parametrize("n_k,n_q,h_q,h_kv,d,topk", [
+    (4096, 300, 32, 2, 128, 16),     # several tiles, ragged last tile
+    (9000, 133, 32, 2, 128, 64),     # ragged last KV block (9000 % 64 = 40)
+    (3000, 200, 16, 2, 64, 8),       # G = 8, d = 64
+    (2600, 64, 8, 2, 128, 8),        # G = 4: 32-token tiles
+])
+def test_prefill_bf16_end_to_end(B, PL, n_k, n_q, h_q, h_kv, d, topk):
+    _say(f"prefill bf16 n_k={n_k} n_q={n_q} h_q={h_q} h_kv={h_kv} d={d} topk={topk}")
+    p = Params(topk=topk, dense_len=0)
+    c = make_prefill(5, n_k=n_k, n_q=n_q, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype="bf16",
+                     n_planted=max(1, n_k // 2048), alpha=1.5, beta=1.5)
+    plan, ck = _run_prefill(B, PL, c)
+    rows = sorted(set(list(range(0, n_q, 5)) + [n_q - 1, n_q - 2, 0, 7, 8, 9]))
+    _check_prefill(plan, ck, c, rows)
+
+
+def test_prefill_bf16_dense_below_dense_len(B, PL):
+    _say("prefill bf16 dense")
+    p = Params(dense_len=4096)
+    c = make_prefill(6, n_k=4095, n_q=150, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=2, alpha=1.5, beta=1.5)
+    plan, ck = _run_prefill(B, PL, c)
+    assert plan.dense
+    _check_prefill(plan, ck, c, rows=list(range(0, 150, 3)) + [149])
+
+
+# --------------------------------------------------------------- decode ----
+def _run_decode(B, PL, c, cap=None):
+    p = c.params
+    bsz = len(c.seqlens)
+    h_kv, _, d = c.k[0].shape
+    h_q = c.q.shape[1]
+    maxL = int(max(c.seqlens))
+    cap = cap or ((maxL + 63) // 64) * 64
+    kc = np.zeros((bsz, h_kv, cap, d), np.float32)
+    vc = np.zeros((bsz, h_kv, cap, d), np.float32)
+    for i, L in enumerate(c.seqlens):
+        kc[i, :, :L] = c.k[i]
+        vc[i, :, :L] = c.v[i]
+    k = dev(kc, c.dtype)
+    v = dev(vc, c.dtype)
+    q = dev(c.q, c.dtype)
+    seqlens = torch.from_numpy(np.asarray(c.seqlens, np.int32)).cuda()
+    nc_cap = max(1, O.num_windows(cap, p.kernel_size, p.kernel_stride))
+    ck = torch.zeros((bsz, h_kv, nc_cap, d), dtype=tdt(c.dtype), device="cuda")
+    B.infllmv2_compress_keys(k, seqlens, 0, nc_cap, ck, p)
+    plan = PL.DecodePlan(bsz, maxL, h_q, h_kv, d, tdt(c.dtype), p)
+    plan.run(q, k, v, ck, seqlens)
+    torch.cuda.synchronize()
+    return plan
+
+
+def _check_decode(plan, c):
+    p = c.params
+    res = O.decode(c.q, c.k, c.v, c.seqlens, p, c.dtype)
+    out = host(plan.out)
+    lse = plan.lse.cpu().numpy()
+    sel = plan.block_idx.cpu().numpy()
+    for i, L in enumerate(c.seqlens):
+        pos = int(L) - 1
+        if res["dense"][i]:
+            ref_o, ref_l = res["o"][i], res["lse"][i]
+        else:
+            P = [check_selection(sel[i, g], res["S"][i][g], res["sel"][i][g], pos, p,
+                                 f"seq {i} g {g}") for g in range(c.k[i].shape[0])]
+            ref_o, ref_l = O.attend_selected(c.q[i], c.k[i], c.v[i], P, pos, p)
+        check_close(out[i], ref_o, c.dtype, f"seq {i}")
+        np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if c.dtype == "bf16" else 1e-4)
+
+
+@pytest.mark.parametrize("dtype,d,h_q,h_kv", [("bf16", 128, 32, 2), ("f32", 64, 4, 2),
+                                              ("bf16", 64, 8, 1)])
+def test_decode_ragged(B, PL, dtype, d, h_q, h_kv):
+    _say(f"decode ragged {dtype} d={d} h_q={h_q} h_kv={h_kv}")
+    p = Params(dense_len=2048, topk=16)
+    c = make_decode(7, [100, 2047, 2048, 5000, 9001, 64, 1], h_q=h_q, h_kv=h_kv, d=d, params=p,
+                    dtype=dtype, planted_per_token=1 / 512)
+    plan = _run_decode(B, PL, c)
+    _check_decode(plan, c)
+
+
+# ----------------------------------------------------------------- tree ----
+@pytest.mark.parametrize("dtype,n_ctx,T,dense_len", [("bf16", 12000, 16, 8192),
+                                                     ("bf16", 5000, 16, 8192),
+                                                     ("bf16", 9000, 40, 0),
+                                                     ("f32", 3000, 7, 0)])
+def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len):
+    _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len}")
+    p = Params(dense_len=dense_len, topk=16)
+    h_q, h_kv, d = (32, 2, 128) if dtype == "bf16" else (4, 2, 64)
+    c = make_tree(8, n_ctx=n_ctx, n_draft=T, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
+                  n_planted=max(1, n_ctx // 2048))
+    q = dev(c.q, dtype)
+    k = dev(c.k, dtype)
+    v = dev(c.v, dtype)
+    kd = dev(c.k_draft, dtype)
+    vd = dev(c.v_draft, dtype)
+    mask = torch.from_numpy(c.mask.astype(np.int64)).cuda()
+    nc = O.num_windows(n_ctx, 32, 16)
+    ck = torch.zeros((h_kv, nc, d), dtype=tdt(dtype), device="cuda")
+    B.infllmv2_compress_keys(k.unsqueeze(0), torch.tensor([n_ctx], dtype=torch.int32,
+                                                          device="cuda"), 0, nc,
+                             ck.unsqueeze(0), p)
+    plan = PL.TreePlan(T, n_ctx, h_q, h_kv, d, tdt(dtype), p)
+    plan.run(q, k, v, ck, kd, vd, mask)
+    torch.cuda.synchronize()
+    res = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, dtype)
+    out = host(plan.out)
+    lse = plan.lse.cpu().numpy()
+    pos = n_ctx - 1
+    for i in range(T):
+        anc = [j for j in range(T) if (int(c.mask[i]) >> j) & 1]
+        extra = (c.k_draft[:, anc], c.v_draft[:, anc])
+        if res["dense"]:
+            ref_o, ref_l = res["o"][i], res["lse"][i]
+        else:
+            sel = plan.block_idx.cpu().numpy()
+            P = [check_selection(sel[i, g], res["S"][i][g], res["sel"][i][g], pos, p,
+                                 f"draft {i} g {g}") for g in range(h_kv)]
+            ref_o, ref_l = O.attend_selected(c.q[i], c.k, c.v, P, pos, p, extra)
+        check_close(out[i], ref_o, dtype, f"draft {i}")
+        np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if dtype == "bf16" else 1e-4)
