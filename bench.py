@@ -147,8 +147,10 @@ class Workload:
             mark("start")
             pl.compress(self.k, self.ck)
             mark("compress_keys")
-            pl.select(self.q, self.ck)      # block_scores + select_topk
-            mark("scores_topk")
+            pl.score(self.q, self.ck)
+            mark("block_scores")
+            pl.topk()
+            mark("select_topk")
             pl.attend(self.q, self.k, self.v)
             mark("sparse_attn_prefill")
         elif self.kind == "decode":

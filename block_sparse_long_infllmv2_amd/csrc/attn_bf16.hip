@@ -148,32 +148,57 @@ struct RowState {
         s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s[kt], 0, 0, 0);
       }
     }
-    // mask, scale into the log2 domain, row max
-    float mx = -INFINITY;
+    // Scale into the log2 domain, mask, row max, exponentials.  Common case
+    // (every row of the wave keeps all 64 keys or none of them): no per-key
+    // masking -- rows that keep nothing subtract +inf, so their p is 0.
+    const bool partial = (lim >= 0 && lim < 63) || use_bits;
+    const bool keep = lim >= 0;
+    float m_new, alpha, psum = 0.0f;
+    if (!__ballot(partial)) {
+      float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int off = 32 * kt + 8 * (v >> 2) + 4 * half + (v & 3);
-        bool ok = off <= lim;
-        if (use_bits) ok = ok && ((draft_bits >> off) & 1ull);
-        const float x = ok ? s[kt][v] * scale_log2 : -INFINITY;
-        s[kt][v] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - m_new);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+      mx = keep ? mx * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, swap_halves(mx));
+      m_new = fmaxf(m, mx);
+      alpha = fast_exp2(m - m_new);
+      const float msub = keep ? m_new : INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(__builtin_fmaf(s[kt][v], scale_log2, -msub));
+          s[kt][v] = p;
+          psum += p;
+        }
+    } else {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = 32 * kt + 8 * (v >> 2) + 4 * half + (v & 3);
+          bool ok = off <= lim;
+          if (use_bits) ok = ok && ((draft_bits >> off) & 1ull);
+          const float x = ok ? s[kt][v] * scale_log2 : -INFINITY;
+          s[kt][v] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, swap_halves(mx));
+      m_new = fmaxf(m, mx);
+      alpha = fast_exp2(m - m_new);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(s[kt][v] - m_new);
+          s[kt][v] = p;
+          psum += p;
+        }
+    }
     m = m_new;
-    float psum = 0.0f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(s[kt][v] - m_new);
-        s[kt][v] = p;
-        psum += p;
-      }
     l = l * alpha + psum;
     if (__ballot(alpha != 1.0f)) {
 #pragma unroll
@@ -314,7 +339,8 @@ __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, 
 //   W waves, each 32 rows = TPW tokens x G heads; TT = W * TPW tokens.
 // ---------------------------------------------------------------------------
 template <int D, int G, int W, int MODE>
-__global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = W * 64;
   constexpr int TPW = 32 / G;
   constexpr int TT = (MODE == kDecode) ? 1 : W * TPW;
@@ -409,8 +435,10 @@ __global__ __launch_bounds__(W * 64) void attn_bf16_kernel(AttnArgs a) {
   const int n_units_total = n_entries * cpb + (has_draft ? 1 : 0);
   int u_begin = 0, u_end = n_units_total;
   if constexpr (MODE != kPrefill) {
-    u_begin = split * a.entries_per_split * cpb;
-    u_end = min(n_units_total, u_begin + a.entries_per_split * cpb);
+    // balanced contiguous slices of this row's units over the n_split splits
+    const int per = (n_units_total + a.n_split - 1) / a.n_split;
+    u_begin = min(n_units_total, split * per);
+    u_end = min(n_units_total, u_begin + per);
   }
 
   // unit -> (block id, key0 of the chunk, #valid keys, token bitmask)
@@ -596,31 +624,38 @@ __global__ __launch_bounds__(kPlanThreads) void tree_union_kernel(
 template <int D, typename TOut>
 __global__ __launch_bounds__(64) void combine_kernel(const float* ws, int n_split, TOut* out,
                                                      float* lse) {
+  constexpr int kMaxSplit = 64;
+  __shared__ float wsh[kMaxSplit];
   const int rh = blockIdx.x;   // row * h_q + head
+  const int lane = threadIdx.x;
   const float* base = ws + (int64_t)rh * n_split * (D + 2);
-  float M = kNoMax;
-  for (int s = 0; s < n_split; ++s) {
-    const float l = base[s * (D + 2) + D + 1];
-    if (l > 0.0f) M = fmaxf(M, base[s * (D + 2) + D]);
+  // lane s holds split s (n_split <= 64): max, weights and normaliser in
+  // parallel over the splits
+  float m = kNoMax, l = 0.0f;
+  if (lane < n_split) {
+    l = base[lane * (D + 2) + D + 1];
+    m = l > 0.0f ? base[lane * (D + 2) + D] : kNoMax;
   }
-  float L = 0.0f;
+  const float M = wave_max(m);
+  const float w = l > 0.0f ? fast_exp2(m - M) : 0.0f;
+  const float L = wave_sum(w * l);
+  if (lane < kMaxSplit) wsh[lane] = w;
+  __syncthreads();
   float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.0f;
   for (int s = 0; s < n_split; ++s) {
+    const float ww = wsh[s];
+    if (ww == 0.0f) continue;
     const float* p = base + s * (D + 2);
-    const float l = p[D + 1];
-    if (!(l > 0.0f)) continue;
-    const float w = fast_exp2(p[D] - M);
-    L += w * l;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += w * p[threadIdx.x + 64 * i];
+    for (int i = 0; i < D / 64; ++i) acc[i] += ww * p[lane + 64 * i];
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
   for (int i = 0; i < D / 64; ++i)
-    Elem<TOut>::store(out + (int64_t)rh * D + threadIdx.x + 64 * i, acc[i] * inv);
-  if (lse && threadIdx.x == 0) lse[rh] = (M + __log2f(L)) * kLn2;
+    Elem<TOut>::store(out + (int64_t)rh * D + lane + 64 * i, acc[i] * inv);
+  if (lse && lane == 0) lse[rh] = (M + __log2f(L)) * kLn2;
 }
 
 }  // namespace infllmv2
@@ -632,8 +667,10 @@ using namespace infllmv2;
 
 namespace {
 
-constexpr int kDecodeEntriesPerSplit = 2;
-constexpr int kTreeEntriesPerSplit = 2;
+// Splits per (row, KV head): enough workgroups to cover the GPU for batched
+// decode and tree verification while keeping the float32 partials small.
+constexpr int kMaxDecodeSplits = 32;
+constexpr int kMaxTreeSplits = 32;
 
 template <int D, int G, int W, int MODE>
 int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
@@ -718,7 +755,8 @@ int64_t decode_max_entries(int64_t max_seqlen, const Resolved& r) {
 }
 
 int64_t decode_splits(int64_t max_seqlen, const Resolved& r) {
-  return ceil_div(decode_max_entries(max_seqlen, r), kDecodeEntriesPerSplit);
+  const int64_t units = decode_max_entries(max_seqlen, r) * ceil_div(r.B, kChunk);
+  return units < kMaxDecodeSplits ? units : kMaxDecodeSplits;
 }
 
 int64_t tree_union_cap(int n_draft, int64_t n_ctx, const Resolved& r) {
@@ -733,7 +771,7 @@ int64_t tree_splits(int n_draft, int64_t n_ctx, const Resolved& r) {
   // + 1 entry's worth for the chunk of draft tokens
   const int64_t cpb = ceil_div(r.B, kChunk);
   const int64_t units = entries * cpb + 1;
-  return ceil_div(units, (int64_t)kTreeEntriesPerSplit * cpb);
+  return units < kMaxTreeSplits ? units : kMaxTreeSplits;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -810,7 +848,7 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   a.out = (uint16_t*)out; a.lse = lse; a.ws = (float*)ws;
   a.cap = cap; a.n_k = max_seqlen; a.n_rows = batch; a.h_q = h_q; a.h_kv = h_kv;
   a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
-  a.n_split = (int)n_split; a.entries_per_split = kDecodeEntriesPerSplit;
+  a.n_split = (int)n_split;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == INFLLMV2_F32) return decode_f32(a, d, st);
   const int G = h_q / h_kv;
@@ -878,7 +916,7 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   a.union_cap = (int)ucap;
   a.cap = cap; a.n_k = n_ctx; a.n_rows = n_draft; a.h_q = h_q; a.h_kv = h_kv;
   a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
-  a.n_split = (int)n_split; a.entries_per_split = kTreeEntriesPerSplit;
+  a.n_split = (int)n_split;
   hipStream_t st = (hipStream_t)stream;
   if (dtype == INFLLMV2_F32) return tree_f32(a, d, st);
   const int G = h_q / h_kv;

@@ -31,7 +31,7 @@ struct AttnArgs {
   int64_t cap;                // tokens per (sequence, KV head) in the cache
   int64_t n_k;                // prefill: keys; tree: context length
   int n_rows;                 // prefill: n_q; decode: batch; tree: n_draft
-  int h_q, h_kv, topk, B, dense_len, n_split, entries_per_split, n_tiles, union_cap;
+  int h_q, h_kv, topk, B, dense_len, n_split, n_tiles, union_cap;
   float scale_log2;           // softmax scale * log2(e)
 };
 

@@ -20,6 +20,7 @@ namespace infllmv2 {
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreMaxWindows = 1024;   // window scores held in LDS per chunk
+constexpr int kMfmaMinRows = 64;         // fewer rows: the streaming kernel
 
 struct ScoreArgs {
   const void* q;
@@ -29,7 +30,7 @@ struct ScoreArgs {
   const int32_t* seqlens;
   float* scores;
   int64_t nc_cap, nb_cap;
-  int h_q, h_kv, B, ks, s, dense_len, blocks_per_wg, chunks_per_row, batch, max_pos;
+  int h_q, h_kv, B, ks, s, dense_len, blocks_per_wg, chunks_per_row, batch, max_pos, rows;
   float scale;
 };
 
@@ -107,6 +108,176 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Matrix-core variant for many rows of one sequence (prefill chunks, draft
+// batches) with the default window geometry: B = 4*s and ks = 2*s, so block b
+// overlaps windows 4b-1 .. 4b+3 (its four "own" windows and the last own
+// window of block b-1).
+//
+// sigma^T = CK . qsum^T on v_mfma_f32_32x32x16_bf16: the A operand is 32
+// windows x 16 dims of compressed keys, the B operand 16 dims x 32 rows of
+// the group-summed query.  qsum (float32) is split into hi + lo bfloat16
+// parts and both are multiplied, which keeps ~16 significant bits of the
+// query sum so the scores match a float32 dot product to ~1e-5 relative.
+// In the 32x32 accumulator a lane (row j, half h) holds windows 8q + 4h + e
+// (e = 0..3), i.e. exactly the four own windows of block 2q + h of the tile;
+// the fifth (halo) window comes from the other half-wave or the previous tile.
+//
+// Workgroup = 32 rows x one KV head; its 4 waves take interleaved 8-block
+// tiles of the window range, so qsum is built once (in LDS) per workgroup.
+// ---------------------------------------------------------------------------
+constexpr int kMfmaRows = 32;
+
+template <int D>
+__global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
+  constexpr int KS = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
+  __shared__ int64_t pos_lds[kMfmaRows];
+
+  const int w = xcd_contiguous_index(blockIdx.x, gridDim.x);
+  const int g = w / n_row_tiles, tile = w % n_row_tiles;
+  const int r0 = tile * kMfmaRows;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = a.h_q / a.h_kv;
+  const int64_t L = a.seqlens[0];
+  if (L < a.dense_len) return;
+
+  // group-summed query rows -> hi/lo bf16 in LDS; positions
+  for (int it = tid; it < kMfmaRows * (D / 8); it += 256) {
+    const int rr = it / (D / 8), c = it % (D / 8);
+    const int row = r0 + rr;
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    if (row < a.rows) {
+      const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.h_q + (int64_t)g * G) * D + c * 8;
+      for (int h = 0; h < G; ++h) {
+        float x[8];
+        Elem<uint16_t>::unpack(ldg16(qp + (int64_t)h * D), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      }
+    }
+    u32x4 hi, lo;
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      hb[e] = float_to_bf16_bits(acc[e]);
+      lb[e] = float_to_bf16_bits(acc[e] - bf16_bits_to_float(hb[e]));
+    }
+    hi.x = hb[0] | (hb[1] << 16); hi.y = hb[2] | (hb[3] << 16);
+    hi.z = hb[4] | (hb[5] << 16); hi.w = hb[6] | (hb[7] << 16);
+    lo.x = lb[0] | (lb[1] << 16); lo.y = lb[2] | (lb[3] << 16);
+    lo.z = lb[4] | (lb[5] << 16); lo.w = lb[6] | (lb[7] << 16);
+    *reinterpret_cast<u32x4*>(&qlds[0][rr][c * 8]) = hi;
+    *reinterpret_cast<u32x4*>(&qlds[1][rr][c * 8]) = lo;
+  }
+  if (tid < kMfmaRows) {
+    const int row = r0 + tid;
+    int64_t pos = -1;
+    if (row < a.rows) {
+      pos = a.row_pos ? a.row_pos[row] : L - 1;
+      if (pos >= L || pos > a.max_pos) pos = -1;
+    }
+    pos_lds[tid] = pos;
+  }
+  __syncthreads();
+
+  bf16x8 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qh[ks] = *reinterpret_cast<const bf16x8*>(&qlds[0][col][16 * ks + 8 * half]);
+    ql[ks] = *reinterpret_cast<const bf16x8*>(&qlds[1][col][16 * ks + 8 * half]);
+  }
+  const int64_t pos = pos_lds[col];
+  const int row = r0 + col;
+  const bool row_ok = pos >= 0;
+  // visible windows: m*s + ks - 1 <= pos
+  const int64_t n_vis = pos >= a.ks - 1 ? (pos - a.ks + 1) / a.s + 1 : 0;
+  const int64_t b_own = row_ok ? pos / a.B : -1;
+  int64_t tile_max_pos = -1;
+  for (int j = 0; j < kMfmaRows; ++j) tile_max_pos = max(tile_max_pos, pos_lds[j]);
+  const int64_t nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
+  const int64_t n_tiles8 = (nb_tile + 7) / 8;
+  float* out = a.scores + ((int64_t)row * a.h_kv + g) * a.nb_cap;
+  const uint16_t* ckb = (const uint16_t*)a.ck + (int64_t)g * a.nc_cap * D;
+  const float sc = a.scale;
+
+  // dot of this lane's query half with one compressed key (VALU), combined
+  // over the two half-waves: used for the halo window before a wave's first
+  // tile
+  auto single_window = [&](int64_t m) -> float {
+    float part = 0.0f;
+    if (m >= 0 && m < a.nc_cap) {
+      const uint16_t* c = ckb + m * D;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        Elem<uint16_t>::unpack(ldg16(c + 16 * ks + 8 * half), x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          part += ((float)qh[ks][e] + (float)ql[ks][e]) * x[e];
+      }
+    }
+    const float full = part + swap_halves(part);
+    return (m >= 0 && m < n_vis) ? full * sc : -INFINITY;
+  };
+
+  // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
+  // the halo of a tile's first block is the previous tile's last window,
+  // carried in registers (computed directly only for the range's first tile)
+  const int64_t per_wave = (n_tiles8 + 3) / 4;
+  const int64_t t_begin = wave * per_wave;
+  const int64_t t_end = min(n_tiles8, t_begin + per_wave);
+  float carry = t_begin < t_end ? single_window(t_begin * 32 - 1) : -INFINITY;
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int64_t bt = t * 8;
+    const int64_t mt = bt * 4;                 // first own window of the tile
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    const int64_t mrow = mt + col;             // A-operand window of this lane
+    const bool in = mrow < a.nc_cap;
+    const uint16_t* crow = ckb + (in ? mrow : 0) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (in) wv = ldg16(crow + 16 * ks);
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&wv);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qh[ks], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ql[ks], acc, 0, 0, 0);
+    }
+    // own maxima and last windows per block group q (block bt + 2q + half)
+    float own[4], last[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = mt + 8 * q + 4 * half + e;
+        const float x = m < n_vis ? acc[4 * q + e] * sc : -INFINITY;
+        mx = fmaxf(mx, x);
+        if (e == 3) last[q] = x;
+      }
+      own[q] = mx;
+    }
+    float other[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) other[q] = swap_halves(last[q]);
+    // halo window of block bt + 2q + half is the last own window of the
+    // block before it: half 1 <- (q, half 0); half 0 <- (q-1, half 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry);
+      const int64_t b = bt + 2 * q + half;
+      if (row_ok && b <= b_own) out[b] = fmaxf(own[q], halo);
+    }
+    carry = other[3];       // for half-0 lanes: last window of block bt + 7
+  }
+}
+
 template <typename T, int D>
 static int launch_scores(const ScoreArgs& a, int rows, hipStream_t st) {
   dim3 grid((unsigned)((int64_t)a.chunks_per_row * rows), a.h_kv, 1);
@@ -140,7 +311,7 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.q = q; a.row_seq = row_seq; a.row_pos = row_pos; a.ck = ck; a.seqlens = seqlens;
   a.scores = scores; a.nc_cap = nc_cap; a.nb_cap = nb_cap; a.h_q = h_q; a.h_kv = h_kv;
   a.B = r.B; a.ks = r.ks; a.s = r.s; a.dense_len = r.dense_len; a.scale = r.scale;
-  a.batch = batch; a.max_pos = max_pos;
+  a.batch = batch; a.max_pos = max_pos; a.rows = rows;
   // blocks per workgroup: as many as keep the chunk's windows within the LDS
   // buffer (a chunk of n blocks spans at most (n*B + ks - 2)/s + 2 windows)
   int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * r.s - r.ks + 2) / r.B);
@@ -151,6 +322,18 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.chunks_per_row = (int)ceil_div(nb_launch, bpw);
   if ((int64_t)a.chunks_per_row * rows >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
+  const bool mfma_geometry = r.B == 4 * r.s && r.ks == 2 * r.s;
+  if (dtype == INFLLMV2_BF16 && batch == 1 && row_seq == nullptr && mfma_geometry &&
+      rows >= kMfmaMinRows) {
+    const int n_row_tiles = (int)ceil_div(rows, kMfmaRows);
+    if ((int64_t)n_row_tiles * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
+    dim3 grid((unsigned)(n_row_tiles * h_kv));
+    if (d == 128)
+      hipLaunchKernelGGL(block_scores_mfma_kernel<128>, grid, dim3(256), 0, st, a, n_row_tiles);
+    else
+      hipLaunchKernelGGL(block_scores_mfma_kernel<64>, grid, dim3(256), 0, st, a, n_row_tiles);
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   if (dtype == INFLLMV2_BF16)
     return d == 128 ? launch_scores<uint16_t, 128>(a, rows, st)
                     : launch_scores<uint16_t, 64>(a, rows, st);

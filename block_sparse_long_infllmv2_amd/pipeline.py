@@ -49,11 +49,17 @@ class PrefillPlan:
         B.infllmv2_compress_keys(k_cache.unsqueeze(0), self.seqlens, mb, self.m_end,
                                  ck_cache.unsqueeze(0), self.p)
 
-    def select(self, q, ck_cache):
+    def score(self, q, ck_cache):
         B.infllmv2_block_scores(q, None, self.row_pos, ck_cache.unsqueeze(0), self.seqlens,
                                 self.scores, self.n_k - 1, self.p)
+
+    def topk(self):
         B.infllmv2_select_topk(self.scores, None, self.row_pos, self.seqlens, self.block_idx,
                                self.p)
+
+    def select(self, q, ck_cache):
+        self.score(q, ck_cache)
+        self.topk()
 
     def attend(self, q, k_cache, v_cache):
         B.infllmv2_sparse_attn_prefill(q, k_cache, v_cache, self.n_k, self.block_idx, self.out,

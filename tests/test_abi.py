@@ -86,11 +86,10 @@ def test_defaults_status_version(lib):
 def test_workspace_sizes(lib):
     ws = lib.infllmv2_workspace_size
     dec = ws(0, 8, 32, 2, 128, 131072, params(lib))
-    # 8 rows x 32 heads x (128 blocks of a dense 8191-token sequence / 2 per
-    # split) x (128 + 2) floats: dense rows may walk more blocks than topk
-    assert dec == 8 * 32 * 64 * 130 * 4
-    dec_dense = ws(0, 1, 32, 2, 128, 4096, params(lib))
-    assert dec_dense == ((1 * 32 * 32 * 130 * 4 + 255) // 256) * 256
+    # 8 rows x 32 heads x 32 splits x (128 + 2) floats
+    assert dec == 8 * 32 * 32 * 130 * 4
+    dec_short = ws(0, 1, 32, 2, 128, 640, params(lib))   # 10 blocks -> 10 splits
+    assert dec_short == ((1 * 32 * 10 * 130 * 4 + 255) // 256) * 256
     tree = ws(1, 16, 32, 2, 128, 131072, params(lib))
     assert tree > 16 * 32 * 130 * 4
     assert ws(1, 65, 32, 2, 128, 131072, params(lib)) == 0      # > 64 drafts
