@@ -256,6 +256,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times): the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path is "
@@ -264,6 +267,15 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": a.numel() * 4,
+                          "bytes_written": b.numel() * 4, "launches": 3}))
+        return
     wl = Workload(args.workload, torch)
     print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
 

@@ -14,7 +14,8 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libinfllmv2.so")
+# INFLLMV2_LIB selects another build of the same library (same ABI)
+LIB_PATH = os.environ.get("INFLLMV2_LIB") or os.path.join(_HERE, "libinfllmv2.so")
 
 F32, BF16 = 0, 1
 OP_DECODE, OP_TREE = 0, 1

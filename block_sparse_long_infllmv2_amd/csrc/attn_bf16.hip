@@ -38,7 +38,7 @@ namespace infllmv2 {
 template <int D>
 struct Lds {
   static constexpr int kKStride = D + 8;         // bf16 elements per staged K row
-  static constexpr int kVStride = kChunk + 4;    // bf16 elements per staged V^T row
+  static constexpr int kVStride = kChunk + 8;    // bf16 elements per staged V^T row
   static constexpr int kKElems = kChunk * kKStride;
   static constexpr int kVElems = D * kVStride;
   static constexpr int kStageElems = kKElems + kVElems;
@@ -48,61 +48,96 @@ struct Lds {
 // ---------------------------------------------------------------------------
 // Staging of one 64-key chunk: keys [key0, key0 + nvalid) of a K/V row block.
 // ---------------------------------------------------------------------------
+// V^T rows hold the 64 keys of a chunk in a permuted order: key bits 2 and 3
+// are swapped, so that the 8 keys one lane needs for a P.V k-step
+// (16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}) sit in 16 contiguous bytes.
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
 template <int D, int NT>
 struct Stager {
-  static constexpr int kKPieces = kChunk * D / 8;        // 16-byte pieces of K
-  static constexpr int kKPer = (kKPieces + NT - 1) / NT;
-  static constexpr int kVJobs = (kChunk / 2) * (D / 8);  // (key pair, 8 dims)
+  // K: thread t owns kKPer consecutive keys of one 16-byte column chunk:
+  //    key = kKPer * (t / CPR) + i, chunk = t % CPR  (CPR = D/8 chunks per row).
+  //    Its global pieces sit at immediate offsets 0, 2D, 4D, ... bytes.
+  // V: thread t owns key pairs kp = t % 32 for chunks c = t / 32 + (NT/32) * i,
+  //    i.e. rows 2kp and 2kp+1 of kVPer chunks (again immediate offsets).
+  static constexpr int CPR = D / 8;
+  static constexpr int kKPer = kChunk * CPR / NT;
+  static constexpr int kVJobs = (kChunk / 2) * CPR;
   static constexpr int kVPer = (kVJobs + NT - 1) / NT;
+  static_assert(kKPer >= 1 && (kChunk * CPR) % NT == 0, "K staging shape");
   u32x4 kr[kKPer];
   u32x4 vr[kVPer][2];
 
-  // kbase/vbase point at key 0 of the chunk; nvalid keys are real, the rest
-  // are zero-filled so that masked lanes never multiply garbage.
+  __device__ static __forceinline__ int k_key0(int tid) { return kKPer * (tid / CPR); }
+  __device__ static __forceinline__ int k_chunk(int tid) { return tid % CPR; }
+  __device__ static __forceinline__ int v_pair(int tid) { return tid % (kChunk / 2); }
+  __device__ static __forceinline__ int v_chunk(int tid, int i) {
+    return tid / (kChunk / 2) + (NT / (kChunk / 2)) * i;
+  }
+
+  // kbase/vbase point at key 0 of the chunk (or at any valid row when
+  // nvalid == 0); keys >= nvalid are zero-filled so that masked lanes never
+  // multiply garbage.  Full chunks take the branch-free path.
   __device__ __forceinline__ void load(const uint16_t* kbase, const uint16_t* vbase,
                                        int nvalid, int tid) {
+    const int kk0 = k_key0(tid), kc = k_chunk(tid);
+    const int vk0 = 2 * v_pair(tid);
+    if (nvalid == kChunk) {
+      const uint16_t* kp = kbase + kk0 * D + kc * 8;
+#pragma unroll
+      for (int i = 0; i < kKPer; ++i) kr[i] = ldg16(kp + i * D);
+      const uint16_t* vp = vbase + vk0 * D;
+#pragma unroll
+      for (int i = 0; i < kVPer; ++i) {
+        const int c = v_chunk(tid, i);
+        if (kVJobs % NT != 0 && c >= CPR) break;
+        vr[i][0] = ldg16(vp + c * 8);
+        vr[i][1] = ldg16(vp + D + c * 8);
+      }
+      return;
+    }
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < kKPer; ++i) {
-      const int pc = tid + i * NT;
-      const int key = pc / (D / 8), c = pc % (D / 8);
-      kr[i] = (pc < kKPieces && key < nvalid) ? ldg16(kbase + (int64_t)key * D + c * 8) : z;
+      const int key = kk0 + i;
+      const bool ok = key < nvalid;
+      const u32x4 x = ldg16(kbase + (ok ? key : 0) * D + kc * 8);
+      kr[i] = ok ? x : z;
     }
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) {
-      const int jb = tid + i * NT;
-      const int kp = jb % (kChunk / 2), c = jb / (kChunk / 2);
-      const int k0 = 2 * kp;
-      const bool in = jb < kVJobs;
-      vr[i][0] = (in && k0 < nvalid) ? ldg16(vbase + (int64_t)k0 * D + c * 8) : z;
-      vr[i][1] = (in && k0 + 1 < nvalid) ? ldg16(vbase + (int64_t)(k0 + 1) * D + c * 8) : z;
+      const int c = v_chunk(tid, i);
+      const bool in = c < CPR;
+      const bool ok0 = in && vk0 < nvalid, ok1 = in && vk0 + 1 < nvalid;
+      const u32x4 x0 = ldg16(vbase + (ok0 ? vk0 : 0) * D + (in ? c : 0) * 8);
+      const u32x4 x1 = ldg16(vbase + (ok1 ? vk0 + 1 : 0) * D + (in ? c : 0) * 8);
+      vr[i][0] = ok0 ? x0 : z;
+      vr[i][1] = ok1 ? x1 : z;
     }
   }
 
   __device__ __forceinline__ void store(uint16_t* stage, int tid) const {
-    uint16_t* Ks = stage;
-    uint16_t* Vt = stage + Lds<D>::kKElems;
+    uint16_t* Ks = stage + k_key0(tid) * Lds<D>::kKStride + k_chunk(tid) * 8;
 #pragma unroll
-    for (int i = 0; i < kKPer; ++i) {
-      const int pc = tid + i * NT;
-      if (pc >= kKPieces) break;
-      const int key = pc / (D / 8), c = pc % (D / 8);
-      *reinterpret_cast<u32x4*>(Ks + key * Lds<D>::kKStride + c * 8) = kr[i];
-    }
+    for (int i = 0; i < kKPer; ++i)
+      *reinterpret_cast<u32x4*>(Ks + i * Lds<D>::kKStride) = kr[i];
+    // keys 2kp, 2kp+1 stay adjacent in the permuted V^T row order
+    uint16_t* Vt = stage + Lds<D>::kKElems + vt_pos(2 * v_pair(tid));
 #pragma unroll
     for (int i = 0; i < kVPer; ++i) {
-      const int jb = tid + i * NT;
-      if (jb >= kVJobs) break;
-      const int kp = jb % (kChunk / 2), c = jb / (kChunk / 2);
+      const int c = v_chunk(tid, i);
+      if (kVJobs % NT != 0 && c >= CPR) break;
       const uint32_t a[4] = {vr[i][0].x, vr[i][0].y, vr[i][0].z, vr[i][0].w};
       const uint32_t b[4] = {vr[i][1].x, vr[i][1].y, vr[i][1].z, vr[i][1].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // dims c*8 + 2e (low halves) and c*8 + 2e + 1 (high halves)
-        const uint32_t lo = (a[e] & 0xffffu) | (b[e] << 16);
-        const uint32_t hi = (a[e] >> 16) | (b[e] & 0xffff0000u);
-        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e) * Lds<D>::kVStride + 2 * kp) = lo;
-        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e + 1) * Lds<D>::kVStride + 2 * kp) = hi;
+        const uint32_t lo = __builtin_amdgcn_perm(b[e], a[e], 0x05040100u);
+        const uint32_t hi = __builtin_amdgcn_perm(b[e], a[e], 0x07060302u);
+        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e) * Lds<D>::kVStride) = lo;
+        *reinterpret_cast<uint32_t*>(Vt + (c * 8 + 2 * e + 1) * Lds<D>::kVStride) = hi;
       }
     }
   }
@@ -110,7 +145,12 @@ struct Stager {
 
 // ---------------------------------------------------------------------------
 // Per-wave online-softmax state for 32 query rows (one row per lane column).
+// The running max m is only raised when a block's max exceeds it by more
+// than kRescaleSlack (log2 units): exponentials then stay below 2^slack, which
+// float32 sums and bf16 P fragments hold without loss, and the O rescale runs
+// rarely.  The result is unchanged: numerator and denominator use the same m.
 // ---------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.0f;
 template <int D>
 struct RowState {
   bf16x8 q[D / 16];      // Q^T B-operand fragments (row = lane % 32)
@@ -129,18 +169,21 @@ struct RowState {
   // One staged 64-key chunk.  `lim` = largest valid key offset (0..63) inside
   // the chunk for this lane's row, or -1 if the row keeps none of it.
   // `draft_bits` (tree chunk) restricts the valid offsets further.
-  __device__ __forceinline__ void step(const uint16_t* stage, int lim, bool use_bits,
-                                       uint64_t draft_bits, float scale_log2, bool tile1) {
+  // P^T fragments of one chunk: k-step t of key tile kt.
+  struct PFrag { bf16x8 f[2][2]; };
+
+  // S^T = K Q^T for one staged chunk, masked online softmax; returns the
+  // P^T fragments (and rescales O when the running max moves).
+  __device__ __forceinline__ PFrag scores(const uint16_t* stage, int lim, bool use_bits,
+                                          uint64_t draft_bits, float scale_log2) {
     const int lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const uint16_t* Ks = stage;
-    const uint16_t* Vt = stage + Lds<D>::kKElems;
     f32x16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kt][v] = 0.0f;
-      if (kt == 1 && !tile1) continue;
       const uint16_t* krow = Ks + (32 * kt + col) * Lds<D>::kKStride + 8 * half;
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
@@ -151,7 +194,7 @@ struct RowState {
     // Scale into the log2 domain, mask, row max, exponentials.  Common case
     // (every row of the wave keeps all 64 keys or none of them): no per-key
     // masking -- rows that keep nothing subtract +inf, so their p is 0.
-    const bool partial = (lim >= 0 && lim < 63) || use_bits;
+    const bool partial = (lim >= 0 && lim < kChunk - 1) || use_bits;
     const bool keep = lim >= 0;
     float m_new, alpha, psum = 0.0f;
     if (!__ballot(partial)) {
@@ -162,7 +205,7 @@ struct RowState {
         for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
       mx = keep ? mx * scale_log2 : -INFINITY;
       mx = fmaxf(mx, swap_halves(mx));
-      m_new = fmaxf(m, mx);
+      m_new = mx > m + kRescaleSlack ? mx : m;
       alpha = fast_exp2(m - m_new);
       const float msub = keep ? m_new : INFINITY;
 #pragma unroll
@@ -187,7 +230,7 @@ struct RowState {
           mx = fmaxf(mx, x);
         }
       mx = fmaxf(mx, swap_halves(mx));
-      m_new = fmaxf(m, mx);
+      m_new = mx > m + kRescaleSlack ? mx : m;
       alpha = fast_exp2(m - m_new);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -207,27 +250,34 @@ struct RowState {
         for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
     }
     // P^T fragments: k-step t of key tile kt uses accumulator entries 8t..8t+7
-    bf16x8 pb[2][2];
+    PFrag pf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[kt][t][e] = (__bf16)s[kt][8 * t + e];
-    // O^T += V^T P^T; A-operand element e of half h <-> key 16t + 8(e/4) + 4h + e%4
+        for (int e = 0; e < 8; ++e) pf.f[kt][t][e] = (__bf16)s[kt][8 * t + e];
+    return pf;
+  }
+
+  // O^T += V^T P^T; A-operand element e of half h <-> key 16t + 8(e/4) + 4h + e%4.
+  // Run for every staged chunk (with zero P when the wave keeps none of it),
+  // so that O flows through the same instructions on every iteration.
+  __device__ __forceinline__ void pv(const uint16_t* stage, const PFrag& pf) {
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31, half = lane >> 5;
+    const uint16_t* Vt = stage + Lds<D>::kKElems;
+    const auto& pb = pf.f;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const uint16_t* vrow = Vt + (32 * dt + col) * Lds<D>::kVStride + 4 * half;
+      const uint16_t* vrow = Vt + (32 * dt + col) * Lds<D>::kVStride + 8 * half;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        if (kt == 1 && !tile1) continue;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const uint16_t* src = vrow + 32 * kt + 16 * t;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(src);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(src + 8);
-          u32x4 w = {lo.x, lo.y, hi.x, hi.y};
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&w);
+          // keys 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}: permuted layout
+          // puts them at positions 16t + 8h .. +8
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * kt + 16 * t);
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][t], o[dt], 0, 0, 0);
         }
       }
@@ -290,12 +340,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int* total, int* lds) {
 }
 
 // Union of the kept-block lists of TT tokens: sorted unique block ids with a
-// bitmask of the tokens (bit t) that kept each.  `sortbuf` holds N >= TT*topk
-// (power of two) words; returns the union length.
+// bitmask of the tokens (bit t) that kept each, written to ents[] as
+// (block, mask).  `sortbuf` holds N >= TT*topk (power of two) words; returns
+// the union length.
 template <int NT, int TT>
 __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, int n_tok,
-                           int topk, int64_t n_b, uint32_t* sortbuf, int N, int32_t* ublk,
-                           uint32_t* umask, int* scan_lds) {
+                           int topk, int n_b, uint32_t* sortbuf, int N, int2* ents,
+                           int* scan_lds) {
   for (int i = threadIdx.x; i < N; i += NT) {
     uint32_t key = 0xffffffffu;
     const int t = i / topk, j = i % topk;
@@ -325,8 +376,7 @@ __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, 
       for (int i2 = i; i2 < N && sortbuf[i2] != 0xffffffffu && (sortbuf[i2] >> 5) == (key >> 5);
            ++i2)
         msk |= 1u << (sortbuf[i2] & 31u);
-      ublk[slot] = (int32_t)(key >> 5);
-      umask[slot] = msk;
+      ents[slot] = make_int2((int)(key >> 5), (int)msk);
       ++slot;
     }
   }
@@ -334,9 +384,14 @@ __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, 
   return total;
 }
 
+// Entries a split workgroup may hold in LDS (host keeps units per split below).
+constexpr int kSplitEntryCap = 64;
+
 // ---------------------------------------------------------------------------
 // The attention kernel.
 //   W waves, each 32 rows = TPW tokens x G heads; TT = W * TPW tokens.
+// Indices are 32-bit inside the kernel: the host rejects caches with more
+// than 2^31 - 1 tokens per (sequence, KV head).
 // ---------------------------------------------------------------------------
 template <int D, int G, int W, int MODE>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
@@ -347,10 +402,9 @@ void attn_bf16_kernel(AttnArgs a) {
   static_assert(TT <= 32, "token bitmask is 32 bits");
   static_assert(MODE != kPrefill || TT > 1, "prefill tiles hold several tokens");
   constexpr int SORT_N = (MODE == kPrefill) ? TT * kSortCap : 0;
-  constexpr int UCAP = (MODE == kPrefill) ? TT * kSortCap : 1;
+  constexpr int ECAP = (MODE == kPrefill) ? TT * kSortCap : kSplitEntryCap;
   __shared__ __attribute__((aligned(16))) uint16_t stage[2 * Lds<D>::kStageElems];
-  __shared__ int32_t ublk[UCAP];
-  __shared__ uint32_t umask[UCAP];
+  __shared__ int2 ents[ECAP];
   __shared__ int scan_lds[NT / 64];
   static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
 
@@ -370,26 +424,24 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   // tokens of this workgroup and their query positions
-  int64_t n_keys;                   // keys of the sequence (context for tree)
-  int tok0, n_tok;
-  if constexpr (MODE == kPrefill) {
-    n_keys = a.n_k;
-    tok0 = tile * TT;
-    n_tok = min(TT, a.n_rows - tok0);
-  } else if constexpr (MODE == kDecode) {
+  int n_keys, tok0, n_tok;
+  if constexpr (MODE == kDecode) {
     // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
-    int64_t L = a.seqlens[seq];
-    n_keys = L < 1 ? 1 : (L > a.n_k ? a.n_k : L);
+    const int L = a.seqlens[seq];
+    n_keys = L < 1 ? 1 : (L > (int)a.n_k ? (int)a.n_k : L);
     tok0 = seq;
     n_tok = 1;
   } else {
-    n_keys = a.n_k;
+    n_keys = (int)a.n_k;
     tok0 = tile * TT;
     n_tok = min(TT, a.n_rows - tok0);
   }
   const bool dense = n_keys < a.dense_len || a.block_idx == nullptr;
-  const int64_t n_b = (n_keys + a.B - 1) / a.B;
+  const int n_b = (n_keys + a.B - 1) / a.B;
   const int cpb = (a.B + kChunk - 1) / kChunk;            // chunks per block
+  const uint32_t full_mask = n_tok >= 32 ? 0xffffffffu : ((1u << n_tok) - 1u);
+  // first query position of the tile (prefill: consecutive positions)
+  const int p0 = (MODE == kPrefill) ? (int)a.n_k - a.n_rows + tok0 : n_keys - 1;
 
   // this lane's row
   const int t_in_wave = col / G, head_in_group = col % G;
@@ -398,40 +450,33 @@ void attn_bf16_kernel(AttnArgs a) {
   const bool row_ok = my_t < n_tok;
   const int my_row = tok0 + (row_ok ? my_t : 0);
   const int my_head = g * G + head_in_group;
-  int64_t my_pos;
-  if constexpr (MODE == kPrefill) my_pos = a.n_k - a.n_rows + my_row;
-  else my_pos = n_keys - 1;
-  const int64_t my_bown = my_pos / a.B;
+  const int my_pos = (MODE == kPrefill) ? p0 + (row_ok ? my_t : 0) : n_keys - 1;
 
-  // ---- unit list -----------------------------------------------------------
-  // entries: kept blocks (or all blocks when dense), plus the draft chunk
+  // ---- entries (kept blocks with token masks) and this workgroup's units ---
+  const bool has_draft = MODE == kTree;
   int n_entries;
-  const int32_t* dec_list = nullptr;
   if constexpr (MODE == kPrefill) {
     if (dense) {
-      const int64_t last_pos = a.n_k - a.n_rows + tok0 + n_tok - 1;
-      n_entries = (int)(last_pos / a.B + 1);
+      n_entries = (p0 + n_tok - 1) / a.B + 1;
     } else {
       int N = 1;
       while (N < TT * a.topk) N <<= 1;
       if (N < NT) N = NT;
       n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, n_b,
-                                      reinterpret_cast<uint32_t*>(stage), N, ublk, umask,
-                                      scan_lds);
+                                      reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
     }
   } else if constexpr (MODE == kDecode) {
     if (dense) {
-      n_entries = (int)n_b;
+      n_entries = n_b;
     } else {
-      dec_list = a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk;
+      const int32_t* lst = a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk;
       int n = 0;
-      while (n < a.topk && dec_list[n] >= 0 && dec_list[n] < n_b) ++n;
+      while (n < a.topk && lst[n] >= 0 && lst[n] < n_b) ++n;
       n_entries = n;
     }
   } else {
-    n_entries = dense ? (int)n_b : a.union_len[g];
+    n_entries = dense ? n_b : a.union_len[g];
   }
-  const bool has_draft = MODE == kTree;
   const int n_units_total = n_entries * cpb + (has_draft ? 1 : 0);
   int u_begin = 0, u_end = n_units_total;
   if constexpr (MODE != kPrefill) {
@@ -440,44 +485,58 @@ void attn_bf16_kernel(AttnArgs a) {
     u_begin = min(n_units_total, split * per);
     u_end = min(n_units_total, u_begin + per);
   }
-
-  // unit -> (block id, key0 of the chunk, #valid keys, token bitmask)
-  auto unit_info = [&](int u, int64_t& key0, int& nvalid, uint32_t& tmask, bool& is_draft) {
-    is_draft = has_draft && u == n_entries * cpb;
-    if (is_draft) {
-      key0 = 0;
-      nvalid = a.n_rows;
-      tmask = 0xffffffffu;
-      return;
+  // split modes: copy this slice's entries into LDS (entry e -> ents[e - e_base])
+  int e_base = 0;
+  if constexpr (MODE != kPrefill) {
+    if (!dense) {
+      e_base = u_begin / cpb;
+      const int e_end = min(n_entries, (u_end + cpb - 1) / cpb);
+      for (int e = e_base + tid; e < e_end && e - e_base < kSplitEntryCap; e += NT) {
+        if constexpr (MODE == kDecode) {
+          ents[e - e_base] = make_int2(a.block_idx[((int64_t)seq * a.h_kv + g) * a.topk + e], 1);
+        } else {
+          const int64_t ix = (int64_t)g * a.union_cap + e;
+          ents[e - e_base] = make_int2(a.union_blk[ix], (int)(uint32_t)(a.union_mask[ix] >> tok0));
+        }
+      }
+      __syncthreads();
     }
-    const int e = u / cpb, c = u % cpb;
-    int64_t b;
+  }
+
+  // unit -> first key, #valid keys, token mask, draft flag
+  struct UnitInfo { int key0, nv; uint32_t tm; bool isd; };
+  auto unit_info = [&](int u) -> UnitInfo {
+    UnitInfo r;
+    r.isd = has_draft && u == n_entries * cpb;
+    if (r.isd) {
+      r.key0 = 0; r.nv = a.n_rows; r.tm = full_mask;
+      return r;
+    }
+    int e = u, c = 0;
+    if (cpb != 1) { e = u / cpb; c = u - e * cpb; }
+    int b;
     if (dense) {
       b = e;
-      // token t keeps block b iff b <= its own block
-      tmask = 0;
       if constexpr (MODE == kPrefill) {
-        const int64_t p0 = a.n_k - a.n_rows + tok0;
-        for (int t = 0; t < n_tok; ++t)
-          if (b <= (p0 + t) / a.B) tmask |= 1u << t;
+        // token t keeps block b iff b <= (p0 + t) / B, i.e. t >= b*B - p0
+        const int t_min = b * a.B - p0;
+        r.tm = t_min <= 0 ? full_mask : (t_min >= 32 ? 0u : (full_mask & (0xffffffffu << t_min)));
       } else {
-        tmask = (1u << n_tok) - 1u;
-        if (n_tok == 32) tmask = 0xffffffffu;
+        r.tm = full_mask;
       }
-    } else if constexpr (MODE == kPrefill) {
-      b = ublk[e];
-      tmask = umask[e];
-    } else if constexpr (MODE == kDecode) {
-      b = dec_list[e];
-      tmask = 1u;
     } else {
-      b = a.union_blk[(int64_t)g * a.union_cap + e];
-      tmask = (uint32_t)(a.union_mask[(int64_t)g * a.union_cap + e] >> tok0);
+      const int2 en = ents[e - e_base];
+      b = en.x;
+      r.tm = (uint32_t)en.y;
     }
-    key0 = b * a.B + (int64_t)c * kChunk;
-    const int64_t blk_end = min((b + 1) * (int64_t)a.B, n_keys);
-    const int64_t nv = blk_end - key0;
-    nvalid = nv > kChunk ? kChunk : (nv < 0 ? 0 : (int)nv);
+    r.key0 = b * a.B + c * kChunk;
+    const int blk_end = min((b + 1) * a.B, n_keys);
+    r.nv = max(0, min(kChunk, blk_end - r.key0));
+    // identical in every lane: keep them in scalar registers
+    r.key0 = __builtin_amdgcn_readfirstlane(r.key0);
+    r.nv = __builtin_amdgcn_readfirstlane(r.nv);
+    r.tm = __builtin_amdgcn_readfirstlane(r.tm);
+    return r;
   };
 
   const int64_t kv_head_off = (MODE == kDecode ? ((int64_t)seq * a.h_kv + g) : (int64_t)g) *
@@ -486,6 +545,12 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vbase_seq = a.v + kv_head_off;
   const uint16_t* kdraft = has_draft ? a.k_draft + (int64_t)g * a.n_rows * D : nullptr;
   const uint16_t* vdraft = has_draft ? a.v_draft + (int64_t)g * a.n_rows * D : nullptr;
+  auto kptr = [&](const UnitInfo& ui) {
+    return ui.isd ? kdraft : kbase_seq + (ui.nv > 0 ? (int64_t)ui.key0 * D : 0);
+  };
+  auto vptr = [&](const UnitInfo& ui) {
+    return ui.isd ? vdraft : vbase_seq + (ui.nv > 0 ? (int64_t)ui.key0 * D : 0);
+  };
 
   RowState<D> st;
   st.init();
@@ -497,34 +562,39 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 
   Stager<D, NT> sg;
+  UnitInfo cur = {0, 0, 0u, false};
   if (u_begin < u_end) {
-    int64_t key0; int nv; uint32_t tm; bool isd;
-    unit_info(u_begin, key0, nv, tm, isd);
-    sg.load(isd ? kdraft : kbase_seq + key0 * D, isd ? vdraft : vbase_seq + key0 * D, nv, tid);
+    cur = unit_info(u_begin);
+    sg.load(kptr(cur), vptr(cur), cur.nv, tid);
   }
   for (int u = u_begin; u < u_end; ++u) {
     uint16_t* buf = stage + ((u - u_begin) & 1) * Lds<D>::kStageElems;
     sg.store(buf, tid);
     __syncthreads();
-    int64_t key0; int nv; uint32_t tm; bool isd;
-    unit_info(u, key0, nv, tm, isd);
+    UnitInfo nxt = cur;
     if (u + 1 < u_end) {
-      int64_t k1; int n1; uint32_t t1; bool d1;
-      unit_info(u + 1, k1, n1, t1, d1);
-      sg.load(d1 ? kdraft : kbase_seq + k1 * D, d1 ? vdraft : vbase_seq + k1 * D, n1, tid);
+      nxt = unit_info(u + 1);
+      sg.load(kptr(nxt), vptr(nxt), nxt.nv, tid);
     }
     // which of my rows use this chunk, and up to which key offset
-    const bool keep = row_ok && ((tm >> my_t) & 1u);
     int lim = -1;
-    if (keep) {
-      if (isd) {
-        lim = nv - 1;
-      } else {
-        const int64_t last = min(my_pos, key0 + nv - 1) - key0;
-        lim = last < 0 ? -1 : (int)last;
-      }
+    if (row_ok && ((cur.tm >> my_t) & 1u)) {
+      const int last = (cur.isd ? cur.nv - 1 : min(my_pos - cur.key0, cur.nv - 1));
+      lim = last < 0 ? -1 : last;
     }
-    if (__ballot(lim >= 0)) st.step(buf, lim, isd, my_bits, a.scale_log2, nv > 32);
+    typename RowState<D>::PFrag pf;
+    if (__ballot(lim >= 0)) {
+      pf = st.scores(buf, lim, cur.isd, my_bits, a.scale_log2);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf.f[kt][t][e] = (__bf16)0.0f;
+    }
+    st.pv(buf, pf);
+    cur = nxt;
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -671,6 +741,7 @@ namespace {
 // decode and tree verification while keeping the float32 partials small.
 constexpr int kMaxDecodeSplits = 32;
 constexpr int kMaxTreeSplits = 32;
+constexpr int kMaxCombineSplits = 64;      // lanes of the combine kernel
 
 template <int D, int G, int W, int MODE>
 int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
@@ -754,9 +825,18 @@ int64_t decode_max_entries(int64_t max_seqlen, const Resolved& r) {
   return r.topk > dense_max ? r.topk : dense_max;
 }
 
+// Split count for `units` 64-key units: at most `max_default` splits, but
+// enough that one split's entries fit the kernel's LDS list.  Callers reject
+// counts above kMaxCombineSplits.
+int64_t split_count(int64_t units, int64_t cpb, int64_t max_default) {
+  int64_t n = units < max_default ? units : max_default;
+  const int64_t need = ceil_div(units, (int64_t)(kSplitEntryCap - 1) * cpb);
+  return n < need ? need : (n < 1 ? 1 : n);
+}
+
 int64_t decode_splits(int64_t max_seqlen, const Resolved& r) {
-  const int64_t units = decode_max_entries(max_seqlen, r) * ceil_div(r.B, kChunk);
-  return units < kMaxDecodeSplits ? units : kMaxDecodeSplits;
+  const int64_t cpb = ceil_div(r.B, kChunk);
+  return split_count(decode_max_entries(max_seqlen, r) * cpb, cpb, kMaxDecodeSplits);
 }
 
 int64_t tree_union_cap(int n_draft, int64_t n_ctx, const Resolved& r) {
@@ -771,7 +851,7 @@ int64_t tree_splits(int n_draft, int64_t n_ctx, const Resolved& r) {
   // + 1 entry's worth for the chunk of draft tokens
   const int64_t cpb = ceil_div(r.B, kChunk);
   const int64_t units = entries * cpb + 1;
-  return units < kMaxTreeSplits ? units : kMaxTreeSplits;
+  return split_count(units, cpb, kMaxTreeSplits);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -800,6 +880,7 @@ extern "C" int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_
   INFLLMV2_TRY(check_params(p, d, &r));
   if (!q || !k || !v || !out) return INFLLMV2_ERR_INVALID_ARG;
   if (n_q < 0 || n_k <= 0 || cap < n_k || n_q > n_k) return INFLLMV2_ERR_INVALID_ARG;
+  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
   const bool dense = n_k < r.dense_len;
   if (!dense && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -835,11 +916,13 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   INFLLMV2_TRY(check_params(p, d, &r));
   if (!q || !k || !v || !out || !seqlens) return INFLLMV2_ERR_INVALID_ARG;
   if (batch < 0 || max_seqlen <= 0 || cap < max_seqlen) return INFLLMV2_ERR_INVALID_ARG;
+  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
   if (max_seqlen >= r.dense_len && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return INFLLMV2_ERR_INVALID_ARG;
   if (batch == 0) return INFLLMV2_OK;
   const int64_t n_split = decode_splits(max_seqlen, r);
+  if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
   const size_t need = partial_bytes(batch, h_q, d, n_split);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
   AttnArgs a = {};
@@ -892,15 +975,17 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   if (!q || !k || !v || !k_draft || !v_draft || !tree_mask || !out)
     return INFLLMV2_ERR_INVALID_ARG;
   if (n_draft < 0 || n_draft > 64 || n_ctx <= 0 || cap < n_ctx) return INFLLMV2_ERR_INVALID_ARG;
+  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
   const bool dense = n_ctx < r.dense_len;
   if (!dense && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !aligned16(k_draft) || !aligned16(v_draft))
     return INFLLMV2_ERR_INVALID_ARG;
   if (n_draft == 0) return INFLLMV2_OK;
+  const int64_t n_split = tree_splits(n_draft, n_ctx, r);
+  if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
   const size_t need = tree_workspace_bytes(n_draft, h_q, h_kv, d, n_ctx, r);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
-  const int64_t n_split = tree_splits(n_draft, n_ctx, r);
   const int64_t ucap = tree_union_cap(n_draft, n_ctx, r);
   AttnArgs a = {};
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;

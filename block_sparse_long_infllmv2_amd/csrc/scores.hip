@@ -31,6 +31,7 @@ struct ScoreArgs {
   float* scores;
   int64_t nc_cap, nb_cap;
   int h_q, h_kv, B, ks, s, dense_len, blocks_per_wg, chunks_per_row, batch, max_pos, rows;
+  bool vec_store;             // rows of `scores` are 16-byte aligned
   float scale;
 };
 
@@ -191,27 +192,33 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int
     qh[ks] = *reinterpret_cast<const bf16x8*>(&qlds[0][col][16 * ks + 8 * half]);
     ql[ks] = *reinterpret_cast<const bf16x8*>(&qlds[1][col][16 * ks + 8 * half]);
   }
-  const int64_t pos = pos_lds[col];
+  const int pos = (int)pos_lds[col];
   const int row = r0 + col;
   const bool row_ok = pos >= 0;
-  // visible windows: m*s + ks - 1 <= pos
-  const int64_t n_vis = pos >= a.ks - 1 ? (pos - a.ks + 1) / a.s + 1 : 0;
-  const int64_t b_own = row_ok ? pos / a.B : -1;
-  int64_t tile_max_pos = -1;
-  for (int j = 0; j < kMfmaRows; ++j) tile_max_pos = max(tile_max_pos, pos_lds[j]);
-  const int64_t nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
-  const int64_t n_tiles8 = (nb_tile + 7) / 8;
+  // visible windows: m*s + ks - 1 <= pos  (all indices fit in 32 bits: the
+  // host bounds max_pos)
+  const int n_vis = pos >= a.ks - 1 ? (pos - a.ks + 1) / a.s + 1 : 0;
+  const int b_own = row_ok ? pos / a.B : -1;
+  int tile_max_pos = -1, tile_min_vis = 0x7fffffff;
+  for (int j = 0; j < kMfmaRows; ++j) {
+    const int pj = (int)pos_lds[j];
+    tile_max_pos = max(tile_max_pos, pj);
+    if (pj >= 0) tile_min_vis = min(tile_min_vis, pj >= a.ks - 1 ? (pj - a.ks + 1) / a.s + 1 : 0);
+  }
+  const int nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
+  const int n_tiles8 = (nb_tile + 7) / 8;
   float* out = a.scores + ((int64_t)row * a.h_kv + g) * a.nb_cap;
   const uint16_t* ckb = (const uint16_t*)a.ck + (int64_t)g * a.nc_cap * D;
+  const int nc_cap = (int)min(a.nc_cap, (int64_t)0x7fffffff);
   const float sc = a.scale;
 
   // dot of this lane's query half with one compressed key (VALU), combined
   // over the two half-waves: used for the halo window before a wave's first
   // tile
-  auto single_window = [&](int64_t m) -> float {
+  auto single_window = [&](int m) -> float {
     float part = 0.0f;
-    if (m >= 0 && m < a.nc_cap) {
-      const uint16_t* c = ckb + m * D;
+    if (m >= 0 && m < nc_cap) {
+      const uint16_t* c = ckb + (int64_t)m * D;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         float x[8];
@@ -228,19 +235,19 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int
   // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
   // the halo of a tile's first block is the previous tile's last window,
   // carried in registers (computed directly only for the range's first tile)
-  const int64_t per_wave = (n_tiles8 + 3) / 4;
-  const int64_t t_begin = wave * per_wave;
-  const int64_t t_end = min(n_tiles8, t_begin + per_wave);
+  const int per_wave = (n_tiles8 + 3) / 4;
+  const int t_begin = wave * per_wave;
+  const int t_end = min(n_tiles8, t_begin + per_wave);
   float carry = t_begin < t_end ? single_window(t_begin * 32 - 1) : -INFINITY;
-  for (int64_t t = t_begin; t < t_end; ++t) {
-    const int64_t bt = t * 8;
-    const int64_t mt = bt * 4;                 // first own window of the tile
+  for (int t = t_begin; t < t_end; ++t) {
+    const int bt = t * 8;
+    const int mt = bt * 4;                     // first own window of the tile
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    const int64_t mrow = mt + col;             // A-operand window of this lane
-    const bool in = mrow < a.nc_cap;
-    const uint16_t* crow = ckb + (in ? mrow : 0) * D + 8 * half;
+    const int mrow = mt + col;                 // A-operand window of this lane
+    const bool in = mrow < nc_cap;
+    const uint16_t* crow = ckb + (int64_t)(in ? mrow : 0) * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
@@ -249,32 +256,59 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qh[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ql[ks], acc, 0, 0, 0);
     }
-    // own maxima and last windows per block group q (block bt + 2q + half)
+    // own maxima and last windows per block group q (block bt + 2q + half);
+    // tiles wholly visible to every row of the workgroup skip the masking
     float own[4], last[4];
+    if (mt + 32 <= tile_min_vis) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t m = mt + 8 * q + 4 * half + e;
-        const float x = m < n_vis ? acc[4 * q + e] * sc : -INFINITY;
-        mx = fmaxf(mx, x);
-        if (e == 3) last[q] = x;
+      for (int q = 0; q < 4; ++q) {
+        own[q] = sc * fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
+        last[q] = sc * acc[4 * q + 3];
       }
-      own[q] = mx;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = mt + 8 * q + 4 * half + e;
+          const float x = m < n_vis ? acc[4 * q + e] * sc : -INFINITY;
+          mx = fmaxf(mx, x);
+          if (e == 3) last[q] = x;
+        }
+        own[q] = mx;
+      }
     }
     float other[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) other[q] = swap_halves(last[q]);
     // halo window of block bt + 2q + half is the last own window of the
     // block before it: half 1 <- (q, half 0); half 0 <- (q-1, half 1)
+    float bs[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry);
-      const int64_t b = bt + 2 * q + half;
-      if (row_ok && b <= b_own) out[b] = fmaxf(own[q], halo);
+      bs[q] = fmaxf(own[q], halo);
     }
     carry = other[3];       // for half-0 lanes: last window of block bt + 7
+    // regroup so that half 0 holds blocks bt..bt+3 and half 1 bt+4..bt+7:
+    // half 0 has bt+{0,2,4,6}, half 1 has bt+{1,3,5,7}
+    const float x0 = swap_halves(half ? bs[0] : bs[2]);
+    const float x1 = swap_halves(half ? bs[1] : bs[3]);
+    f32x4 w4;
+    if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }     // bt+0..3
+    else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }     // bt+4..7
+    const int b4 = bt + 4 * half;
+    if (row_ok) {
+      if (b4 + 3 <= b_own && a.vec_store) {
+        *reinterpret_cast<f32x4*>(out + b4) = w4;
+      } else {
+        if (b4 + 0 <= b_own) out[b4 + 0] = w4.x;
+        if (b4 + 1 <= b_own) out[b4 + 1] = w4.y;
+        if (b4 + 2 <= b_own) out[b4 + 2] = w4.z;
+        if (b4 + 3 <= b_own) out[b4 + 3] = w4.w;
+      }
+    }
   }
 }
 
@@ -312,6 +346,7 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.scores = scores; a.nc_cap = nc_cap; a.nb_cap = nb_cap; a.h_q = h_q; a.h_kv = h_kv;
   a.B = r.B; a.ks = r.ks; a.s = r.s; a.dense_len = r.dense_len; a.scale = r.scale;
   a.batch = batch; a.max_pos = max_pos; a.rows = rows;
+  a.vec_store = (nb_cap % 4 == 0) && aligned16(scores);
   // blocks per workgroup: as many as keep the chunk's windows within the LDS
   // buffer (a chunk of n blocks spans at most (n*B + ks - 2)/s + 2 windows)
   int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * r.s - r.ks + 2) / r.B);

@@ -156,6 +156,108 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(TopkArgs a) {
   for (int i = tot + tid; i < a.topk; i += kTopkThreads) out[i] = -1;
 }
 
+
+// ---------------------------------------------------------------------------
+// One wave per (row, KV head) when the eligible blocks fit in registers
+// (64 * KPL of them).  Keys live in registers (KPL per lane, block
+// b = lane + 64 j); a bitwise search builds the threshold T from the most
+// significant bit down, counting keys >= candidate with ballots and scalar
+// popcounts -- no LDS atomics, no barriers.  The search stops early as soon
+// as some candidate admits exactly `need` keys.  The ascending output order
+// comes from ballot prefix counts (block b = lane + 64 j precedes b' when
+// j < j', or j == j' and lane < lane').
+// ---------------------------------------------------------------------------
+template <int KPL>
+__global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n_units) {
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= n_units) return;                   // whole wave leaves
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  const int r = unit / a.h_kv, g = unit % a.h_kv;
+  int32_t* out = a.block_idx + ((int64_t)r * a.h_kv + g) * a.topk;
+  const int seq = a.row_seq ? a.row_seq[r] : 0;
+  bool skip = seq < 0 || seq >= a.batch;
+  const int64_t L = skip ? 0 : a.seqlens[seq];
+  const int64_t pos = a.row_pos ? a.row_pos[r] : L - 1;
+  skip = skip || L < a.dense_len || pos < 0 || pos >= L || pos / a.B + 1 > a.nb_cap;
+  if (skip) {
+    for (int i = lane; i < a.topk; i += 64) out[i] = -1;
+    return;
+  }
+  const int b_own = (int)(pos / a.B);
+  const int n_elig = b_own + 1;
+  if (n_elig <= a.topk) {
+    for (int i = lane; i < a.topk; i += 64) out[i] = i < n_elig ? i : -1;
+    return;
+  }
+  const int f_init = a.init < n_elig ? a.init : n_elig;
+  const int f_lo = b_own - a.local + 1 > 0 ? b_own - a.local + 1 : 0;
+  const int overlap = f_init > f_lo ? f_init - f_lo : 0;
+  const int n_forced = f_init + (n_elig - f_lo) - overlap;
+  const int need = a.topk - n_forced;
+  const float* S = a.scores + ((int64_t)r * a.h_kv + g) * a.nb_cap;
+
+  // 0 = not a candidate (forced or past the eligible range); candidates >= 1
+  uint32_t key[KPL];
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int b = lane + 64 * j;
+    uint32_t k = 0;
+    if (b < n_elig && b >= f_init && b < f_lo) {
+      k = orderable_key(S[b]);
+      k = k == 0 ? 1u : k;
+    }
+    key[j] = k;
+  }
+  // T = largest value with #(key >= T) >= need (the need-th largest key)
+  uint32_t T = 0;
+  bool exact = need <= 0;       // nothing to choose, or #(key >= T) == need
+  if (need > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+      if (cnt >= need) {
+        T = cand;
+        if (cnt == need) { exact = true; break; }
+      }
+    }
+  }
+  // keys > T are kept; of the keys == T the lowest-indexed ones fill the rest
+  int take = 0;
+  if (!exact) {
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
+    take = need - gt;
+  }
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int b = lane + 64 * j;
+    const bool forced = b < n_elig && (b < f_init || b >= f_lo);
+    bool sel;
+    if (need <= 0) {
+      sel = forced;
+    } else if (exact) {
+      sel = forced || key[j] >= T;
+    } else {
+      const uint64_t eqm = __ballot(key[j] == T);
+      const int rank = eq_seen + __popcll(eqm & below);
+      eq_seen += __popcll(eqm);
+      sel = forced || key[j] > T || (key[j] == T && rank < take);
+    }
+    const uint64_t selm = __ballot(sel);
+    if (sel) {
+      const int slot = base + __popcll(selm & below);
+      if (slot < a.topk) out[slot] = b;
+    }
+    base += __popcll(selm);
+  }
+  for (int i = base + lane; i < a.topk; i += 64) out[i] = -1;
+}
+
 }  // namespace infllmv2
 
 using namespace infllmv2;
@@ -175,7 +277,17 @@ extern "C" int infllmv2_select_topk(const float* scores, int32_t rows,
   a.scores = scores; a.row_seq = row_seq; a.row_pos = row_pos; a.seqlens = seqlens;
   a.block_idx = block_idx; a.nb_cap = nb_cap; a.h_kv = h_kv; a.B = r.B; a.topk = r.topk;
   a.init = r.init; a.local = r.local; a.dense_len = r.dense_len; a.batch = batch;
-  hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)(rows * h_kv)), dim3(kTopkThreads), 0,
-                     (hipStream_t)stream, a);
+  const int n_units = rows * h_kv;
+  hipStream_t st = (hipStream_t)stream;
+  // eligible blocks per row <= nb_cap: registers hold 64 * KPL keys per wave
+  if (nb_cap <= 64 * 32)
+    hipLaunchKernelGGL(select_topk_wave_kernel<32>, dim3((unsigned)((n_units + 3) / 4)),
+                       dim3(256), 0, st, a, n_units);
+  else if (nb_cap <= 64 * 64)
+    hipLaunchKernelGGL(select_topk_wave_kernel<64>, dim3((unsigned)((n_units + 3) / 4)),
+                       dim3(256), 0, st, a, n_units);
+  else
+    hipLaunchKernelGGL(select_topk_kernel, dim3((unsigned)n_units), dim3(kTopkThreads), 0, st,
+                       a);
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
 }
