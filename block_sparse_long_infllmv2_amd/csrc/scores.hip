@@ -129,9 +129,10 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 // tiles of the window range, so qsum is built once (in LDS) per workgroup.
 // ---------------------------------------------------------------------------
 constexpr int kMfmaRows = 32;
+constexpr int kMfmaWaves = 8;            // waves per workgroup, splitting the windows
 
 template <int D>
-__global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
+__global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
   constexpr int KS = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
   __shared__ int64_t pos_lds[kMfmaRows];
@@ -146,7 +147,7 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int
   if (L < a.dense_len) return;
 
   // group-summed query rows -> hi/lo bf16 in LDS; positions
-  for (int it = tid; it < kMfmaRows * (D / 8); it += 256) {
+  for (int it = tid; it < kMfmaRows * (D / 8); it += kMfmaWaves * 64) {
     const int rr = it / (D / 8), c = it % (D / 8);
     const int row = r0 + rr;
     float acc[8];
@@ -235,24 +236,37 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(ScoreArgs a, int
   // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
   // the halo of a tile's first block is the previous tile's last window,
   // carried in registers (computed directly only for the range's first tile)
-  const int per_wave = (n_tiles8 + 3) / 4;
+  const int per_wave = (n_tiles8 + kMfmaWaves - 1) / kMfmaWaves;
   const int t_begin = wave * per_wave;
   const int t_end = min(n_tiles8, t_begin + per_wave);
   float carry = t_begin < t_end ? single_window(t_begin * 32 - 1) : -INFINITY;
-  for (int t = t_begin; t < t_end; ++t) {
-    const int bt = t * 8;
-    const int mt = bt * 4;                     // first own window of the tile
-    f32x16 acc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-    const int mrow = mt + col;                 // A-operand window of this lane
+  // A-operand fragments of a tile: window mt + col, dims 16ks + 8half
+  auto load_tile = [&](int tt, u32x4* fr) {
+    const int mrow = tt * 32 + col;
     const bool in = mrow < nc_cap;
     const uint16_t* crow = ckb + (int64_t)(in ? mrow : 0) * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4 wv = {0u, 0u, 0u, 0u};
-      if (in) wv = ldg16(crow + 16 * ks);
-      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&wv);
+      const u32x4 wv = ldg16(crow + 16 * ks);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      fr[ks] = in ? wv : z;
+    }
+  };
+  u32x4 frag[KS];
+  if (t_begin < t_end) load_tile(t_begin, frag);
+  for (int t = t_begin; t < t_end; ++t) {
+    const int bt = t * 8;
+    const int mt = bt * 4;                     // first own window of the tile
+    u32x4 cur[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) cur[ks] = frag[ks];
+    if (t + 1 < t_end) load_tile(t + 1, frag);  // next tile's loads in flight
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cur[ks]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qh[ks], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ql[ks], acc, 0, 0, 0);
     }
@@ -364,9 +378,9 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
     if ((int64_t)n_row_tiles * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
     dim3 grid((unsigned)(n_row_tiles * h_kv));
     if (d == 128)
-      hipLaunchKernelGGL(block_scores_mfma_kernel<128>, grid, dim3(256), 0, st, a, n_row_tiles);
+      hipLaunchKernelGGL(block_scores_mfma_kernel<128>, grid, dim3(kMfmaWaves * 64), 0, st, a, n_row_tiles);
     else
-      hipLaunchKernelGGL(block_scores_mfma_kernel<64>, grid, dim3(256), 0, st, a, n_row_tiles);
+      hipLaunchKernelGGL(block_scores_mfma_kernel<64>, grid, dim3(kMfmaWaves * 64), 0, st, a, n_row_tiles);
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   if (dtype == INFLLMV2_BF16)
