@@ -393,7 +393,7 @@ constexpr int kSplitEntryCap = 64;
 // Indices are 32-bit inside the kernel: the host rejects caches with more
 // than 2^31 - 1 tokens per (sequence, KV head).
 // ---------------------------------------------------------------------------
-template <int D, int G, int W, int MODE>
+template <int D, int G, int W, int MODE, int PF = 1>
 __global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int NT = W * 64;
@@ -561,30 +561,16 @@ void attn_bf16_kernel(AttnArgs a) {
     my_bits = (a.tree_mask[my_row] & full) | (1ull << my_row);
   }
 
-  Stager<D, NT> sg;
-  UnitInfo cur = {0, 0, 0u, false};
-  if (u_begin < u_end) {
-    cur = unit_info(u_begin);
-    sg.load(kptr(cur), vptr(cur), cur.nv, tid);
-  }
-  for (int u = u_begin; u < u_end; ++u) {
-    uint16_t* buf = stage + ((u - u_begin) & 1) * Lds<D>::kStageElems;
-    sg.store(buf, tid);
-    __syncthreads();
-    UnitInfo nxt = cur;
-    if (u + 1 < u_end) {
-      nxt = unit_info(u + 1);
-      sg.load(kptr(nxt), vptr(nxt), nxt.nv, tid);
-    }
-    // which of my rows use this chunk, and up to which key offset
+  // one staged chunk: which of my rows use it, up to which key offset
+  auto compute_chunk = [&](const uint16_t* buf, const UnitInfo& ui) {
     int lim = -1;
-    if (row_ok && ((cur.tm >> my_t) & 1u)) {
-      const int last = (cur.isd ? cur.nv - 1 : min(my_pos - cur.key0, cur.nv - 1));
+    if (row_ok && ((ui.tm >> my_t) & 1u)) {
+      const int last = (ui.isd ? ui.nv - 1 : min(my_pos - ui.key0, ui.nv - 1));
       lim = last < 0 ? -1 : last;
     }
     typename RowState<D>::PFrag pf;
     if (__ballot(lim >= 0)) {
-      pf = st.scores(buf, lim, cur.isd, my_bits, a.scale_log2);
+      pf = st.scores(buf, lim, ui.isd, my_bits, a.scale_log2);
     } else {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -594,7 +580,59 @@ void attn_bf16_kernel(AttnArgs a) {
           for (int e = 0; e < 8; ++e) pf.f[kt][t][e] = (__bf16)0.0f;
     }
     st.pv(buf, pf);
-    cur = nxt;
+  };
+
+  if constexpr (PF == 1) {
+    // register prefetch one chunk ahead; store -> barrier -> prefetch -> compute
+    Stager<D, NT> sg;
+    UnitInfo cur = {0, 0, 0u, false};
+    if (u_begin < u_end) {
+      cur = unit_info(u_begin);
+      sg.load(kptr(cur), vptr(cur), cur.nv, tid);
+    }
+    for (int u = u_begin; u < u_end; ++u) {
+      uint16_t* buf = stage + ((u - u_begin) & 1) * Lds<D>::kStageElems;
+      sg.store(buf, tid);
+      __syncthreads();
+      UnitInfo nxt = cur;
+      if (u + 1 < u_end) {
+        nxt = unit_info(u + 1);
+        sg.load(kptr(nxt), vptr(nxt), nxt.nv, tid);
+      }
+      compute_chunk(buf, cur);
+      cur = nxt;
+    }
+  } else {
+    // two register sets: chunk u+1 is stored while chunk u is multiplied,
+    // and the loads of chunk u+3 go out into the set just stored, so every
+    // chunk has two iterations to arrive.  Iteration i (u = u_begin + i):
+    //   barrier; store set[(i+1)&1] -> stage[(i+1)&1]; load u+3 -> that set;
+    //   compute stage[i&1].
+    Stager<D, NT> sgA, sgB;
+    auto fetch = [&](Stager<D, NT>& sg, int u) {
+      if (u < u_end) {
+        const UnitInfo ui = unit_info(u);
+        sg.load(kptr(ui), vptr(ui), ui.nv, tid);
+      }
+    };
+    fetch(sgA, u_begin);
+    fetch(sgB, u_begin + 1);
+    if (u_begin < u_end) sgA.store(stage, tid);
+    fetch(sgA, u_begin + 2);
+    auto iter = [&](int i, Stager<D, NT>& nxt_set) {
+      const int u = u_begin + i;
+      __syncthreads();
+      if (u + 1 < u_end) {
+        nxt_set.store(stage + ((i + 1) & 1) * Lds<D>::kStageElems, tid);
+        fetch(nxt_set, u + 3);
+      }
+      compute_chunk(stage + (i & 1) * Lds<D>::kStageElems, unit_info(u));
+    };
+    const int n = u_end - u_begin;
+    for (int i = 0; i < n; i += 2) {
+      iter(i, sgB);                       // stores chunk u+1 from set B
+      if (i + 1 < n) iter(i + 1, sgA);    // stores chunk u+2 from set A
+    }
   }
 
   // ---- epilogue ------------------------------------------------------------
@@ -743,9 +781,9 @@ constexpr int kMaxDecodeSplits = 32;
 constexpr int kMaxTreeSplits = 32;
 constexpr int kMaxCombineSplits = 64;      // lanes of the combine kernel
 
-template <int D, int G, int W, int MODE>
+template <int D, int G, int W, int MODE, int PF = 1>
 int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, G, W, MODE>), grid, dim3(W * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, G, W, MODE, PF>), grid, dim3(W * 64), 0, st, a);
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
 }
 

@@ -4,67 +4,80 @@
 // InfLLM v2 (semantic kernels of 32 tokens, stride 16); the kernels add no
 // parameters ("MiniCPM 4.0" blog, shadowrocket9.top, InfLLM v2 section).
 //
-// HBM-bound stream.  Each window is summed by d/E threads that each own one
-// 16-byte chunk of the head dimension, so a window row is read as one
-// coalesced 256-byte (bf16, d=128) segment.  Overlapping windows re-read
-// their shared rows, which hit in L2.
+// HBM-bound stream; overlapping windows re-read their shared rows, which hit
+// in L2.
 #include "device_common.h"
 #include "host_common.h"
 
 namespace infllmv2 {
 
 constexpr int kCompressThreads = 256;
-constexpr int kCompressWindowsPerBlock = 64;
+constexpr int kCompressSplit = 4;       // thread groups sharing one window's rows
 
+// A window is summed by kCompressSplit groups of d/E threads; group q adds
+// rows t = q, q + 4, ... of the window, each thread one 16-byte column chunk
+// (a window row is read as one coalesced 256-byte segment for bf16, d=128).
+// The partial sums meet in LDS.  For bf16 keys every partial and total sum
+// of <= 2^16 values is exact in float32, so the order does not matter.
 template <typename T, int D>
 __global__ __launch_bounds__(kCompressThreads) void compress_keys_kernel(
     const T* __restrict__ k, int h_kv, int64_t cap, const int32_t* __restrict__ seqlens,
     int64_t m_begin, int64_t m_end, T* __restrict__ ck, int64_t nc_cap, int ks, int s) {
   constexpr int E = Elem<T>::kPer16B;
-  constexpr int TPW = D / E;                      // threads per window
-  constexpr int WPP = kCompressThreads / TPW;     // windows per pass
+  constexpr int TPW = D / E;                                  // threads per row chunk set
+  constexpr int WPB = kCompressThreads / (TPW * kCompressSplit);  // windows per block
+  __shared__ float part[WPB][kCompressSplit - 1][D];
   const int g = blockIdx.y, b = blockIdx.z;
   const int64_t L = seqlens[b];
   // windows whose tokens lie inside the sequence: m*s + ks <= L
   const int64_t n_full = L < ks ? 0 : (L - ks) / s + 1;
   const int64_t stop = m_end < n_full ? m_end : n_full;
-  const int sub = threadIdx.x / TPW, lane = threadIdx.x % TPW;
-  const T* kb = k + ((int64_t)b * h_kv + g) * cap * D + lane * E;
-  T* cb = ck + ((int64_t)b * h_kv + g) * nc_cap * D + lane * E;
-  const float fks = (float)ks;
-  const int64_t first = m_begin + (int64_t)blockIdx.x * kCompressWindowsPerBlock;
-  const int64_t last = first + kCompressWindowsPerBlock < stop
-                           ? first + kCompressWindowsPerBlock : stop;
-  for (int64_t m = first + sub; m < last; m += WPP) {
-    float acc[E];
+  const int tid = threadIdx.x;
+  const int lane = tid % TPW, q = (tid / TPW) % kCompressSplit, wl = tid / (TPW * kCompressSplit);
+  const int64_t m = m_begin + (int64_t)blockIdx.x * WPB + wl;
+  const bool live = m < stop;
+  float acc[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = 0.0f;
-    const T* src = kb + m * s * D;
-    for (int t = 0; t < ks; ++t) {
+  for (int e = 0; e < E; ++e) acc[e] = 0.0f;
+  if (live) {
+    const T* src = k + ((int64_t)b * h_kv + g) * cap * D + m * s * D + lane * E;
+    for (int t = q; t < ks; t += kCompressSplit) {
       float x[E];
       Elem<T>::unpack(ldg16(src + (int64_t)t * D), x);
 #pragma unroll
       for (int e = 0; e < E; ++e) acc[e] += x[e];
     }
-    // Divide (rather than multiply by a rounded reciprocal): for the default
-    // ks = 32 the float32 sum of 32 bf16 values and the division are exact in
-    // practice, so the only rounding is the final one to the storage type.
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = acc[e] / fks;
-    u32x4 w;
-    if constexpr (E == 8) {
-      w.x = pack_bf16x2(acc[0], acc[1]);
-      w.y = pack_bf16x2(acc[2], acc[3]);
-      w.z = pack_bf16x2(acc[4], acc[5]);
-      w.w = pack_bf16x2(acc[6], acc[7]);
-    } else {
-      w.x = __float_as_uint(acc[0]);
-      w.y = __float_as_uint(acc[1]);
-      w.z = __float_as_uint(acc[2]);
-      w.w = __float_as_uint(acc[3]);
-    }
-    *reinterpret_cast<u32x4*>(cb + m * D) = w;
   }
+  if (q > 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) part[wl][q - 1][lane * E + e] = acc[e];
+  }
+  __syncthreads();
+  if (q != 0 || !live) return;
+#pragma unroll
+  for (int j = 0; j < kCompressSplit - 1; ++j)
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += part[wl][j][lane * E + e];
+  // Divide (rather than multiply by a rounded reciprocal): for the default
+  // ks = 32 the division is exact, so the only rounding is the final one to
+  // the storage type.
+  const float fks = (float)ks;
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = acc[e] / fks;
+  u32x4 w;
+  if constexpr (E == 8) {
+    w.x = pack_bf16x2(acc[0], acc[1]);
+    w.y = pack_bf16x2(acc[2], acc[3]);
+    w.z = pack_bf16x2(acc[4], acc[5]);
+    w.w = pack_bf16x2(acc[6], acc[7]);
+  } else {
+    w.x = __float_as_uint(acc[0]);
+    w.y = __float_as_uint(acc[1]);
+    w.z = __float_as_uint(acc[2]);
+    w.w = __float_as_uint(acc[3]);
+  }
+  T* dst = ck + ((int64_t)b * h_kv + g) * nc_cap * D + m * D + lane * E;
+  *reinterpret_cast<u32x4*>(dst) = w;
 }
 
 template <typename T, int D>
@@ -72,7 +85,8 @@ static int launch_compress(const void* k, int32_t batch, int32_t h_kv, int64_t c
                            const int32_t* seqlens, int64_t m_begin, int64_t m_end, void* ck,
                            int64_t nc_cap, const Resolved& r, hipStream_t st) {
   const int64_t n = m_end - m_begin;
-  dim3 grid((unsigned)ceil_div(n, kCompressWindowsPerBlock), h_kv, batch);
+  constexpr int WPB = kCompressThreads / ((D / Elem<T>::kPer16B) * kCompressSplit);
+  dim3 grid((unsigned)ceil_div(n, WPB), h_kv, batch);
   hipLaunchKernelGGL((compress_keys_kernel<T, D>), grid, dim3(kCompressThreads), 0, st,
                      (const T*)k, h_kv, cap, seqlens, m_begin, m_end, (T*)ck, nc_cap, r.ks,
                      r.s);
