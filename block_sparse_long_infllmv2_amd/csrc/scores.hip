@@ -125,17 +125,20 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 // (e = 0..3), i.e. exactly the four own windows of block 2q + h of the tile;
 // the fifth (halo) window comes from the other half-wave or the previous tile.
 //
-// Workgroup = 32 rows x one KV head; its 4 waves take interleaved 8-block
-// tiles of the window range, so qsum is built once (in LDS) per workgroup.
+// Workgroup = 64 rows x one KV head; its 8 waves take contiguous ranges of
+// 8-block tiles, so qsum is built once (in LDS) per workgroup, and each wave
+// multiplies every compressed-key fragment it loads by two 32-row groups.
 // ---------------------------------------------------------------------------
-constexpr int kMfmaRows = 32;
+constexpr int kMfmaRG = 2;               // 32-row groups per wave (share A fragments)
+constexpr int kMfmaRows = 32 * kMfmaRG;  // rows per workgroup
 constexpr int kMfmaWaves = 8;            // waves per workgroup, splitting the windows
 
 template <int D>
 __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
   constexpr int KS = D / 16;
+  constexpr int RG = kMfmaRG;
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
-  __shared__ int64_t pos_lds[kMfmaRows];
+  __shared__ int pos_lds[kMfmaRows];
 
   const int w = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int g = w / n_row_tiles, tile = w % n_row_tiles;
@@ -178,45 +181,48 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   }
   if (tid < kMfmaRows) {
     const int row = r0 + tid;
-    int64_t pos = -1;
+    int pos = -1;
     if (row < a.rows) {
-      pos = a.row_pos ? a.row_pos[row] : L - 1;
-      if (pos >= L || pos > a.max_pos) pos = -1;
+      const int64_t p = a.row_pos ? a.row_pos[row] : L - 1;
+      pos = (p >= L || p > a.max_pos || p < 0) ? -1 : (int)p;
     }
     pos_lds[tid] = pos;
   }
   __syncthreads();
 
-  bf16x8 qh[KS], ql[KS];
+  // this lane: column `col` of row groups rg = 0..RG-1 (row r0 + 32 rg + col)
+  bf16x8 qh[RG][KS], ql[RG][KS];
+  int pos[RG], n_vis[RG], b_own[RG];
+  float* out[RG];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    qh[ks] = *reinterpret_cast<const bf16x8*>(&qlds[0][col][16 * ks + 8 * half]);
-    ql[ks] = *reinterpret_cast<const bf16x8*>(&qlds[1][col][16 * ks + 8 * half]);
+  for (int rg = 0; rg < RG; ++rg) {
+    const int rr = 32 * rg + col;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qh[rg][ks] = *reinterpret_cast<const bf16x8*>(&qlds[0][rr][16 * ks + 8 * half]);
+      ql[rg][ks] = *reinterpret_cast<const bf16x8*>(&qlds[1][rr][16 * ks + 8 * half]);
+    }
+    pos[rg] = pos_lds[rr];
+    // visible windows: m*s + ks - 1 <= pos (32-bit: the host bounds max_pos)
+    n_vis[rg] = pos[rg] >= a.ks - 1 ? (pos[rg] - a.ks + 1) / a.s + 1 : 0;
+    b_own[rg] = pos[rg] >= 0 ? pos[rg] / a.B : -1;
+    out[rg] = a.scores + ((int64_t)(r0 + rr) * a.h_kv + g) * a.nb_cap;
   }
-  const int pos = (int)pos_lds[col];
-  const int row = r0 + col;
-  const bool row_ok = pos >= 0;
-  // visible windows: m*s + ks - 1 <= pos  (all indices fit in 32 bits: the
-  // host bounds max_pos)
-  const int n_vis = pos >= a.ks - 1 ? (pos - a.ks + 1) / a.s + 1 : 0;
-  const int b_own = row_ok ? pos / a.B : -1;
   int tile_max_pos = -1, tile_min_vis = 0x7fffffff;
   for (int j = 0; j < kMfmaRows; ++j) {
-    const int pj = (int)pos_lds[j];
+    const int pj = pos_lds[j];
     tile_max_pos = max(tile_max_pos, pj);
     if (pj >= 0) tile_min_vis = min(tile_min_vis, pj >= a.ks - 1 ? (pj - a.ks + 1) / a.s + 1 : 0);
   }
   const int nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
   const int n_tiles8 = (nb_tile + 7) / 8;
-  float* out = a.scores + ((int64_t)row * a.h_kv + g) * a.nb_cap;
   const uint16_t* ckb = (const uint16_t*)a.ck + (int64_t)g * a.nc_cap * D;
   const int nc_cap = (int)min(a.nc_cap, (int64_t)0x7fffffff);
   const float sc = a.scale;
 
   // dot of this lane's query half with one compressed key (VALU), combined
-  // over the two half-waves: used for the halo window before a wave's first
-  // tile
-  auto single_window = [&](int m) -> float {
+  // over the two half-waves: the halo window before a wave's first tile
+  auto single_window = [&](int m, int rg) -> float {
     float part = 0.0f;
     if (m >= 0 && m < nc_cap) {
       const uint16_t* c = ckb + (int64_t)m * D;
@@ -226,11 +232,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
         Elem<uint16_t>::unpack(ldg16(c + 16 * ks + 8 * half), x);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          part += ((float)qh[ks][e] + (float)ql[ks][e]) * x[e];
+          part += ((float)qh[rg][ks][e] + (float)ql[rg][ks][e]) * x[e];
       }
     }
     const float full = part + swap_halves(part);
-    return (m >= 0 && m < n_vis) ? full * sc : -INFINITY;
+    return (m >= 0 && m < n_vis[rg]) ? full * sc : -INFINITY;
   };
 
   // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
@@ -239,8 +245,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   const int per_wave = (n_tiles8 + kMfmaWaves - 1) / kMfmaWaves;
   const int t_begin = wave * per_wave;
   const int t_end = min(n_tiles8, t_begin + per_wave);
-  float carry = t_begin < t_end ? single_window(t_begin * 32 - 1) : -INFINITY;
-  // A-operand fragments of a tile: window mt + col, dims 16ks + 8half
+  float carry[RG];
+#pragma unroll
+  for (int rg = 0; rg < RG; ++rg)
+    carry[rg] = t_begin < t_end ? single_window(t_begin * 32 - 1, rg) : -INFINITY;
+  // A-operand fragments of a tile: window 32 tt + col, dims 16ks + 8half
   auto load_tile = [&](int tt, u32x4* fr) {
     const int mrow = tt * 32 + col;
     const bool in = mrow < nc_cap;
@@ -261,66 +270,75 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) cur[ks] = frag[ks];
     if (t + 1 < t_end) load_tile(t + 1, frag);  // next tile's loads in flight
-    f32x16 acc;
+    f32x16 acc[RG];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[rg][v] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 av = *reinterpret_cast<const bf16x8*>(&cur[ks]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qh[ks], acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ql[ks], acc, 0, 0, 0);
-    }
-    // own maxima and last windows per block group q (block bt + 2q + half);
-    // tiles wholly visible to every row of the workgroup skip the masking
-    float own[4], last[4];
-    if (mt + 32 <= tile_min_vis) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        own[q] = sc * fmaxf(fmaxf(acc[4 * q], acc[4 * q + 1]), fmaxf(acc[4 * q + 2], acc[4 * q + 3]));
-        last[q] = sc * acc[4 * q + 3];
+      for (int rg = 0; rg < RG; ++rg) {
+        acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qh[rg][ks], acc[rg], 0, 0, 0);
+        acc[rg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, ql[rg][ks], acc[rg], 0, 0, 0);
       }
-    } else {
+    }
+    const bool full_vis = mt + 32 <= tile_min_vis;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float mx = -INFINITY;
+    for (int rg = 0; rg < RG; ++rg) {
+      // own maxima and last windows per block group q (block bt + 2q + half);
+      // tiles wholly visible to every row of the workgroup skip the masking
+      float own[4], last[4];
+      if (full_vis) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int m = mt + 8 * q + 4 * half + e;
-          const float x = m < n_vis ? acc[4 * q + e] * sc : -INFINITY;
-          mx = fmaxf(mx, x);
-          if (e == 3) last[q] = x;
+        for (int q = 0; q < 4; ++q) {
+          own[q] = sc * fmaxf(fmaxf(acc[rg][4 * q], acc[rg][4 * q + 1]),
+                              fmaxf(acc[rg][4 * q + 2], acc[rg][4 * q + 3]));
+          last[q] = sc * acc[rg][4 * q + 3];
         }
-        own[q] = mx;
-      }
-    }
-    float other[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) other[q] = swap_halves(last[q]);
-    // halo window of block bt + 2q + half is the last own window of the
-    // block before it: half 1 <- (q, half 0); half 0 <- (q-1, half 1)
-    float bs[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry);
-      bs[q] = fmaxf(own[q], halo);
-    }
-    carry = other[3];       // for half-0 lanes: last window of block bt + 7
-    // regroup so that half 0 holds blocks bt..bt+3 and half 1 bt+4..bt+7:
-    // half 0 has bt+{0,2,4,6}, half 1 has bt+{1,3,5,7}
-    const float x0 = swap_halves(half ? bs[0] : bs[2]);
-    const float x1 = swap_halves(half ? bs[1] : bs[3]);
-    f32x4 w4;
-    if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }     // bt+0..3
-    else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }     // bt+4..7
-    const int b4 = bt + 4 * half;
-    if (row_ok) {
-      if (b4 + 3 <= b_own && a.vec_store) {
-        *reinterpret_cast<f32x4*>(out + b4) = w4;
       } else {
-        if (b4 + 0 <= b_own) out[b4 + 0] = w4.x;
-        if (b4 + 1 <= b_own) out[b4 + 1] = w4.y;
-        if (b4 + 2 <= b_own) out[b4 + 2] = w4.z;
-        if (b4 + 3 <= b_own) out[b4 + 3] = w4.w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = mt + 8 * q + 4 * half + e;
+            const float x = m < n_vis[rg] ? acc[rg][4 * q + e] * sc : -INFINITY;
+            mx = fmaxf(mx, x);
+            if (e == 3) last[q] = x;
+          }
+          own[q] = mx;
+        }
+      }
+      float other[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) other[q] = swap_halves(last[q]);
+      // halo window of block bt + 2q + half is the last own window of the
+      // block before it: half 1 <- (q, half 0); half 0 <- (q-1, half 1)
+      float bs[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry[rg]);
+        bs[q] = fmaxf(own[q], halo);
+      }
+      carry[rg] = other[3];     // for half-0 lanes: last window of block bt + 7
+      // regroup: half 0 -> blocks bt..bt+3, half 1 -> bt+4..bt+7
+      const float x0 = swap_halves(half ? bs[0] : bs[2]);
+      const float x1 = swap_halves(half ? bs[1] : bs[3]);
+      f32x4 w4;
+      if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }
+      else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }
+      const int b4 = bt + 4 * half;
+      if (pos[rg] >= 0) {
+        if (b4 + 3 <= b_own[rg] && a.vec_store) {
+          *reinterpret_cast<f32x4*>(out[rg] + b4) = w4;
+        } else {
+          if (b4 + 0 <= b_own[rg]) out[rg][b4 + 0] = w4.x;
+          if (b4 + 1 <= b_own[rg]) out[rg][b4 + 1] = w4.y;
+          if (b4 + 2 <= b_own[rg]) out[rg][b4 + 2] = w4.z;
+          if (b4 + 3 <= b_own[rg]) out[rg][b4 + 3] = w4.w;
+        }
       }
     }
   }
