@@ -144,6 +144,135 @@ struct Stager {
 };
 
 // ---------------------------------------------------------------------------
+// Direct staging: global_load_lds_dwordx4 moves 16 bytes per lane from HBM
+// straight into LDS (lane l of one instruction lands at M0 + 16 l), so a
+// chunk in flight holds no registers and costs no LDS write instructions.
+// K and V tiles keep the natural [key][d] layout; the 16-byte column chunk c
+// of row r is stored at chunk position c ^ f(r), which keeps both fragment
+// reads free of bank conflicts on the 64-bank LDS:
+//   K (16-byte reads, 16 lanes per pass): 16 consecutive rows reading one
+//     logical chunk hit 16 distinct 16-byte bank groups;
+//   V (8-byte transposing reads, 32 lanes per pass): 4 consecutive rows x 4
+//     consecutive chunks hit 16 distinct groups.
+// f depends on r mod 16 only, so tiles of 16 rows repeat the same pattern.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Swz {
+  static constexpr int RB = 2 * D;              // bytes per row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int TILE = kChunk * RB;      // bytes per K or V tile
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+  }
+};
+
+// One 16-byte-per-lane copy global -> LDS.  `lds_addr` (wave-uniform) is the
+// byte address of lane 0's destination; `gbase` (wave-uniform) plus the
+// lane's byte offset `voff` is its source.  M0 must be written one wait state
+// before the load that reads it.
+__device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are still in
+// flight (they complete in issue order) and its LDS reads are done, then
+// meet the other waves.  The compiler does not see the direct loads, so this
+// is the only wait that orders them before the LDS reads of their tile.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+template <int D, int NT>
+struct DmaTile {
+  static constexpr int CPR = Swz<D>::CPR;
+  static constexpr int RB = Swz<D>::RB;
+  static constexpr int kLoads = Swz<D>::TILE / (NT * 16);   // per thread and tile
+  static_assert(kLoads >= 1 && Swz<D>::TILE % (NT * 16) == 0, "tile copy shape");
+  static_assert(2 * kLoads <= 63, "vmcnt range");
+  // Instruction i, thread t -> LDS slot s = i*NT + t: row s / CPR, position
+  // s % CPR.  When one instruction spans a multiple of 16 rows, the swizzle
+  // phase f(r) is the same for every i and the source offsets differ by a
+  // whole number of rows: one base offset, the row step goes to the pointer.
+  static constexpr int kRowsPerInst = NT / CPR;
+  static constexpr bool kUniform = kRowsPerInst % 16 == 0;
+  uint32_t voff[kUniform ? 1 : kLoads];   // source byte offsets in a full tile
+
+  __device__ __forceinline__ void init(int tid) {
+#pragma unroll
+    for (int i = 0; i < (kUniform ? 1 : kLoads); ++i) {
+      const int s = i * NT + tid, r = s / CPR;
+      voff[i] = (uint32_t)(r * RB + (((s % CPR) ^ Swz<D>::f(r)) * 16));
+    }
+  }
+  // rows >= nv are copies of row nv - 1 (finite data; the softmax masks them)
+  __device__ __forceinline__ void issue(uint32_t lds_tile, const uint16_t* g, int nv, int tid,
+                                        int wave) const {
+    if (nv == kChunk) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        if constexpr (kUniform)
+          lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g + i * kRowsPerInst * D,
+                    voff[0]);
+        else
+          lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g, voff[i]);
+      }
+    } else {
+      const int last = nv > 0 ? nv - 1 : 0;
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int s = i * NT + tid, r = s / CPR;
+        const int rr = r < last ? r : last;
+        lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g,
+                  (uint32_t)(rr * RB + (((s % CPR) ^ Swz<D>::f(r)) * 16)));
+      }
+    }
+  }
+};
+
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+__device__ __forceinline__ bf16x8 lds_read16(uint32_t addr) {
+  return *reinterpret_cast<const lds_bf16x8*>((uintptr_t)addr);
+}
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte pieces addressed by lanes 4j + i/4, j = 0..3.
+__device__ __forceinline__ bf16x4 lds_read_tr8(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)addr);
+}
+
+// Per-lane fragment addresses inside a swizzled tile.
+//   K, A operand of S^T = K Q^T: lane (col, half), k-step ks reads row
+//     32 kt + col, logical chunk 2 ks + half (kt adds 32 rows).
+//   V^T A operand of O^T = V^T P^T, d-tile dt: element e of half h is key
+//     16 t + 8 (e/4) + 4 h + e%4 of tile kt, at d = 32 dt + col.  Two
+//     transposing reads (e/4 = 0, 1) each give 4 keys; lane L addresses key
+//     8 c' + 4 h + (L%16)/4 (+ 32 kt + 16 t) and d = 32 dt + 16 ((L/16)%2) + 4 (L%4).
+// Position bits of a chunk (bits 4.. of the byte offset inside a row) never
+// overlap the row bits, so k-step ks and d-tile dt enter as XOR masks:
+//   K:  (2 ks + half) ^ f = 2 ks ^ (half ^ f)  ->  k0 ^ (32 ks)
+//   V:  (4 dt + 2 g + q/2) ^ f = 4 dt ^ (...)  ->  v0[c'] ^ (64 dt)
+template <int D>
+struct FragAddr {
+  uint32_t k0;
+  uint32_t v0[2];
+  __device__ __forceinline__ void init(int lane) {
+    constexpr int RB = Swz<D>::RB;
+    const int col = lane & 31, half = lane >> 5;
+    k0 = (uint32_t)(col * RB + ((half ^ Swz<D>::f(col)) * 16));
+    const int g = (lane >> 4) & 1, j = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int row = 8 * c + 4 * half + j;
+      v0[c] = (uint32_t)(row * RB + (((2 * g + (q >> 1)) ^ Swz<D>::f(row)) * 16) + 8 * (q & 1));
+    }
+  }
+  __device__ __forceinline__ uint32_t k(int ks) const { return k0 ^ (uint32_t)(32 * ks); }
+  __device__ __forceinline__ uint32_t v(int dt, int c) const { return v0[c] ^ (uint32_t)(64 * dt); }
+};
+
+// ---------------------------------------------------------------------------
 // Per-wave online-softmax state for 32 query rows (one row per lane column).
 // The running max m is only raised when a block's max exceeds it by more
 // than kRescaleSlack (log2 units): exponentials then stay below 2^slack, which
@@ -174,21 +303,44 @@ struct RowState {
 
   // S^T = K Q^T for one staged chunk, masked online softmax; returns the
   // P^T fragments (and rescales O when the running max moves).
-  __device__ __forceinline__ PFrag scores(const uint16_t* stage, int lim, bool use_bits,
+  // kfrag(kt, ks): this lane's A fragment of key tile kt, k-step ks.
+  // LA > 0: software pipeline, LA fragments read ahead of the MFMA that uses
+  // them (the two key tiles' accumulation chains alternate).
+  template <int LA = 0, class KFrag>
+  __device__ __forceinline__ PFrag scores(KFrag kfrag, int lim, bool use_bits,
                                           uint64_t draft_bits, float scale_log2) {
     const int lane = threadIdx.x & 63;
-    const int col = lane & 31, half = lane >> 5;
-    const uint16_t* Ks = stage;
+    const int half = lane >> 5;
     f32x16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kt][v] = 0.0f;
-      const uint16_t* krow = Ks + (32 * kt + col) * Lds<D>::kKStride + 8 * half;
+    if constexpr (LA > 0) {
+      constexpr int NM = 2 * (D / 16);
+      static_assert(LA < NM, "lookahead");
+      bf16x8 a[NM];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + 16 * ks);
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, q[ks], s[kt], 0, 0, 0);
+      for (int m = 0; m < NM; ++m) a[m] = kfrag(m & 1, m >> 1);
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        s[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], q[m >> 1], s[m & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);        // LDS reads
+#pragma unroll
+      for (int m = 0; m < NM - LA; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);       // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        bf16x8 a[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) a[ks] = kfrag(kt, ks);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+          s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], q[ks], s[kt], 0, 0, 0);
       }
     }
     // Scale into the log2 domain, mask, row max, exponentials.  Common case
@@ -263,24 +415,156 @@ struct RowState {
   // O^T += V^T P^T; A-operand element e of half h <-> key 16t + 8(e/4) + 4h + e%4.
   // Run for every staged chunk (with zero P when the wave keeps none of it),
   // so that O flows through the same instructions on every iteration.
-  __device__ __forceinline__ void pv(const uint16_t* stage, const PFrag& pf) {
-    const int lane = threadIdx.x & 63;
-    const int col = lane & 31, half = lane >> 5;
-    const uint16_t* Vt = stage + Lds<D>::kKElems;
+  // vfrag(dt, kt, t): this lane's A fragment of V^T rows 32 dt.., k-step t of
+  // key tile kt.
+  // LA > 0: k-step outer, d-tile inner (consecutive MFMAs are independent),
+  // LA fragments (2 LDS reads each) read ahead of their MFMA.
+  template <int LA = 0, class VFrag>
+  __device__ __forceinline__ void pv(VFrag vfrag, const PFrag& pf) {
     const auto& pb = pf.f;
+    if constexpr (LA > 0) {
+      constexpr int NDT = D / 32, NF = 4 * NDT;
+      static_assert(LA < NF, "lookahead");
+      bf16x8 b[NF];
+#pragma unroll
+      for (int f = 0; f < NF; ++f) b[f] = vfrag(f % NDT, f / NDT / 2, (f / NDT) & 1);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+        o[f % NDT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[f], pb[f / NDT / 2][(f / NDT) & 1],
+                                                             o[f % NDT], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * LA, 0);
+#pragma unroll
+      for (int f = 0; f < NF - LA; ++f) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, LA, 0);
+      return;
+    }
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const uint16_t* vrow = Vt + (32 * dt + col) * Lds<D>::kVStride + 8 * half;
+      bf16x8 a[2][2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          // keys 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}: permuted layout
-          // puts them at positions 16t + 8h .. +8
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vrow + 32 * kt + 16 * t);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kt][t], o[dt], 0, 0, 0);
+        for (int t = 0; t < 2; ++t) a[kt][t] = vfrag(dt, kt, t);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kt][t], pb[kt][t], o[dt], 0, 0, 0);
+    }
+  }
+
+  // ---- split form for the software-pipelined loop ------------------------
+  // S^T = K Q^T only (LA fragments read ahead of their MFMA).
+  template <int LA, class KFrag>
+  __device__ __forceinline__ void qk(KFrag kfrag, f32x16 (&s)[2]) const {
+    constexpr int NM = 2 * (D / 16);
+    static_assert(LA > 0 && LA < NM, "lookahead");
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[kt][v] = 0.0f;
+    bf16x8 a[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) a[m] = kfrag(m & 1, m >> 1);
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      s[m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m], q[m >> 1], s[m & 1], 0, 0, 0);
+  }
+
+  // Online softmax of one chunk's S^T (this lane's row), without the O
+  // rescale: returns P^T and sets alpha = 2^(m_old - m_new) (1 when the
+  // running max stays).  MASKED: per-key limit `lim` and draft bits;
+  // otherwise every row keeps all 64 keys (lim = 63) or none (lim = -1).
+  template <bool MASKED>
+  __device__ __forceinline__ PFrag softmax(f32x16 (&s)[2], int lim, bool use_bits,
+                                           uint64_t draft_bits, float scale_log2,
+                                           float& alpha) {
+    const int half = (threadIdx.x & 63) >> 5;
+    const bool keep = lim >= 0;
+    float mx = -INFINITY;
+    if constexpr (!MASKED) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kt][v]);
+      mx = keep ? mx * scale_log2 : -INFINITY;
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = 32 * kt + 8 * (v >> 2) + 4 * half + (v & 3);
+          bool ok = off <= lim;
+          if (use_bits) ok = ok && ((draft_bits >> off) & 1ull);
+          const float x = ok ? s[kt][v] * scale_log2 : -INFINITY;
+          s[kt][v] = x;
+          mx = fmaxf(mx, x);
         }
+    }
+    // the other half-wave holds the other 32 keys of this row
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    const float m_new = mx > m + kRescaleSlack ? mx : m;
+    alpha = fast_exp2(m - m_new);
+    float psum = 0.0f;
+    if constexpr (!MASKED) {
+      const float msub = keep ? m_new : INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(__builtin_fmaf(s[kt][v], scale_log2, -msub));
+          s[kt][v] = p;
+          psum += p;
+        }
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = fast_exp2(s[kt][v] - m_new);
+          s[kt][v] = p;
+          psum += p;
+        }
+    }
+    m = m_new;
+    l = l * alpha + psum;
+    PFrag pf;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pf.f[kt][t][e] = (__bf16)s[kt][8 * t + e];
+    return pf;
+  }
+
+  // Partial chunk: scores of keys past `lim` (or outside the draft bits) ->
+  // -inf, after which the unmasked softmax gives them p = 0.
+  __device__ __forceinline__ void mask_scores(f32x16 (&s)[2], int lim, bool use_bits,
+                                              uint64_t draft_bits) const {
+    const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int off = 32 * kt + 8 * (v >> 2) + 4 * half + (v & 3);
+        bool ok = off <= lim;
+        if (use_bits) ok = ok && ((draft_bits >> off) & 1ull);
+        s[kt][v] = ok ? s[kt][v] : -INFINITY;
       }
+  }
+
+  __device__ __forceinline__ void rescale(float alpha) {
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[dt][v] *= alpha;
     }
   }
 };
@@ -387,6 +671,32 @@ __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, 
 // Entries a split workgroup may hold in LDS (host keeps units per split below).
 constexpr int kSplitEntryCap = 64;
 
+template <int S> struct StageTag { static constexpr int value = S; };
+
+// Instruction order for a block holding NM QK MFMAs and their NM fragment
+// reads (and, with VALU > 0, another chunk's softmax): LA reads first, then
+// each MFMA followed by the next read and up to VALU vector instructions.
+template <int NM, int LA, int VALU>
+__device__ __forceinline__ void sched_qk() {
+  __builtin_amdgcn_sched_group_barrier(0x100, LA, 0);          // LDS reads
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    if (m + LA < NM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(0x002, VALU, 0);
+  }
+}
+// fragments read ahead of their MFMA in the directly staged loop
+#ifndef INFLLMV2_LOOKAHEAD
+#define INFLLMV2_LOOKAHEAD 2
+#endif
+constexpr int kLookahead = INFLLMV2_LOOKAHEAD;
+// vector instructions placed after each QK MFMA when a softmax runs beside it
+#ifndef INFLLMV2_VALU_PER_MFMA
+#define INFLLMV2_VALU_PER_MFMA 4
+#endif
+constexpr int kValuPerMfma = INFLLMV2_VALU_PER_MFMA;
+
 // ---------------------------------------------------------------------------
 // The attention kernel.
 //   W waves, each 32 rows = TPW tokens x G heads; TT = W * TPW tokens.
@@ -403,7 +713,9 @@ void attn_bf16_kernel(AttnArgs a) {
   static_assert(MODE != kPrefill || TT > 1, "prefill tiles hold several tokens");
   constexpr int SORT_N = (MODE == kPrefill) ? TT * kSortCap : 0;
   constexpr int ECAP = (MODE == kPrefill) ? TT * kSortCap : kSplitEntryCap;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2 * Lds<D>::kStageElems];
+  // PF 1/2: two padded K + V^T stages; PF 3/4: K0 K1 V0 V1 swizzled tiles
+  constexpr int STAGE_ELEMS = PF >= 3 ? 2 * Swz<D>::TILE : 2 * Lds<D>::kStageElems;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[STAGE_ELEMS];
   __shared__ int2 ents[ECAP];
   __shared__ int scan_lds[NT / 64];
   static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
@@ -505,7 +817,8 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // unit -> first key, #valid keys, token mask, draft flag
   struct UnitInfo { int key0, nv; uint32_t tm; bool isd; };
-  auto unit_info = [&](int u) -> UnitInfo {
+  // per-lane form (u may differ between lanes; u < n_units_total)
+  auto unit_info_lane = [&](int u) -> UnitInfo {
     UnitInfo r;
     r.isd = has_draft && u == n_entries * cpb;
     if (r.isd) {
@@ -532,6 +845,10 @@ void attn_bf16_kernel(AttnArgs a) {
     r.key0 = b * a.B + c * kChunk;
     const int blk_end = min((b + 1) * a.B, n_keys);
     r.nv = max(0, min(kChunk, blk_end - r.key0));
+    return r;
+  };
+  auto unit_info = [&](int u) -> UnitInfo {
+    UnitInfo r = unit_info_lane(u);
     // identical in every lane: keep them in scalar registers
     r.key0 = __builtin_amdgcn_readfirstlane(r.key0);
     r.nv = __builtin_amdgcn_readfirstlane(r.nv);
@@ -561,16 +878,20 @@ void attn_bf16_kernel(AttnArgs a) {
     my_bits = (a.tree_mask[my_row] & full) | (1ull << my_row);
   }
 
-  // one staged chunk: which of my rows use it, up to which key offset
-  auto compute_chunk = [&](const uint16_t* buf, const UnitInfo& ui) {
+  // one staged chunk: largest key offset my row uses, -1 if none
+  auto chunk_lim = [&](const UnitInfo& ui) {
     int lim = -1;
     if (row_ok && ((ui.tm >> my_t) & 1u)) {
       const int last = (ui.isd ? ui.nv - 1 : min(my_pos - ui.key0, ui.nv - 1));
       lim = last < 0 ? -1 : last;
     }
+    return lim;
+  };
+  // scores + softmax when any row of the wave uses the chunk, else zero P
+  auto chunk_scores = [&](auto kfrag, const UnitInfo& ui, int lim) {
     typename RowState<D>::PFrag pf;
     if (__ballot(lim >= 0)) {
-      pf = st.scores(buf, lim, ui.isd, my_bits, a.scale_log2);
+      pf = st.scores(kfrag, lim, ui.isd, my_bits, a.scale_log2);
     } else {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -579,10 +900,194 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf.f[kt][t][e] = (__bf16)0.0f;
     }
-    st.pv(buf, pf);
+    return pf;
+  };
+  // padded layout (PF 1/2): K rows of kKStride, V^T rows of kVStride
+  auto compute_chunk = [&](const uint16_t* buf, const UnitInfo& ui) {
+    const uint16_t* krow = buf + col * Lds<D>::kKStride + 8 * half;
+    const uint16_t* vrow = buf + Lds<D>::kKElems + col * Lds<D>::kVStride + 8 * half;
+    auto kfrag = [&](int kt, int ks) {
+      return *reinterpret_cast<const bf16x8*>(krow + 32 * kt * Lds<D>::kKStride + 16 * ks);
+    };
+    // keys 16t + 4h + {0..3} and 16t + 8 + 4h + {0..3}: the permuted V^T
+    // rows put them at positions 16t + 8h .. +8
+    auto vfrag = [&](int dt, int kt, int t) {
+      return *reinterpret_cast<const bf16x8*>(vrow + 32 * dt * Lds<D>::kVStride + 32 * kt + 16 * t);
+    };
+    const typename RowState<D>::PFrag pf = chunk_scores(kfrag, ui, chunk_lim(ui));
+    st.pv(vfrag, pf);
   };
 
-  if constexpr (PF == 1) {
+  if constexpr (PF == 4) {
+    // Direct staging with a software pipeline inside each wave: while the
+    // matrix cores compute S^T = K Q^T of chunk i+1, the vector ALU runs the
+    // softmax of chunk i (same basic block, so the scheduler interleaves
+    // them); then O^T += V^T P^T of chunk i.  Chunk i sits in K[i&1], V[i&1].
+    // One barrier per iteration, X_i: K(i+1) and V(i) have landed and every
+    // wave is done with iteration i-1, so K(i+2) -> K[i&1] (read by QK(i)
+    // in iteration i-1) and V(i+1) -> V[(i+1)&1] (read by PV(i-1)) are
+    // issued right after it and have one iteration to arrive.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // Q and draft mask loads: vmcnt(0)
+    using DT = DmaTile<D, NT>;
+    constexpr int TILE = Swz<D>::TILE;
+    DT dma;
+    dma.init(tid);
+    FragAddr<D> fa;
+    fa.init(lane);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
+    const int n = u_end - u_begin;
+    const UnitInfo none = {0, 0, 0u, false};
+    // Metadata of 64 consecutive units, one unit per lane; unit u is taken
+    // from lane u - wb with readlane (units are visited in increasing order,
+    // so the window only moves forward).
+    int wb = u_begin;
+    UnitInfo wl = none;
+    auto load_window = [&]() {
+      const int uu = wb + lane;
+      wl = uu < u_end ? unit_info_lane(uu) : none;
+    };
+    load_window();
+    auto info = [&](int u) -> UnitInfo {
+      if (u >= u_end) return none;
+      if (u >= wb + 64) {
+        wb += 64;
+        load_window();
+      }
+      UnitInfo r;
+      const int ln = u - wb;
+      r.key0 = __builtin_amdgcn_readlane(wl.key0, ln);
+      r.nv = __builtin_amdgcn_readlane(wl.nv, ln);
+      r.tm = (uint32_t)__builtin_amdgcn_readlane((int)wl.tm, ln);
+      r.isd = has_draft && u == n_entries * cpb;
+      return r;
+    };
+    auto kfrag_at = [&](uint32_t kb) {
+      return [=, &fa](int kt, int ks) {
+        return lds_read16(kb + fa.k(ks) + kt * 32 * Swz<D>::RB);
+      };
+    };
+    auto vfrag_at = [&](uint32_t vb) {
+      return [=, &fa](int dt, int kt, int t) {
+        const uint32_t off = vb + (32 * kt + 16 * t) * Swz<D>::RB;
+        const bf16x4 lo = lds_read_tr8(off + fa.v(dt, 0));
+        const bf16x4 hi = lds_read_tr8(off + fa.v(dt, 1));
+        return (bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+    };
+    UnitInfo I0 = info(u_begin), I1 = info(u_begin + 1), I2 = info(u_begin + 2);
+    if (n > 0) {
+      dma.issue(lds0, kptr(I0), I0.nv, tid, wave_u);
+      dma.issue(lds0 + 2 * TILE, vptr(I0), I0.nv, tid, wave_u);
+    }
+    if (n > 1) dma.issue(lds0 + TILE, kptr(I1), I1.nv, tid, wave_u);
+    wait_vm_barrier<0>();
+    f32x16 sA[2], sB[2];
+    int lim0 = n > 0 ? chunk_lim(I0) : -1;
+    bool use0 = __ballot(lim0 >= 0) != 0;
+    if (use0) st.template qk<kLookahead>(kfrag_at(lds0), sA);
+
+    // iteration i: scores of chunk i in `sc`, chunk i+1's go to `sn`
+    auto iter = [&](int i, auto stage_tag, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int u = u_begin + i;
+      wait_vm_barrier<0>();
+      if (i + 2 < n) dma.issue(lds0 + S * TILE, kptr(I2), I2.nv, tid, wave_u);
+      if (i + 1 < n) dma.issue(lds0 + (3 - S) * TILE, vptr(I1), I1.nv, tid, wave_u);
+      const int lim1 = i + 1 < n ? chunk_lim(I1) : -1;
+      const bool use1 = __ballot(lim1 >= 0) != 0;
+      const bool part0 = __ballot((lim0 >= 0 && lim0 < kChunk - 1) || I0.isd) != 0;
+      // One straight-line block (variants of it would each need their own
+      // register assignment): QK of chunk i+1, computed whether or not a row
+      // of the wave uses it, beside the softmax of chunk i (p = 0 in rows
+      // that do not use it; masked keys were set to -inf just before).
+      if (part0) st.mask_scores(sc, lim0, I0.isd, my_bits);
+      float alpha;
+      st.template qk<kLookahead>(kfrag_at(lds0 + (1 - S) * TILE), sn);
+      const typename RowState<D>::PFrag pf =
+          st.template softmax<false>(sc, lim0, false, 0ull, a.scale_log2, alpha);
+      sched_qk<2 * (D / 16), kLookahead, kValuPerMfma>();
+      (void)use1;
+      if (use0) {
+        st.rescale(alpha);
+        st.template pv<kLookahead>(vfrag_at(lds0 + (2 + S) * TILE), pf);
+      }
+      (void)u;
+      lim0 = lim1;
+      use0 = use1;
+      I0 = I1;
+      I1 = I2;
+      I2 = info(u + 3);
+    };
+    for (int i = 0; i < n; i += 2) {
+      iter(i, StageTag<0>(), sA, sB);
+      if (i + 1 < n) iter(i + 1, StageTag<1>(), sB, sA);
+    }
+  } else if constexpr (PF == 3) {
+    // Direct staging, two K and two V tiles.  Chunk i is read from K[i&1],
+    // V[i&1].  Issue order: K0 V0 K1 | A0 V1 B0 K2 | A1 V2 B1 K3 | ...
+    //   barrier A_i (K(i) has landed):  V(i+1) -> V[(i+1)&1], which PV(i-1)
+    //                                  finished reading before A_i;
+    //   S^T = K Q^T and the softmax of chunk i;
+    //   barrier B_i (V(i) has landed):  K(i+2) -> K[i&1], free after QK(i);
+    //   O^T += V^T P^T.
+    // Every tile thus has about one and a half iterations to arrive.  At A_i
+    // the loads issued after K(i) are V(i) and K(i+1) (if it exists); at B_i
+    // those after V(i) are K(i+1) and V(i+1) (both exist iff i+1 < n).
+    // Q (and the draft mask) must have arrived before the loop: the compiler
+    // would otherwise wait for them inside it with vmcnt counts that do not
+    // know about the direct loads, i.e. wait for those too.
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+    using DT = DmaTile<D, NT>;
+    constexpr int TILE = Swz<D>::TILE;
+    constexpr int KL = DT::kLoads;
+    DT dma;
+    dma.init(tid);
+    FragAddr<D> fa;
+    fa.init(lane);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
+    auto issue_k = [&](int u, int sidx) {
+      const UnitInfo ui = unit_info(u);
+      dma.issue(lds0 + sidx * TILE, kptr(ui), ui.nv, tid, wave_u);
+    };
+    auto issue_v = [&](int u, int sidx) {
+      const UnitInfo ui = unit_info(u);
+      dma.issue(lds0 + (2 + sidx) * TILE, vptr(ui), ui.nv, tid, wave_u);
+    };
+    const int n = u_end - u_begin;
+    if (n > 0) { issue_k(u_begin, 0); issue_v(u_begin, 0); }
+    if (n > 1) issue_k(u_begin + 1, 1);
+    auto iter = [&](int i, auto stage_tag) {
+      constexpr int S = decltype(stage_tag)::value;
+      const int u = u_begin + i;
+      const bool more = i + 1 < n;
+      if (more) wait_vm_barrier<2 * KL>(); else wait_vm_barrier<KL>();
+      if (more) issue_v(u + 1, S ^ 1);
+      const UnitInfo ui = unit_info(u);
+      const uint32_t kb = lds0 + S * TILE, vb = lds0 + (2 + S) * TILE;
+      auto kfrag = [&](int kt, int ks) {
+        return lds_read16(kb + fa.k(ks) + kt * 32 * Swz<D>::RB);
+      };
+      auto vfrag = [&](int dt, int kt, int t) {
+        const uint32_t off = vb + (32 * kt + 16 * t) * Swz<D>::RB;
+        const bf16x4 lo = lds_read_tr8(off + fa.v(dt, 0));
+        const bf16x4 hi = lds_read_tr8(off + fa.v(dt, 1));
+        return (bf16x8)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      const int lim = chunk_lim(ui);
+      const bool use = __ballot(lim >= 0) != 0;
+      typename RowState<D>::PFrag pf;
+      if (use) pf = st.template scores<kLookahead>(kfrag, lim, ui.isd, my_bits, a.scale_log2);
+      if (more) wait_vm_barrier<2 * KL>(); else wait_vm_barrier<0>();
+      if (i + 2 < n) issue_k(u + 2, S);
+      if (use) st.template pv<kLookahead>(vfrag, pf);
+    };
+    for (int i = 0; i < n; i += 2) {
+      iter(i, StageTag<0>());
+      if (i + 1 < n) iter(i + 1, StageTag<1>());
+    }
+  } else if constexpr (PF == 1) {
     // register prefetch one chunk ahead; store -> barrier -> prefetch -> compute
     Stager<D, NT> sg;
     UnitInfo cur = {0, 0, 0u, false};
@@ -790,13 +1295,17 @@ int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
 // Prefill uses W = min(4, G) waves (TT = 32/G * W <= 32 tokens per tile).
 template <int D>
 int dispatch_prefill(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+#ifndef INFLLMV2_PREFILL_PF
+#define INFLLMV2_PREFILL_PF 4
+#endif
+  constexpr int PF = INFLLMV2_PREFILL_PF;
   switch (G) {
-    case 1:  return launch_attn<D, 1, 1, kPrefill>(a, grid, st);
-    case 2:  return launch_attn<D, 2, 2, kPrefill>(a, grid, st);
-    case 4:  return launch_attn<D, 4, 4, kPrefill>(a, grid, st);
-    case 8:  return launch_attn<D, 8, 4, kPrefill>(a, grid, st);
-    case 16: return launch_attn<D, 16, 4, kPrefill>(a, grid, st);
-    case 32: return launch_attn<D, 32, 4, kPrefill>(a, grid, st);
+    case 1:  return launch_attn<D, 1, 1, kPrefill, PF>(a, grid, st);
+    case 2:  return launch_attn<D, 2, 2, kPrefill, PF>(a, grid, st);
+    case 4:  return launch_attn<D, 4, 4, kPrefill, PF>(a, grid, st);
+    case 8:  return launch_attn<D, 8, 4, kPrefill, PF>(a, grid, st);
+    case 16: return launch_attn<D, 16, 4, kPrefill, PF>(a, grid, st);
+    case 32: return launch_attn<D, 32, 4, kPrefill, PF>(a, grid, st);
   }
   return INFLLMV2_ERR_UNSUPPORTED;
 }
