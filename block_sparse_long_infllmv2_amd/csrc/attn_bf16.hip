@@ -184,12 +184,12 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
 }
 
-template <int D, int NT>
+template <int D, int NT, class SW = Swz<D>>
 struct DmaTile {
-  static constexpr int CPR = Swz<D>::CPR;
-  static constexpr int RB = Swz<D>::RB;
-  static constexpr int kLoads = Swz<D>::TILE / (NT * 16);   // per thread and tile
-  static_assert(kLoads >= 1 && Swz<D>::TILE % (NT * 16) == 0, "tile copy shape");
+  static constexpr int CPR = SW::CPR;
+  static constexpr int RB = SW::RB;
+  static constexpr int kLoads = SW::TILE / (NT * 16);   // per thread and tile
+  static_assert(kLoads >= 1 && SW::TILE % (NT * 16) == 0, "tile copy shape");
   static_assert(2 * kLoads <= 63, "vmcnt range");
   // Instruction i, thread t -> LDS slot s = i*NT + t: row s / CPR, position
   // s % CPR.  When one instruction spans a multiple of 16 rows, the swizzle
@@ -203,7 +203,7 @@ struct DmaTile {
 #pragma unroll
     for (int i = 0; i < (kUniform ? 1 : kLoads); ++i) {
       const int s = i * NT + tid, r = s / CPR;
-      voff[i] = (uint32_t)(r * RB + (((s % CPR) ^ Swz<D>::f(r)) * 16));
+      voff[i] = (uint32_t)(r * RB + (((s % CPR) ^ SW::f(r)) * 16));
     }
   }
   // rows >= nv are copies of row nv - 1 (finite data; the softmax masks them)
@@ -225,7 +225,7 @@ struct DmaTile {
         const int s = i * NT + tid, r = s / CPR;
         const int rr = r < last ? r : last;
         lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g,
-                  (uint32_t)(rr * RB + (((s % CPR) ^ Swz<D>::f(r)) * 16)));
+                  (uint32_t)(rr * RB + (((s % CPR) ^ SW::f(r)) * 16)));
       }
     }
   }
@@ -1180,6 +1180,309 @@ void attn_bf16_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Prefill with 16 query rows per wave: one token's 16 heads of a KV group, on
+// v_mfma_f32_16x16x32_bf16.  Operand layouts (lane l = j + 16 h):
+//   A[i][k]: lane i + 16 (k/8), element k%8     (16 x 32)
+//   B[k][j]: lane j + 16 (k/8), element k%8     (32 x 16)
+//   D[i][j]: lane j + 16 (i/4), register i%4    (16 x 16, float32)
+// As in the 32-row kernel the products are transposed: S^T = K Q^T (A = 16
+// keys of K, B = Q^T) and O^T = V^T P^T, so lane (j, h) owns query row j:
+// its S^T registers hold keys 16 kt + 4 h + r of key tile kt, and the P^T
+// B operand of k-step s is built from its own registers, element e <-> key
+// 16 (2 s + e/4) + 4 h + e%4.  V^T fragments come from transposing LDS reads.
+// A wave computes exactly the chunks its token kept: a workgroup of 8 waves
+// stages the union of its 8 tokens' blocks and each wave skips the others.
+// Per-wave state is half that of the 32-row kernel, so four waves share a
+// SIMD and hide each other's barrier and staging waits.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Swz16 {
+  static constexpr int RB = 2 * D;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = kChunk * RB;
+  // K reads: 16 consecutive rows, one logical chunk -> 16 distinct bank
+  // groups.  V reads (32 lanes): 8 consecutive rows x chunk pair {2m, 2m+1}
+  // -> 16 distinct groups.  Depends on r mod 16 only.
+  __device__ static __forceinline__ int f(int r) {
+    return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  }
+};
+
+template <int D>
+struct Row16 {
+  static constexpr int NKS = D / 32;       // QK k-steps of 32 dims
+  static constexpr int NDT = D / 16;       // O^T d-tiles of 16
+  static constexpr int RB = Swz16<D>::RB;
+  bf16x8 q[NKS];                           // lane (j, h): Q[row j][32 ks + 8 h .. +8]
+  f32x4 o[NDT];                            // lane (j, h): O[row j][16 dt + 4 h + r]
+  float m, l;
+  uint32_t k0, v0;                         // fragment addresses inside a tile
+  struct PFrag { bf16x8 f[2]; };
+
+  __device__ __forceinline__ void init(int lane) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m = kNoMax;
+    l = 0.0f;
+    const int i = lane & 15, h = lane >> 4;
+    // K A operand, key tile kt, k-step ks: row 16 kt + i, logical chunk 4 ks + h
+    k0 = (uint32_t)(i * RB + ((h ^ Swz16<D>::f(i)) * 16));
+    // V^T A operand, d-tile dt, k-step s, half c: this lane addresses row
+    // 16 (2 s + c) + 4 h + i/4 at d = 16 dt + 4 (i%4) (8 bytes)
+    const int row = 4 * h + (i >> 2), qd = i & 3;
+    v0 = (uint32_t)(row * RB + (((qd >> 1) ^ Swz16<D>::f(row)) * 16) + 8 * (qd & 1));
+  }
+  __device__ __forceinline__ uint32_t kaddr(int kt, int ks) const {
+    return (k0 ^ (uint32_t)(64 * ks)) + (uint32_t)(16 * kt * RB);
+  }
+  __device__ __forceinline__ uint32_t vaddr(int dt, int s, int c) const {
+    return (v0 ^ (uint32_t)(32 * dt)) + (uint32_t)(16 * (2 * s + c) * RB);
+  }
+
+  // S^T for the 64 keys of the tile at kb: 4 independent accumulation chains
+  __device__ __forceinline__ void qk(uint32_t kb, f32x4 (&s)[4]) const {
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(kb + kaddr(kt, ks)), q[ks],
+                                                        s[kt], 0, 0, 0);
+  }
+
+  // keys past `lim` -> -inf (partial chunks)
+  __device__ __forceinline__ void mask(f32x4 (&s)[4], int lim) const {
+    const int h = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s[kt][r] = 16 * kt + 4 * h + r <= lim ? s[kt][r] : -INFINITY;
+  }
+
+  // online softmax (log2 domain, lazy rescale as in the 32-row kernel); rows
+  // with keep == false get p = 0 and leave m, l unchanged
+  __device__ __forceinline__ PFrag softmax(f32x4 (&s)[4], bool keep, float scale_log2) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
+    mx = keep ? mx * scale_log2 : -INFINITY;
+    // the row's other 48 keys sit in lanes j + 16, j + 32, j + 48
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    const float m_new = mx > m + kRescaleSlack ? mx : m;
+    const float alpha = fast_exp2(m - m_new);
+    const float msub = keep ? m_new : INFINITY;
+    float psum = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -msub));
+        s[kt][r] = p;
+        psum += p;
+      }
+    m = m_new;
+    l = l * alpha + psum;
+    if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+    }
+    PFrag pf;
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf.f[sidx][e] = (__bf16)s[2 * sidx + (e >> 2)][e & 3];
+    return pf;
+  }
+
+  // O^T += V^T P^T for the tile at vb; k-step outer, d-tile inner
+  __device__ __forceinline__ void pv(uint32_t vb, const PFrag& pf) {
+#pragma unroll
+    for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x4 lo = lds_read_tr8(vb + vaddr(dt, sidx, 0));
+        const bf16x4 hi = lds_read_tr8(vb + vaddr(dt, sidx, 1));
+        const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pf.f[sidx], o[dt], 0, 0, 0);
+      }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void attn16_prefill_kernel(AttnArgs a) {
+  constexpr int G = 16, W = 8, NT = W * 64;
+  constexpr int TT = W;                          // one token per wave
+  constexpr int TILE = Swz16<D>::TILE;
+  constexpr int SORT_N = TT * kSortCap;
+  constexpr int ECAP = TT * kSortCap;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2 * TILE];   // K0 K1 V0 V1
+  __shared__ int2 ents[ECAP];
+  __shared__ int scan_lds[NT / 64];
+  static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int w = xcd_contiguous_index(blockIdx.x, gridDim.x);
+  const int g = w / a.n_tiles, tile = w % a.n_tiles;
+  const int n_keys = (int)a.n_k;
+  const int tok0 = tile * TT;
+  const int n_tok = min(TT, a.n_rows - tok0);
+  const bool dense = n_keys < a.dense_len || a.block_idx == nullptr;
+  const int n_b = (n_keys + a.B - 1) / a.B;
+  const int cpb = (a.B + kChunk - 1) / kChunk;
+  const uint32_t full_mask = n_tok >= 32 ? 0xffffffffu : ((1u << n_tok) - 1u);
+  const int p0 = (int)a.n_k - a.n_rows + tok0;   // query position of the tile's first token
+
+  const int my_t = wave;                          // this wave's token
+  const bool row_ok = my_t < n_tok;
+  const int my_row = tok0 + (row_ok ? my_t : 0);
+  const int my_head = g * G + (lane & 15);
+  const int my_pos = p0 + (row_ok ? my_t : 0);
+
+  int n_entries;
+  if (dense) {
+    n_entries = (p0 + n_tok - 1) / a.B + 1;
+  } else {
+    int N = 1;
+    while (N < TT * a.topk) N <<= 1;
+    if (N < NT) N = NT;
+    n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, n_b,
+                                    reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
+  }
+  const int n = n_entries * cpb;
+
+  // unit u -> first key, valid keys, mask of the tile's tokens that use it
+  struct Unit { int key0, nv; uint32_t tm; };
+  auto unit_lane = [&](int u) -> Unit {
+    Unit r;
+    int e = u, c = 0;
+    if (cpb != 1) { e = u / cpb; c = u - e * cpb; }
+    int b;
+    if (dense) {
+      b = e;
+      const int t_min = b * a.B - p0;      // token t keeps block b iff t >= b*B - p0
+      r.tm = t_min <= 0 ? full_mask : (t_min >= 32 ? 0u : (full_mask & (0xffffffffu << t_min)));
+    } else {
+      const int2 en = ents[e];
+      b = en.x;
+      r.tm = (uint32_t)en.y;
+    }
+    r.key0 = b * a.B + c * kChunk;
+    r.nv = max(0, min(kChunk, min((b + 1) * a.B, n_keys) - r.key0));
+    return r;
+  };
+  // metadata of 64 consecutive units, one per lane, read with readlane
+  int wb = 0;
+  Unit wl = {0, 0, 0u};
+  auto load_window = [&]() {
+    const int uu = wb + lane;
+    if (uu < n) wl = unit_lane(uu); else wl = Unit{0, 0, 0u};
+  };
+  load_window();
+  auto info = [&](int u) -> Unit {
+    if (u >= n) return Unit{0, 0, 0u};
+    if (u >= wb + 64) {
+      wb += 64;
+      load_window();
+    }
+    const int ln = u - wb;
+    return Unit{__builtin_amdgcn_readlane(wl.key0, ln), __builtin_amdgcn_readlane(wl.nv, ln),
+                (uint32_t)__builtin_amdgcn_readlane((int)wl.tm, ln)};
+  };
+
+  const uint16_t* kseq = a.k + (int64_t)g * a.cap * D;
+  const uint16_t* vseq = a.v + (int64_t)g * a.cap * D;
+  auto kp = [&](const Unit& un) { return kseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
+  auto vp = [&](const Unit& un) { return vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
+
+  Row16<D> st;
+  st.init(lane);
+  {
+    const uint16_t* qrow = a.q + ((int64_t)my_row * a.h_q + my_head) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < Row16<D>::NKS; ++ks) {
+      u32x4 wv = {0u, 0u, 0u, 0u};
+      if (row_ok) wv = ldg16(qrow + 32 * ks);
+      st.q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
+
+  using DT = DmaTile<D, NT, Swz16<D>>;
+  DT dma;
+  dma.init(tid);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
+  // chunk i sits in K[i&1] (lds0 + (i&1) TILE) and V[i&1] (lds0 + (2 + (i&1)) TILE).
+  // Iteration i: barrier (chunk i landed, iteration i-1 done everywhere),
+  // copy chunk i+1 into the other stage, compute chunk i.
+  Unit cur = info(0);
+  if (n > 0) {
+    dma.issue(lds0, kp(cur), cur.nv, tid, wave_u);
+    dma.issue(lds0 + 2 * TILE, vp(cur), cur.nv, tid, wave_u);
+  }
+  auto iter = [&](int i, auto stage_tag) {
+    constexpr int S = decltype(stage_tag)::value;
+    wait_vm_barrier<0>();
+    const Unit nxt = info(i + 1);
+    if (i + 1 < n) {
+      dma.issue(lds0 + (1 - S) * TILE, kp(nxt), nxt.nv, tid, wave_u);
+      dma.issue(lds0 + (3 - S) * TILE, vp(nxt), nxt.nv, tid, wave_u);
+    }
+    int lim = -1;
+    if (row_ok && ((cur.tm >> my_t) & 1u)) lim = min(my_pos - cur.key0, cur.nv - 1);
+    // lim is the same in all lanes of the wave (one token): a scalar branch
+    lim = __builtin_amdgcn_readfirstlane(lim);
+    if (lim >= 0) {
+      f32x4 sc[4];
+      st.qk(lds0 + S * TILE, sc);
+      if (lim < kChunk - 1) st.mask(sc, lim);
+      const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
+      st.pv(lds0 + (2 + S) * TILE, pf);
+    }
+    cur = nxt;
+  };
+  for (int i = 0; i < n; i += 2) {
+    iter(i, StageTag<0>());
+    if (i + 1 < n) iter(i + 1, StageTag<1>());
+  }
+
+  // row sum over the four lanes of the row, then normalise and store
+  float lt = st.l;
+  {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                      false, false);
+    lt = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                      false, false);
+    lt = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  }
+  if (row_ok) {
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    const int h = lane >> 4;
+    uint16_t* orow = a.out + ((int64_t)my_row * a.h_q + my_head) * D;
+#pragma unroll
+    for (int dt = 0; dt < Row16<D>::NDT; ++dt) {
+      u32x2 wv;
+      wv.x = pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv);
+      wv.y = pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv);
+      *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * h) = wv;
+    }
+    if (a.lse && h == 0) a.lse[(int64_t)my_row * a.h_q + my_head] = (st.m + __log2f(lt)) * kLn2;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tree planner: union of the drafts' kept blocks per KV head (sorted, with the
 // bitmask of drafts that kept each block).  One workgroup per KV head.
 // ---------------------------------------------------------------------------
@@ -1299,6 +1602,10 @@ int dispatch_prefill(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
 #define INFLLMV2_PREFILL_PF 4
 #endif
   constexpr int PF = INFLLMV2_PREFILL_PF;
+  if (G == 16) {
+    hipLaunchKernelGGL((attn16_prefill_kernel<D>), grid, dim3(512), 0, st, a);
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   switch (G) {
     case 1:  return launch_attn<D, 1, 1, kPrefill, PF>(a, grid, st);
     case 2:  return launch_attn<D, 2, 2, kPrefill, PF>(a, grid, st);

@@ -222,6 +222,7 @@ def test_prefill_tiny_f32_config(B, PL):
     (9000, 133, 32, 2, 128, 64),     # ragged last KV block (9000 % 64 = 40)
     (3000, 200, 16, 2, 64, 8),       # G = 8, d = 64
     (2600, 64, 8, 2, 128, 8),        # G = 4: 32-token tiles
+    (5000, 150, 32, 2, 64, 16),      # G = 16, d = 64
 ])
 def test_prefill_bf16_end_to_end(B, PL, n_k, n_q, h_q, h_kv, d, topk):
     _say(f"prefill bf16 n_k={n_k} n_q={n_q} h_q={h_q} h_kv={h_kv} d={d} topk={topk}")
@@ -231,6 +232,16 @@ def test_prefill_bf16_end_to_end(B, PL, n_k, n_q, h_q, h_kv, d, topk):
     plan, ck = _run_prefill(B, PL, c)
     rows = sorted(set(list(range(0, n_q, 5)) + [n_q - 1, n_q - 2, 0, 7, 8, 9]))
     _check_prefill(plan, ck, c, rows)
+
+
+def test_prefill_bf16_block128(B, PL):
+    # 128-token blocks: two 64-key chunks per kept block, ragged last block
+    _say("prefill bf16 block_size=128")
+    p = Params(block_size=128, topk=8, dense_len=0)
+    c = make_prefill(9, n_k=7000, n_q=120, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=3, alpha=1.5, beta=1.5)
+    plan, ck = _run_prefill(B, PL, c)
+    _check_prefill(plan, ck, c, rows=list(range(0, 120, 4)) + [119])
 
 
 def test_prefill_bf16_dense_below_dense_len(B, PL):
