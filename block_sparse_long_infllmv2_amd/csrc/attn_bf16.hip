@@ -188,43 +188,48 @@ template <int D, int NT, class SW = Swz<D>>
 struct DmaTile {
   static constexpr int CPR = SW::CPR;
   static constexpr int RB = SW::RB;
-  static constexpr int kLoads = SW::TILE / (NT * 16);   // per thread and tile
-  static_assert(kLoads >= 1 && SW::TILE % (NT * 16) == 0, "tile copy shape");
+  // 16-byte slots per tile; with more threads than slots, the first
+  // kActive threads (whole waves) copy and the others issue nothing
+  static constexpr int kSlots = SW::TILE / 16;
+  static constexpr int kActive = kSlots >= NT ? NT : kSlots;
+  static constexpr int kLoads = kSlots / kActive;          // per copying thread and tile
+  static_assert(kActive % 64 == 0 && kSlots % kActive == 0, "tile copy shape");
   static_assert(2 * kLoads <= 63, "vmcnt range");
-  // Instruction i, thread t -> LDS slot s = i*NT + t: row s / CPR, position
-  // s % CPR.  When one instruction spans a multiple of 16 rows, the swizzle
-  // phase f(r) is the same for every i and the source offsets differ by a
-  // whole number of rows: one base offset, the row step goes to the pointer.
-  static constexpr int kRowsPerInst = NT / CPR;
+  // Instruction i, thread t -> LDS slot s = i*kActive + t: row s / CPR,
+  // position s % CPR.  When one instruction spans a multiple of 16 rows, the
+  // swizzle phase f(r) is the same for every i and the source offsets differ
+  // by a whole number of rows: one base offset, the row step goes to the pointer.
+  static constexpr int kRowsPerInst = kActive / CPR;
   static constexpr bool kUniform = kRowsPerInst % 16 == 0;
   uint32_t voff[kUniform ? 1 : kLoads];   // source byte offsets in a full tile
 
   __device__ __forceinline__ void init(int tid) {
 #pragma unroll
     for (int i = 0; i < (kUniform ? 1 : kLoads); ++i) {
-      const int s = i * NT + tid, r = s / CPR;
+      const int s = i * kActive + (tid % kActive), r = s / CPR;
       voff[i] = (uint32_t)(r * RB + (((s % CPR) ^ SW::f(r)) * 16));
     }
   }
   // rows >= nv are copies of row nv - 1 (finite data; the softmax masks them)
   __device__ __forceinline__ void issue(uint32_t lds_tile, const uint16_t* g, int nv, int tid,
                                         int wave) const {
+    if (kActive < NT && wave * 64 >= kActive) return;
     if (nv == kChunk) {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         if constexpr (kUniform)
-          lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g + i * kRowsPerInst * D,
-                    voff[0]);
+          lds_dma16(lds_tile + (uint32_t)(i * kActive + wave * 64) * 16u,
+                    g + i * kRowsPerInst * D, voff[0]);
         else
-          lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g, voff[i]);
+          lds_dma16(lds_tile + (uint32_t)(i * kActive + wave * 64) * 16u, g, voff[i]);
       }
     } else {
       const int last = nv > 0 ? nv - 1 : 0;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
-        const int s = i * NT + tid, r = s / CPR;
+        const int s = i * kActive + tid, r = s / CPR;
         const int rr = r < last ? r : last;
-        lds_dma16(lds_tile + (uint32_t)(i * NT + wave * 64) * 16u, g,
+        lds_dma16(lds_tile + (uint32_t)(i * kActive + wave * 64) * 16u, g,
                   (uint32_t)(rr * RB + (((s % CPR) ^ SW::f(r)) * 16)));
       }
     }
@@ -1317,15 +1322,17 @@ struct Row16 {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+// W waves (= tokens) per workgroup, NS staging slots of one K and one V tile.
+template <int D, int W, int NS>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
 void attn16_prefill_kernel(AttnArgs a) {
-  constexpr int G = 16, W = 8, NT = W * 64;
+  constexpr int G = 16, NT = W * 64;
   constexpr int TT = W;                          // one token per wave
+  static_assert(TT <= 32, "token bitmask is 32 bits");
   constexpr int TILE = Swz16<D>::TILE;
   constexpr int SORT_N = TT * kSortCap;
   constexpr int ECAP = TT * kSortCap;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2 * TILE];   // K0 K1 V0 V1
+  __shared__ __attribute__((aligned(16))) uint16_t stage[NS * TILE];   // K[0..NS) V[0..NS)
   __shared__ int2 ents[ECAP];
   __shared__ int scan_lds[NT / 64];
   static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
@@ -1419,26 +1426,42 @@ void attn16_prefill_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
 
   using DT = DmaTile<D, NT, Swz16<D>>;
+  constexpr int KL = DT::kLoads;
+  static_assert(2 * KL * (NS - 1) <= 63, "vmcnt range");
   DT dma;
   dma.init(tid);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
-  // chunk i sits in K[i&1] (lds0 + (i&1) TILE) and V[i&1] (lds0 + (2 + (i&1)) TILE).
-  // Iteration i: barrier (chunk i landed, iteration i-1 done everywhere),
-  // copy chunk i+1 into the other stage, compute chunk i.
+  // Chunk i sits in slot i % NS: K at lds0 + slot TILE, V at lds0 + (NS + slot) TILE.
+  // Iteration i: barrier (chunk i landed, iteration i-1 done everywhere, so
+  // slot (i-1) % NS is free), copy chunk i + NS - 1 into it, compute chunk i.
+  // At the barrier the copies issued after chunk i's are those of chunks
+  // i+1 .. i+NS-2, the ones that exist.
+  auto issue = [&](const Unit& un, int slot) {
+    dma.issue(lds0 + slot * TILE, kp(un), un.nv, tid, wave_u);
+    dma.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, tid, wave_u);
+  };
   Unit cur = info(0);
-  if (n > 0) {
-    dma.issue(lds0, kp(cur), cur.nv, tid, wave_u);
-    dma.issue(lds0 + 2 * TILE, vp(cur), cur.nv, tid, wave_u);
+  Unit ahead[NS > 2 ? NS - 2 : 1];       // chunks i+1 .. i+NS-2 (already issued)
+#pragma unroll
+  for (int j = 0; j + 1 < NS; ++j) {
+    const Unit un = j == 0 ? cur : info(j);
+    if (j < n) issue(un, j);
+    if (j >= 1 && j - 1 < NS - 2) ahead[j - 1] = un;
   }
   auto iter = [&](int i, auto stage_tag) {
     constexpr int S = decltype(stage_tag)::value;
-    wait_vm_barrier<0>();
-    const Unit nxt = info(i + 1);
-    if (i + 1 < n) {
-      dma.issue(lds0 + (1 - S) * TILE, kp(nxt), nxt.nv, tid, wave_u);
-      dma.issue(lds0 + (3 - S) * TILE, vp(nxt), nxt.nv, tid, wave_u);
+    // in flight after chunk i: chunks i+1 .. min(i+NS-2, n-1)
+    const int after = min(NS - 2, n - 1 - i);
+    if constexpr (NS == 2) {
+      wait_vm_barrier<0>();
+    } else {
+      if (after >= NS - 2) wait_vm_barrier<2 * KL * (NS - 2)>();
+      else if (NS > 3 && after >= 1) wait_vm_barrier<2 * KL>();
+      else wait_vm_barrier<0>();
     }
+    const Unit far = info(i + NS - 1);
+    if (i + NS - 1 < n) issue(far, (S + NS - 1) % NS);
     int lim = -1;
     if (row_ok && ((cur.tm >> my_t) & 1u)) lim = min(my_pos - cur.key0, cur.nv - 1);
     // lim is the same in all lanes of the wave (one token): a scalar branch
@@ -1448,13 +1471,29 @@ void attn16_prefill_kernel(AttnArgs a) {
       st.qk(lds0 + S * TILE, sc);
       if (lim < kChunk - 1) st.mask(sc, lim);
       const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
-      st.pv(lds0 + (2 + S) * TILE, pf);
+      st.pv(lds0 + (NS + S) * TILE, pf);
     }
-    cur = nxt;
+    if constexpr (NS == 2) {
+      cur = far;
+    } else {
+      cur = ahead[0];
+#pragma unroll
+      for (int j = 0; j + 1 < NS - 2; ++j) ahead[j] = ahead[j + 1];
+      ahead[NS - 3] = far;
+    }
   };
-  for (int i = 0; i < n; i += 2) {
-    iter(i, StageTag<0>());
-    if (i + 1 < n) iter(i + 1, StageTag<1>());
+  static_assert(NS == 2 || NS == 3, "staging depth");
+  if constexpr (NS == 2) {
+    for (int i = 0; i < n; i += 2) {
+      iter(i, StageTag<0>());
+      if (i + 1 < n) iter(i + 1, StageTag<1>());
+    }
+  } else {
+    for (int i = 0; i < n; i += 3) {
+      iter(i, StageTag<0>());
+      if (i + 1 < n) iter(i + 1, StageTag<1>());
+      if (i + 2 < n) iter(i + 2, StageTag<2>());
+    }
   }
 
   // row sum over the four lanes of the row, then normalise and store
@@ -1595,6 +1634,16 @@ int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
 }
 
+// 16-head groups: one token per wave, kRows16Waves tokens per workgroup.
+#ifndef INFLLMV2_ROWS16_WAVES
+#define INFLLMV2_ROWS16_WAVES 8
+#endif
+#ifndef INFLLMV2_ROWS16_STAGES
+#define INFLLMV2_ROWS16_STAGES 2
+#endif
+constexpr int kRows16Waves = INFLLMV2_ROWS16_WAVES;
+constexpr int kRows16Stages = INFLLMV2_ROWS16_STAGES;
+
 // Prefill uses W = min(4, G) waves (TT = 32/G * W <= 32 tokens per tile).
 template <int D>
 int dispatch_prefill(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
@@ -1603,7 +1652,8 @@ int dispatch_prefill(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
 #endif
   constexpr int PF = INFLLMV2_PREFILL_PF;
   if (G == 16) {
-    hipLaunchKernelGGL((attn16_prefill_kernel<D>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((attn16_prefill_kernel<D, kRows16Waves, kRows16Stages>), grid,
+                       dim3(kRows16Waves * 64), 0, st, a);
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   switch (G) {
@@ -1624,7 +1674,7 @@ int prefill_tile_tokens(int G) {
     case 2: return 32;
     case 4: return 32;
     case 8: return 16;
-    case 16: return 8;
+    case 16: return kRows16Waves;
     case 32: return 4;
   }
   return 0;

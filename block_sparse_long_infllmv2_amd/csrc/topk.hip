@@ -167,8 +167,65 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(TopkArgs a) {
 // comes from ballot prefix counts (block b = lane + 64 j precedes b' when
 // j < j', or j == j' and lane < lane').
 // ---------------------------------------------------------------------------
+// Keys a wave keeps in LDS for the threshold search after the lower-bound filter.
+constexpr int kSurvivors = 256;
+
+// k-th largest (1 <= k <= 64) of one value per lane: bitonic sort across the
+// wave (ascending), then the value at lane 64 - k.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k, int lane) {
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const uint32_t other = (uint32_t)__shfl_xor((int)v, stride, 64);
+      const bool up = (lane & size) == 0;
+      const bool low = (lane & stride) == 0;
+      const uint32_t mn = v < other ? v : other, mx = v < other ? other : v;
+      v = (low == up) ? mn : mx;
+    }
+  }
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 64 - k);
+}
+
+// Exclusive prefix sum over the lanes of a wave; *total = sum over all lanes.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total, int lane) {
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  *total = __builtin_amdgcn_readlane(x, 63);
+  return x - v;
+}
+
+// Largest T with #(key >= T) >= need over the wave's N keys per lane (keys
+// of 0 never count), found bit by bit from the top; *exact is set when the
+// count reaches need exactly (then T is the need-th largest and no tie
+// remains to break).  The keys may be only those >= lo (a lower bound of the
+// answer): below lo the counts are too small, which never changes a
+// `cnt >= need` decision there (all of them pass), but an exact count only
+// means something at candidates >= lo.
+template <int N>
+__device__ __forceinline__ uint32_t threshold_search(const uint32_t (&key)[N], int need,
+                                                     uint32_t lo, bool* exact) {
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) cnt += __popcll(__ballot(key[j] >= cand));
+    if (cnt >= need) {
+      T = cand;
+      if (cnt == need && cand >= lo) { *exact = true; break; }
+    }
+  }
+  return T;
+}
+
 template <int KPL>
 __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n_units) {
+  __shared__ uint32_t surv[4][kSurvivors];
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= n_units) return;                   // whole wave leaves
   const int lane = threadIdx.x & 63;
@@ -213,15 +270,37 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   uint32_t T = 0;
   bool exact = need <= 0;       // nothing to choose, or #(key >= T) == need
   if (need > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int cnt = 0;
+    // Lower bound: at least `need` lanes hold a key >= the need-th largest
+    // lane maximum, so T >= it and smaller keys cannot matter.  The keys at
+    // or above it usually number a few hundred: the search then runs on them
+    // (kSurvivors per wave in LDS) instead of on all 64 * KPL keys.
+    uint32_t lo = 0;
+    if (need <= 64) {
+      uint32_t mx = 0;
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) cnt += __popcll(__ballot(key[j] >= cand));
-      if (cnt >= need) {
-        T = cand;
-        if (cnt == need) { exact = true; break; }
-      }
+      for (int j = 0; j < KPL; ++j) mx = key[j] > mx ? key[j] : mx;
+      lo = wave_kth_largest(mx, need, lane);
+    }
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) mine += key[j] >= lo && key[j] != 0u;
+    int total;
+    const int off = wave_excl_scan(mine, &total, lane);
+    uint32_t* sv = surv[threadIdx.x >> 6];
+    if (lo != 0u && total <= kSurvivors) {
+      for (int i = lane; i < kSurvivors; i += 64) sv[i] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      int o = off;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j)
+        if (key[j] >= lo && key[j] != 0u) sv[o++] = key[j];
+      __builtin_amdgcn_wave_barrier();
+      uint32_t sk[kSurvivors / 64];
+#pragma unroll
+      for (int j = 0; j < kSurvivors / 64; ++j) sk[j] = sv[lane + 64 * j];
+      T = threshold_search<kSurvivors / 64>(sk, need, lo, &exact);
+    } else {
+      T = threshold_search<KPL>(key, need, 0u, &exact);
     }
   }
   // keys > T are kept; of the keys == T the lowest-indexed ones fill the rest
