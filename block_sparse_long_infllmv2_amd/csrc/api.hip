@@ -5,7 +5,8 @@ namespace infllmv2 {
 int64_t decode_splits(int64_t max_seqlen, const Resolved& r);
 size_t tree_workspace_bytes(int n_draft, int h_q, int h_kv, int d, int64_t n_ctx,
                             const Resolved& r);
-size_t decode_workspace_bytes(int batch, int h_q, int d, int64_t max_seqlen, const Resolved& r);
+size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,
+                              const Resolved& r);
 }  // namespace infllmv2
 
 using namespace infllmv2;
@@ -45,7 +46,7 @@ extern "C" size_t infllmv2_workspace_size(int op, int32_t n, int32_t h_q, int32_
   if (n < 0 || max_len <= 0 || check_heads(h_q, h_kv) != INFLLMV2_OK || !head_dim_ok(d) ||
       check_params(p, d, &r) != INFLLMV2_OK)
     return 0;
-  if (op == INFLLMV2_OP_DECODE) return decode_workspace_bytes(n, h_q, d, max_len, r);
+  if (op == INFLLMV2_OP_DECODE) return decode_workspace_bytes(n, h_q, h_kv, d, max_len, r);
   if (op == INFLLMV2_OP_TREE) {
     if (n > 64) return 0;
     return tree_workspace_bytes(n, h_q, h_kv, d, max_len, r);

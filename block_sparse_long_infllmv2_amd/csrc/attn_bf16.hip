@@ -786,10 +786,17 @@ void attn_bf16_kernel(AttnArgs a) {
     if (dense) {
       n_entries = n_b;
     } else {
+      // kept blocks = the leading valid entries of the list (topk <= 128)
       const int32_t* lst = a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk;
-      int n = 0;
-      while (n < a.topk && lst[n] >= 0 && lst[n] < n_b) ++n;
-      n_entries = n;
+      int nn = a.topk;
+#pragma unroll
+      for (int hf = 1; hf >= 0; --hf) {
+        const int i = 64 * hf + lane;
+        const int32_t b = i < a.topk ? lst[i] : -1;
+        const uint64_t bad = __ballot(i < a.topk && !(b >= 0 && b < n_b));
+        if (bad) nn = 64 * hf + (int)__builtin_ctzll(bad);
+      }
+      n_entries = nn;
     }
   } else {
     n_entries = dense ? n_b : a.union_len[g];
@@ -1522,6 +1529,149 @@ void attn16_prefill_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Decode with one wave per (sequence, KV head, split): the decode token's 16
+// heads of the group are one 16-row tile of v_mfma_f32_16x16x32_bf16.  The
+// wave copies its chunks straight into a two-slot LDS ring, the second copy
+// issued before the first chunk is used, so a split's loads overlap each
+// other and those of every other split on the GPU.  Writes float32 partials
+// (o, m, l) that the combine kernel merges.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
+  constexpr int NS = 2;
+  constexpr int TILE = Swz16<D>::TILE;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[NS * TILE];   // K0 K1 V0 V1
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
+  // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
+  const int Lr = a.seqlens[seq];
+  const int L = Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr);
+  const bool dense = L < a.dense_len || a.block_idx == nullptr;
+  const int n_b = (L + a.B - 1) / a.B;
+  const int cpb = (a.B + kChunk - 1) / kChunk;
+  const int32_t* lst = a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk;
+  int n_entries = n_b;
+  if (!dense) {
+    // kept blocks = the leading valid entries of the list (topk <= 128):
+    // one load per lane and a ballot instead of a chain of dependent loads
+    n_entries = a.topk;
+#pragma unroll
+    for (int half = 1; half >= 0; --half) {
+      const int i = 64 * half + lane;
+      const int32_t b = i < a.topk ? lst[i] : -1;
+      const uint64_t bad = __ballot(i < a.topk && !(b >= 0 && b < n_b));
+      if (bad) n_entries = 64 * half + (int)__builtin_ctzll(bad);
+    }
+  }
+  const int units = n_entries * cpb;
+  const int per = (units + a.n_split - 1) / a.n_split;
+  const int u_begin = min(units, split * per);
+  const int n = min(units, u_begin + per) - u_begin;
+  // this split's block ids, one per lane (a split spans at most 64 entries),
+  // loaded before any direct copy is issued so that no global load of the
+  // loop makes the compiler wait on the copies
+  const int e_base = u_begin / cpb;
+  int blk_lane = e_base + lane;
+  if (!dense) blk_lane = e_base + lane < n_entries ? lst[e_base + lane] : 0;
+  struct Unit { int key0, nv; };
+  auto unit = [&](int u) -> Unit {
+    int e = u, c = 0;
+    if (cpb != 1) { e = u / cpb; c = u - e * cpb; }
+    const int b = __builtin_amdgcn_readlane(blk_lane, e - e_base);
+    Unit r;
+    r.key0 = b * a.B + c * kChunk;
+    r.nv = max(0, min(kChunk, min((b + 1) * a.B, L) - r.key0));
+    r.key0 = __builtin_amdgcn_readfirstlane(r.key0);
+    r.nv = __builtin_amdgcn_readfirstlane(r.nv);
+    return r;
+  };
+  const int64_t kv_off = ((int64_t)seq * a.h_kv + g) * a.cap * D;
+  const uint16_t* kseq = a.k + kv_off;
+  const uint16_t* vseq = a.v + kv_off;
+  auto kp = [&](const Unit& un) { return kseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
+  auto vp = [&](const Unit& un) { return vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
+
+  const int head = g * 16 + (lane & 15);
+  Row16<D> st;
+  st.init(lane);
+  {
+    const uint16_t* qrow = a.q + ((int64_t)seq * a.h_q + head) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < Row16<D>::NKS; ++ks) {
+      const u32x4 wv = ldg16(qrow + 32 * ks);
+      st.q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
+
+  using DT = DmaTile<D, 64, Swz16<D>>;
+  constexpr int KL = DT::kLoads;
+  DT dma;
+  dma.init(lane);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
+  auto issue = [&](const Unit& un, int slot) {
+    dma.issue(lds0 + slot * TILE, kp(un), un.nv, lane, 0);
+    dma.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, lane, 0);
+  };
+  Unit cur = {0, 0}, nxt = {0, 0};
+  if (n > 0) { cur = unit(u_begin); issue(cur, 0); }
+  if (n > 1) { nxt = unit(u_begin + 1); issue(nxt, 1); }
+  const int pos = L - 1;
+  auto step = [&](int i, auto slot_tag) {
+    constexpr int S = decltype(slot_tag)::value;
+    // the copy of chunk i+1 (if any) was issued after chunk i's
+    if (i + 1 < n) wait_vm<2 * KL>(); else wait_vm<0>();
+    const int lim = min(pos - cur.key0, cur.nv - 1);
+    if (lim >= 0) {
+      f32x4 sc[4];
+      st.qk(lds0 + S * TILE, sc);
+      if (lim < kChunk - 1) st.mask(sc, lim);
+      const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
+      st.pv(lds0 + (NS + S) * TILE, pf);
+    }
+    if (i + 2 < n) {
+      // slot S is free once this wave's reads of it have returned
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const Unit far = unit(u_begin + i + 2);
+      issue(far, S);
+      cur = nxt;
+      nxt = far;
+    } else {
+      cur = nxt;
+    }
+  };
+  for (int i = 0; i < n; i += 2) {
+    step(i, StageTag<0>());
+    if (i + 1 < n) step(i + 1, StageTag<1>());
+  }
+
+  // partials: lane (j, h) holds O[row j][16 dt + 4 h + r]; m is per row, l per lane
+  float lt = st.l;
+  {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                      false, false);
+    lt = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt),
+                                                      false, false);
+    lt = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  }
+  const int h = lane >> 4;
+  float* part = a.ws + (((int64_t)seq * a.h_q + head) * a.n_split + split) * (D + 2);
+#pragma unroll
+  for (int dt = 0; dt < Row16<D>::NDT; ++dt)
+    *reinterpret_cast<f32x4*>(part + 16 * dt + 4 * h) = st.o[dt];
+  if (h == 0) {
+    part[D] = st.m;
+    part[D + 1] = lt;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tree planner: union of the drafts' kept blocks per KV head (sorted, with the
 // bitmask of drafts that kept each block).  One workgroup per KV head.
 // ---------------------------------------------------------------------------
@@ -1599,12 +1749,14 @@ __global__ __launch_bounds__(64) void combine_kernel(const float* ws, int n_spli
   float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.0f;
+  // no branch in the loop, so the loads of all splits can be in flight
+  // together (empty splits have weight 0 and finite partials)
+#pragma unroll 4
   for (int s = 0; s < n_split; ++s) {
     const float ww = wsh[s];
-    if (ww == 0.0f) continue;
     const float* p = base + s * (D + 2);
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] += ww * p[lane + 64 * i];
+    for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(ww, p[lane + 64 * i], acc[i]);
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
@@ -1707,6 +1859,10 @@ int tree_tile_tokens(int G) {
 
 template <int D>
 int dispatch_decode(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  if (G == 16) {
+    hipLaunchKernelGGL((attn16_decode_kernel<D>), grid, dim3(64), 0, st, a);
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   switch (G) {
     case 1:  return launch_attn<D, 1, 4, kDecode>(a, grid, st);
     case 2:  return launch_attn<D, 2, 4, kDecode>(a, grid, st);
@@ -1763,6 +1919,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t partial_bytes(int rows, int h_q, int d, int64_t n_split) {
   return align256((size_t)rows * h_q * n_split * (d + 2) * sizeof(float));
 }
+
+size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,
+                              const Resolved& r);
 
 }  // namespace infllmv2
 
@@ -1827,7 +1986,7 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   if (batch == 0) return INFLLMV2_OK;
   const int64_t n_split = decode_splits(max_seqlen, r);
   if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
-  const size_t need = partial_bytes(batch, h_q, d, n_split);
+  const size_t need = decode_workspace_bytes(batch, h_q, h_kv, d, max_seqlen, r);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
   AttnArgs a = {};
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
@@ -1860,8 +2019,9 @@ size_t tree_workspace_bytes(int n_draft, int h_q, int h_kv, int d, int64_t n_ctx
          align256((size_t)h_kv * ucap * 4) + align256((size_t)h_kv * ucap * 8) +
          align256((size_t)h_kv * 4);
 }
-size_t decode_workspace_bytes(int batch, int h_q, int d, int64_t max_seqlen,
+size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,
                               const Resolved& r) {
+  (void)h_kv;
   return partial_bytes(batch, h_q, d, decode_splits(max_seqlen, r));
 }
 }  // namespace infllmv2

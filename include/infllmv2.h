@@ -195,7 +195,8 @@ int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_q,
  *            NULL when max_seqlen < dense_len)
  *   out  [batch][h_q][d]        lse float32 [batch][h_q] or NULL
  *   ws   >= infllmv2_workspace_size(INFLLMV2_OP_DECODE, batch, h_q, h_kv, d,
- *            max_seqlen, p) bytes, 256-byte aligned
+ *            max_seqlen, p) bytes, 256-byte aligned; contents on entry do
+ *            not matter.  Calls that share a workspace must not overlap.
  */
 int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t batch,
                                 const void* k, const void* v, int64_t cap,

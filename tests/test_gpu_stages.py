@@ -277,6 +277,7 @@ def _run_decode(B, PL, c, cap=None):
     plan = PL.DecodePlan(bsz, maxL, h_q, h_kv, d, tdt(c.dtype), p)
     plan.run(q, k, v, ck, seqlens)
     torch.cuda.synchronize()
+    plan.inputs = (q, k, v, ck, seqlens)
     return plan
 
 
@@ -299,13 +300,29 @@ def _check_decode(plan, c):
 
 
 @pytest.mark.parametrize("dtype,d,h_q,h_kv", [("bf16", 128, 32, 2), ("f32", 64, 4, 2),
-                                              ("bf16", 64, 8, 1)])
+                                              ("bf16", 64, 8, 1), ("bf16", 64, 16, 1)])
 def test_decode_ragged(B, PL, dtype, d, h_q, h_kv):
     _say(f"decode ragged {dtype} d={d} h_q={h_q} h_kv={h_kv}")
     p = Params(dense_len=2048, topk=16)
     c = make_decode(7, [100, 2047, 2048, 5000, 9001, 64, 1], h_q=h_q, h_kv=h_kv, d=d, params=p,
                     dtype=dtype, planted_per_token=1 / 512)
     plan = _run_decode(B, PL, c)
+    _check_decode(plan, c)
+
+
+def test_decode_repeated_calls_reuse_workspace(B, PL):
+    # a workspace holds nothing across calls: reusing it gives the same result
+    _say("decode repeated calls")
+    p = Params(dense_len=2048, topk=16)
+    c = make_decode(11, [3000, 9001, 64], h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                    planted_per_token=1 / 512)
+    plan = _run_decode(B, PL, c)
+    first = plan.out.clone()
+    plan.ws.fill_(0xAB)
+    for _ in range(3):
+        plan.run(*plan.inputs)
+        torch.cuda.synchronize()
+        assert torch.equal(plan.out, first)
     _check_decode(plan, c)
 
 
