@@ -201,13 +201,18 @@ struct DmaTile {
   // by a whole number of rows: one base offset, the row step goes to the pointer.
   static constexpr int kRowsPerInst = kActive / CPR;
   static constexpr bool kUniform = kRowsPerInst % 16 == 0;
-  uint32_t voff[kUniform ? 1 : kLoads];   // source byte offsets in a full tile
+  // source byte offsets in a full tile; the uniform case recomputes its single
+  // offset at each issue (a few VALU) instead of holding a register
+  uint32_t voff[kUniform ? 1 : kLoads];
 
+  __device__ static __forceinline__ uint32_t offset(int i, int tid) {
+    const int s = i * kActive + (tid % kActive), r = s / CPR;
+    return (uint32_t)(r * RB + (((s % CPR) ^ SW::f(r)) * 16));
+  }
   __device__ __forceinline__ void init(int tid) {
+    if constexpr (!kUniform) {
 #pragma unroll
-    for (int i = 0; i < (kUniform ? 1 : kLoads); ++i) {
-      const int s = i * kActive + (tid % kActive), r = s / CPR;
-      voff[i] = (uint32_t)(r * RB + (((s % CPR) ^ SW::f(r)) * 16));
+      for (int i = 0; i < kLoads; ++i) voff[i] = offset(i, tid);
     }
   }
   // rows >= nv are copies of row nv - 1 (finite data; the softmax masks them)
@@ -215,11 +220,12 @@ struct DmaTile {
                                         int wave) const {
     if (kActive < NT && wave * 64 >= kActive) return;
     if (nv == kChunk) {
+      const uint32_t off0 = kUniform ? offset(0, tid) : 0u;
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         if constexpr (kUniform)
           lds_dma16(lds_tile + (uint32_t)(i * kActive + wave * 64) * 16u,
-                    g + i * kRowsPerInst * D, voff[0]);
+                    g + i * kRowsPerInst * D, off0);
         else
           lds_dma16(lds_tile + (uint32_t)(i * kActive + wave * 64) * 16u, g, voff[i]);
       }
@@ -1207,18 +1213,28 @@ void attn_bf16_kernel(AttnArgs a) {
 // Per-wave state is half that of the 32-row kernel, so four waves share a
 // SIMD and hide each other's barrier and staging waits.
 // ---------------------------------------------------------------------------
+// K and V tiles use different chunk swizzles, each free of LDS bank
+// conflicts for its own read pattern (checked with the bank-conflict counter
+// on gfx950; both depend on r mod 16 only):
+//   K, 16-byte reads: 16 consecutive rows read one logical chunk;
+//   V, transposing 8-byte reads: 8 consecutive rows x chunk pair {2m, 2m+1}.
 template <int D>
-struct Swz16 {
+struct Swz16K {
   static constexpr int RB = 2 * D;
   static constexpr int CPR = D / 8;
   static constexpr int TILE = kChunk * RB;
-  // K reads: 16 consecutive rows, one logical chunk -> 16 distinct bank
-  // groups.  V reads (32 lanes): 8 consecutive rows x chunk pair {2m, 2m+1}
-  // -> 16 distinct groups.  Depends on r mod 16 only.
+  __device__ static __forceinline__ int f(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+};
+template <int D>
+struct Swz16V {
+  static constexpr int RB = 2 * D;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = kChunk * RB;
   __device__ static __forceinline__ int f(int r) {
     return D == 128 ? 2 * (r & 7) + ((r >> 3) & 1) : 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
   }
 };
+template <int D> using Swz16 = Swz16V<D>;   // tile geometry (same for K and V)
 
 template <int D>
 struct Row16 {
@@ -1238,11 +1254,11 @@ struct Row16 {
     l = 0.0f;
     const int i = lane & 15, h = lane >> 4;
     // K A operand, key tile kt, k-step ks: row 16 kt + i, logical chunk 4 ks + h
-    k0 = (uint32_t)(i * RB + ((h ^ Swz16<D>::f(i)) * 16));
+    k0 = (uint32_t)(i * RB + ((h ^ Swz16K<D>::f(i)) * 16));
     // V^T A operand, d-tile dt, k-step s, half c: this lane addresses row
     // 16 (2 s + c) + 4 h + i/4 at d = 16 dt + 4 (i%4) (8 bytes)
     const int row = 4 * h + (i >> 2), qd = i & 3;
-    v0 = (uint32_t)(row * RB + (((qd >> 1) ^ Swz16<D>::f(row)) * 16) + 8 * (qd & 1));
+    v0 = (uint32_t)(row * RB + (((qd >> 1) ^ Swz16V<D>::f(row)) * 16) + 8 * (qd & 1));
   }
   __device__ __forceinline__ uint32_t kaddr(int kt, int ks) const {
     return (k0 ^ (uint32_t)(64 * ks)) + (uint32_t)(16 * kt * RB);
@@ -1329,12 +1345,49 @@ struct Row16 {
   }
 };
 
-// W waves (= tokens) per workgroup, NS staging slots of one K and one V tile.
-template <int D, int W, int NS>
-__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(4)))
+// Two tokens in one wave (32 rows): every K and V^T fragment read from LDS
+// feeds the MFMA of each of the two tokens' 16-row tiles.
+template <int D>
+__device__ __forceinline__ void qk_pair(uint32_t kb, const Row16<D>& x, const Row16<D>& y,
+                                        f32x4 (&sx)[4], f32x4 (&sy)[4]) {
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    sx[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    sy[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+#pragma unroll
+  for (int ks = 0; ks < Row16<D>::NKS; ++ks)
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const bf16x8 kf = lds_read16(kb + x.kaddr(kt, ks));
+      sx[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, x.q[ks], sx[kt], 0, 0, 0);
+      sy[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, y.q[ks], sy[kt], 0, 0, 0);
+    }
+}
+template <int D>
+__device__ __forceinline__ void pv_pair(uint32_t vb, Row16<D>& x,
+                                        const typename Row16<D>::PFrag& px, Row16<D>& y,
+                                        const typename Row16<D>::PFrag& py) {
+#pragma unroll
+  for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+    for (int dt = 0; dt < Row16<D>::NDT; ++dt) {
+      const bf16x4 lo = lds_read_tr8(vb + x.vaddr(dt, sidx, 0));
+      const bf16x4 hi = lds_read_tr8(vb + x.vaddr(dt, sidx, 1));
+      const bf16x8 av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      x.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, px.f[sidx], x.o[dt], 0, 0, 0);
+      y.o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, py.f[sidx], y.o[dt], 0, 0, 0);
+    }
+}
+
+// W waves of TPW tokens each per workgroup, NS staging slots of one K and
+// one V tile.
+template <int D, int W, int NS, int TPW>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(TPW == 1 ? 4 : 2)))
 void attn16_prefill_kernel(AttnArgs a) {
   constexpr int G = 16, NT = W * 64;
-  constexpr int TT = W;                          // one token per wave
+  constexpr int TT = W * TPW;
+  static_assert(TPW == 1 || TPW == 2, "tokens per wave");
   static_assert(TT <= 32, "token bitmask is 32 bits");
   constexpr int TILE = Swz16<D>::TILE;
   constexpr int SORT_N = TT * kSortCap;
@@ -1357,11 +1410,9 @@ void attn16_prefill_kernel(AttnArgs a) {
   const uint32_t full_mask = n_tok >= 32 ? 0xffffffffu : ((1u << n_tok) - 1u);
   const int p0 = (int)a.n_k - a.n_rows + tok0;   // query position of the tile's first token
 
-  const int my_t = wave;                          // this wave's token
-  const bool row_ok = my_t < n_tok;
-  const int my_row = tok0 + (row_ok ? my_t : 0);
+  // this wave's tokens: TPW consecutive ones
   const int my_head = g * G + (lane & 15);
-  const int my_pos = p0 + (row_ok ? my_t : 0);
+  auto tok_of = [&](int j) { return wave * TPW + j; };
 
   int n_entries;
   if (dense) {
@@ -1419,24 +1470,31 @@ void attn16_prefill_kernel(AttnArgs a) {
   auto kp = [&](const Unit& un) { return kseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
   auto vp = [&](const Unit& un) { return vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
 
-  Row16<D> st;
-  st.init(lane);
-  {
-    const uint16_t* qrow = a.q + ((int64_t)my_row * a.h_q + my_head) * D + 8 * (lane >> 4);
+  Row16<D> st[TPW];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    st[j].init(lane);
+    const bool ok = tok_of(j) < n_tok;
+    const int row = tok0 + (ok ? tok_of(j) : 0);
+    const uint16_t* qrow = a.q + ((int64_t)row * a.h_q + my_head) * D + 8 * (lane >> 4);
 #pragma unroll
     for (int ks = 0; ks < Row16<D>::NKS; ++ks) {
       u32x4 wv = {0u, 0u, 0u, 0u};
-      if (row_ok) wv = ldg16(qrow + 32 * ks);
-      st.q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
+      if (ok) wv = ldg16(qrow + 32 * ks);
+      st[j].q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
 
-  using DT = DmaTile<D, NT, Swz16<D>>;
-  constexpr int KL = DT::kLoads;
+  using DTK = DmaTile<D, NT, Swz16K<D>>;
+  using DTV = DmaTile<D, NT, Swz16V<D>>;
+  constexpr int KL = DTK::kLoads;
+  static_assert(DTV::kLoads == KL, "K and V copies are the same size");
   static_assert(2 * KL * (NS - 1) <= 63, "vmcnt range");
-  DT dma;
-  dma.init(tid);
+  DTK dmak;
+  DTV dmav;
+  dmak.init(tid);
+  dmav.init(tid);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
   // Chunk i sits in slot i % NS: K at lds0 + slot TILE, V at lds0 + (NS + slot) TILE.
@@ -1445,8 +1503,8 @@ void attn16_prefill_kernel(AttnArgs a) {
   // At the barrier the copies issued after chunk i's are those of chunks
   // i+1 .. i+NS-2, the ones that exist.
   auto issue = [&](const Unit& un, int slot) {
-    dma.issue(lds0 + slot * TILE, kp(un), un.nv, tid, wave_u);
-    dma.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, tid, wave_u);
+    dmak.issue(lds0 + slot * TILE, kp(un), un.nv, tid, wave_u);
+    dmav.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, tid, wave_u);
   };
   Unit cur = info(0);
   Unit ahead[NS > 2 ? NS - 2 : 1];       // chunks i+1 .. i+NS-2 (already issued)
@@ -1469,16 +1527,40 @@ void attn16_prefill_kernel(AttnArgs a) {
     }
     const Unit far = info(i + NS - 1);
     if (i + NS - 1 < n) issue(far, (S + NS - 1) % NS);
-    int lim = -1;
-    if (row_ok && ((cur.tm >> my_t) & 1u)) lim = min(my_pos - cur.key0, cur.nv - 1);
-    // lim is the same in all lanes of the wave (one token): a scalar branch
-    lim = __builtin_amdgcn_readfirstlane(lim);
-    if (lim >= 0) {
+    // per token: largest key offset it uses in this chunk, -1 if none (the
+    // same in every lane of the wave: scalar branches)
+    int lim[TPW];
+#pragma unroll
+    for (int j = 0; j < TPW; ++j) {
+      const int t = tok_of(j);
+      int l = -1;
+      if (t < n_tok && ((cur.tm >> t) & 1u)) l = min(p0 + t - cur.key0, cur.nv - 1);
+      lim[j] = __builtin_amdgcn_readfirstlane(l);
+    }
+    const uint32_t kb = lds0 + S * TILE, vb = lds0 + (NS + S) * TILE;
+    auto one = [&](Row16<D>& r, int l) {
       f32x4 sc[4];
-      st.qk(lds0 + S * TILE, sc);
-      if (lim < kChunk - 1) st.mask(sc, lim);
-      const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
-      st.pv(lds0 + (NS + S) * TILE, pf);
+      r.qk(kb, sc);
+      if (l < kChunk - 1) r.mask(sc, l);
+      const typename Row16<D>::PFrag pf = r.softmax(sc, true, a.scale_log2);
+      r.pv(vb, pf);
+    };
+    if constexpr (TPW == 1) {
+      if (lim[0] >= 0) one(st[0], lim[0]);
+    } else {
+      if (lim[0] >= 0 && lim[1] >= 0) {
+        f32x4 sx[4], sy[4];
+        qk_pair<D>(kb, st[0], st[1], sx, sy);
+        if (lim[0] < kChunk - 1) st[0].mask(sx, lim[0]);
+        if (lim[1] < kChunk - 1) st[1].mask(sy, lim[1]);
+        const typename Row16<D>::PFrag px = st[0].softmax(sx, true, a.scale_log2);
+        const typename Row16<D>::PFrag py = st[1].softmax(sy, true, a.scale_log2);
+        pv_pair<D>(vb, st[0], px, st[1], py);
+      } else if (lim[0] >= 0) {
+        one(st[0], lim[0]);
+      } else if (lim[1] >= 0) {
+        one(st[1], lim[1]);
+      }
     }
     if constexpr (NS == 2) {
       cur = far;
@@ -1504,27 +1586,30 @@ void attn16_prefill_kernel(AttnArgs a) {
   }
 
   // row sum over the four lanes of the row, then normalise and store
-  float lt = st.l;
-  {
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    float lt = st[j].l;
     const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(lt), __float_as_uint(lt),
                                                       false, false);
     lt = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
     const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lt), __float_as_uint(lt),
                                                       false, false);
     lt = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-  }
-  if (row_ok) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    const int h = lane >> 4;
-    uint16_t* orow = a.out + ((int64_t)my_row * a.h_q + my_head) * D;
+    if (tok_of(j) < n_tok) {
+      const int row = tok0 + tok_of(j);
+      const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+      const int h = lane >> 4;
+      uint16_t* orow = a.out + ((int64_t)row * a.h_q + my_head) * D;
 #pragma unroll
-    for (int dt = 0; dt < Row16<D>::NDT; ++dt) {
-      u32x2 wv;
-      wv.x = pack_bf16x2(st.o[dt][0] * inv, st.o[dt][1] * inv);
-      wv.y = pack_bf16x2(st.o[dt][2] * inv, st.o[dt][3] * inv);
-      *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * h) = wv;
+      for (int dt = 0; dt < Row16<D>::NDT; ++dt) {
+        u32x2 wv;
+        wv.x = pack_bf16x2(st[j].o[dt][0] * inv, st[j].o[dt][1] * inv);
+        wv.y = pack_bf16x2(st[j].o[dt][2] * inv, st[j].o[dt][3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * h) = wv;
+      }
+      if (a.lse && h == 0)
+        a.lse[(int64_t)row * a.h_q + my_head] = (st[j].m + __log2f(lt)) * kLn2;
     }
-    if (a.lse && h == 0) a.lse[(int64_t)my_row * a.h_q + my_head] = (st.m + __log2f(lt)) * kLn2;
   }
 }
 
@@ -1609,14 +1694,17 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
 
-  using DT = DmaTile<D, 64, Swz16<D>>;
-  constexpr int KL = DT::kLoads;
-  DT dma;
-  dma.init(lane);
+  using DTK = DmaTile<D, 64, Swz16K<D>>;
+  using DTV = DmaTile<D, 64, Swz16V<D>>;
+  constexpr int KL = DTK::kLoads;
+  DTK dmak;
+  DTV dmav;
+  dmak.init(lane);
+  dmav.init(lane);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
   auto issue = [&](const Unit& un, int slot) {
-    dma.issue(lds0 + slot * TILE, kp(un), un.nv, lane, 0);
-    dma.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, lane, 0);
+    dmak.issue(lds0 + slot * TILE, kp(un), un.nv, lane, 0);
+    dmav.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, lane, 0);
   };
   Unit cur = {0, 0}, nxt = {0, 0};
   if (n > 0) { cur = unit(u_begin); issue(cur, 0); }
@@ -1786,14 +1874,19 @@ int launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
 }
 
-// 16-head groups: one token per wave, kRows16Waves tokens per workgroup.
+// 16-head groups: kRows16Tpw tokens per wave, INFLLMV2_ROWS16_WAVES tokens
+// per workgroup.
 #ifndef INFLLMV2_ROWS16_WAVES
 #define INFLLMV2_ROWS16_WAVES 8
 #endif
 #ifndef INFLLMV2_ROWS16_STAGES
 #define INFLLMV2_ROWS16_STAGES 2
 #endif
-constexpr int kRows16Waves = INFLLMV2_ROWS16_WAVES;
+#ifndef INFLLMV2_ROWS16_TPW
+#define INFLLMV2_ROWS16_TPW 1
+#endif
+constexpr int kRows16Tpw = INFLLMV2_ROWS16_TPW;      // tokens per wave
+constexpr int kRows16Waves = INFLLMV2_ROWS16_WAVES / kRows16Tpw;
 constexpr int kRows16Stages = INFLLMV2_ROWS16_STAGES;
 
 // Prefill uses W = min(4, G) waves (TT = 32/G * W <= 32 tokens per tile).
@@ -1804,8 +1897,8 @@ int dispatch_prefill(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
 #endif
   constexpr int PF = INFLLMV2_PREFILL_PF;
   if (G == 16) {
-    hipLaunchKernelGGL((attn16_prefill_kernel<D, kRows16Waves, kRows16Stages>), grid,
-                       dim3(kRows16Waves * 64), 0, st, a);
+    hipLaunchKernelGGL((attn16_prefill_kernel<D, kRows16Waves, kRows16Stages, kRows16Tpw>),
+                       grid, dim3(kRows16Waves * 64), 0, st, a);
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   switch (G) {
@@ -1826,7 +1919,7 @@ int prefill_tile_tokens(int G) {
     case 2: return 32;
     case 4: return 32;
     case 8: return 16;
-    case 16: return kRows16Waves;
+    case 16: return kRows16Waves * kRows16Tpw;
     case 32: return 4;
   }
   return 0;
