@@ -82,8 +82,13 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Exchange a value with the lane 32 positions away (the other half-wave).
+// v_permlane32_swap (VALU, no LDS round trip): with both operands = v it
+// returns r[0] = v of lane (l mod 32) and r[1] = v of lane (l mod 32) + 32,
+// so the partner's value is r[1] in the lower half-wave and r[0] in the upper.
 __device__ __forceinline__ float swap_halves(float v) {
-  return __shfl_xor(v, 32, 64);
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

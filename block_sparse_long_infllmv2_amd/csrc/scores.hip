@@ -74,7 +74,14 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
   const T* qrow = (const T*)a.q + ((int64_t)r * a.h_q + (int64_t)g * G) * D;
   for (int d = threadIdx.x; d < D; d += kScoreThreads) {
     float acc = 0.0f;
-    for (int h = 0; h < G; ++h) acc += Elem<T>::load(qrow + h * D + d);
+    // heads in batches of 8 loads in flight together
+    for (int h0 = 0; h0 < G; h0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = h0 + j < G ? Elem<T>::load(qrow + (h0 + j) * D + d) : 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += x[j];
+    }
     qs[d] = acc * a.scale;
   }
   __syncthreads();
@@ -84,18 +91,29 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] = qs[lane * E + e];
   const T* ckb = (const T*)a.ck + ((int64_t)seq * a.h_kv + g) * a.nc_cap * D + lane * E;
-  for (int64_t m0 = m_lo; m0 <= m_hi; m0 += WPP) {
-    const int64_t m = m0 + sub;
-    float part = 0.0f;
-    if (m <= m_hi) {
-      float x[E];
-      Elem<T>::unpack(ldg16(ckb + m * D), x);
+  // kPasses passes of WPP windows each: all their loads go out before any is
+  // used, so a workgroup waits for memory once per kPasses * WPP windows
+  constexpr int kPasses = 8;
+  for (int64_t mb = m_lo; mb <= m_hi; mb += (int64_t)WPP * kPasses) {
+    u32x4 w[kPasses];
 #pragma unroll
-      for (int e = 0; e < E; ++e) part += qv[e] * x[e];
+    for (int pp = 0; pp < kPasses; ++pp) {
+      const int64_t m = mb + (int64_t)pp * WPP + sub;
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      w[pp] = m <= m_hi ? ldg16(ckb + m * D) : z;
     }
 #pragma unroll
-    for (int o = TPW / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
-    if (lane == 0 && m <= m_hi) sig[m - m_lo] = part;
+    for (int pp = 0; pp < kPasses; ++pp) {
+      const int64_t m = mb + (int64_t)pp * WPP + sub;
+      float x[E];
+      Elem<T>::unpack(w[pp], x);
+      float part = 0.0f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) part += qv[e] * x[e];
+#pragma unroll
+      for (int o = TPW / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);
+      if (lane == 0 && m <= m_hi) sig[m - m_lo] = part;
+    }
   }
   __syncthreads();
 
@@ -158,11 +176,21 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     if (row < a.rows) {
       const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.h_q + (int64_t)g * G) * D + c * 8;
-      for (int h = 0; h < G; ++h) {
-        float x[8];
-        Elem<uint16_t>::unpack(ldg16(qp + (int64_t)h * D), x);
+      // heads in batches of 8 loads issued together (the head count is a
+      // run-time value; a plain loop would wait for each load in turn)
+      for (int h0 = 0; h0 < G; h0 += 8) {
+        u32x4 w[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[e];
+        for (int j = 0; j < 8; ++j)
+          if (h0 + j < G) w[j] = ldg16(qp + (int64_t)(h0 + j) * D);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (h0 + j < G) {
+            float x[8];
+            Elem<uint16_t>::unpack(w[j], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += x[e];
+          }
       }
     }
     u32x4 hi, lo;
@@ -382,7 +410,7 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   // blocks per workgroup: as many as keep the chunk's windows within the LDS
   // buffer (a chunk of n blocks spans at most (n*B + ks - 2)/s + 2 windows)
   int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * r.s - r.ks + 2) / r.B);
-  if (bpw > 64) bpw = 64;
+  if (bpw > 32) bpw = 32;
   if (bpw < 1) return INFLLMV2_ERR_UNSUPPORTED;
   a.blocks_per_wg = bpw;
   const int64_t nb_launch = (int64_t)max_pos / r.B + 1;
