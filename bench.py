@@ -8,7 +8,8 @@ top-64, dense_len 8192) -- the long-context prefill the pages quote 128K
 throughput for.  One step = compress the windows this chunk completes ->
 block scores -> top-k -> sparse attention, i.e. every stage of the path.
 Other workloads (for reports): 1 = 32K decode, 3 = 128K tree verification
-with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode.
+with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
+6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence).
 
 Prints one JSON line: tokens/s over K timed steps, per-stage times from HIP
 events recorded on the library's stream, the dominant kernel's roofline
@@ -75,9 +76,18 @@ class Workload:
         self.wid = wid
         dev = torch.device("cuda:0")
         self.dev = dev
+        # batched decode at 128K: `rep` copies of one 131072-token sequence, each
+        # in its own HBM (same values, separate addresses, so every sequence's
+        # K/V is really read); shows the decode kernel where HBM bandwidth,
+        # not launch latency, is the limit
+        self.rep = 1
         if wid == 5:
             self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
             self.name = "decode_bf16_128k"
+        elif wid == 6:
+            self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
+            self.rep = 32
+            self.name = "decode_bf16_128k_batch32"
         else:
             self.case = config(wid, seed=seed)
             self.name = CONFIG_NAMES[wid]
@@ -97,17 +107,18 @@ class Workload:
             torch.cuda.synchronize()
             self.tokens = c.n_q
             self.kind = "prefill"
-        elif wid in (1, 4, 5):
-            lens = np.asarray(c.seqlens)
+        elif wid in (1, 4, 5, 6):
+            lens = np.tile(np.asarray(c.seqlens), self.rep)
             bsz = len(lens)
+            n0 = len(c.seqlens)
             h_kv, _, d = c.k[0].shape
             cap = int(((lens.max() + 63) // 64) * 64)
             self.k = torch.zeros((bsz, h_kv, cap, d), dtype=bf, device=dev)
             self.v = torch.zeros_like(self.k)
             for i, L in enumerate(lens):
-                self.k[i, :, :L] = up(c.k[i])
-                self.v[i, :, :L] = up(c.v[i])
-            self.q = up(c.q)
+                self.k[i, :, :L] = up(c.k[i % n0])
+                self.v[i, :, :L] = up(c.v[i % n0])
+            self.q = up(np.tile(c.q, (self.rep, 1, 1)))
             self.seqlens = torch.from_numpy(lens.astype(np.int32)).to(dev)
             nc = _n_windows(cap, p.kernel_size, p.kernel_stride)
             self.ck = torch.zeros((bsz, h_kv, nc, d), dtype=bf, device=dev)
@@ -184,26 +195,25 @@ class Workload:
         d = c.q.shape[2]
         h_q = c.q.shape[1]
         if self.kind == "decode":
+            # the attention call's own bytes: K and V of the kept keys, Q and O
+            # (the compressed keys are read by the scoring stage, not here)
             total = 0.0
-            for L in c.seqlens:
+            for L in np.tile(np.asarray(c.seqlens), self.rep):
                 L = int(L)
                 h_kv = c.k[0].shape[0]
                 if L < p.dense_len:
                     kv = h_kv * L * d * 2 * 2
-                    ckb = 0
                 else:
                     kv = h_kv * _visible_selected_keys(L - 1, p, p.topk) * d * 2 * 2
-                    ckb = h_kv * _n_windows(L, p.kernel_size, p.kernel_stride) * d * 2
-                total += kv + ckb + h_q * d * 2 * 2
+                total += kv + h_q * d * 2 * 2
             return {"dominant": "sparse_attn_decode", "bound": "hbm", "bytes": total,
                     "src": "attn_bf16.hip"}
-        # tree: CK once + union of kept blocks per KV head + drafts + Q/O
+        # tree: union of kept blocks per KV head + drafts + Q/O + masks
         h_kv, n_ctx, _ = c.k.shape
         sel = self.plan.block_idx.cpu().numpy()
         union = sum(len(np.unique(sel[:, g][sel[:, g] >= 0])) for g in range(h_kv))
         T = c.q.shape[0]
-        total = (h_kv * _n_windows(n_ctx, p.kernel_size, p.kernel_stride) * d * 2 +
-                 union * p.block_size * d * 2 * 2 + T * h_q * d * 2 * 2 +
+        total = (union * p.block_size * d * 2 * 2 + T * h_q * d * 2 * 2 +
                  2 * h_kv * T * d * 2 + T * 8)
         return {"dominant": "tree_verify", "bound": "hbm", "bytes": float(total),
                 "union_blocks": int(union), "src": "attn_bf16.hip"}
