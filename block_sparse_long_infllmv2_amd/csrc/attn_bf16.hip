@@ -1811,6 +1811,44 @@ __global__ __launch_bounds__(kPlanThreads) void tree_union_kernel(
   if (threadIdx.x == 0) ulen[g] = total < union_cap ? total : union_cap;
 }
 
+// Same result for contexts of at most kUnionBitmapBlocks blocks, without a
+// sort: every draft ORs its bit into a per-block 64-bit mask in LDS, then one
+// scan over the blocks compacts the non-zero ones in ascending order.
+constexpr int kUnionBitmapBlocks = 8192;      // 64 KB of masks
+__global__ __launch_bounds__(kPlanThreads) void tree_union_bitmap_kernel(
+    const int32_t* block_idx, int n_draft, int h_kv, int topk, int n_b, int32_t* ublk,
+    uint64_t* umask, int32_t* ulen, int union_cap) {
+  __shared__ uint64_t mask[kUnionBitmapBlocks];
+  __shared__ int scan_lds[kPlanThreads / 64];
+  const int g = blockIdx.x;
+  for (int b = threadIdx.x; b < n_b; b += kPlanThreads) mask[b] = 0ull;
+  __syncthreads();
+  for (int i = threadIdx.x; i < n_draft * topk; i += kPlanThreads) {
+    const int t = i / topk, j = i % topk;
+    const int32_t b = block_idx[((int64_t)t * h_kv + g) * topk + j];
+    if (b >= 0 && b < n_b) atomicOr((unsigned long long*)&mask[b], 1ull << t);
+  }
+  __syncthreads();
+  // thread k owns blocks [k*C, (k+1)*C): count, scan, write in order
+  const int C = (n_b + kPlanThreads - 1) / kPlanThreads;
+  const int b0 = threadIdx.x * C, b1 = min(n_b, b0 + C);
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) cnt += mask[b] != 0ull;
+  int total;
+  int slot = block_excl_scan<kPlanThreads>(cnt, &total, scan_lds);
+  for (int b = b0; b < b1; ++b) {
+    const uint64_t m = mask[b];
+    if (m != 0ull) {
+      if (slot < union_cap) {
+        ublk[(int64_t)g * union_cap + slot] = b;
+        umask[(int64_t)g * union_cap + slot] = m;
+      }
+      ++slot;
+    }
+  }
+  if (threadIdx.x == 0) ulen[g] = total < union_cap ? total : union_cap;
+}
+
 // ---------------------------------------------------------------------------
 // Merge of split partials: out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 // ---------------------------------------------------------------------------
@@ -2165,9 +2203,15 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
   const int TT = tree_tile_tokens(G);
   if (!dense) {
-    hipLaunchKernelGGL(tree_union_kernel, dim3(h_kv), dim3(kPlanThreads), 0, st, block_idx,
-                       n_draft, h_kv, r.topk, ceil_div(n_ctx, r.B), (int32_t*)a.union_blk,
-                       (uint64_t*)a.union_mask, (int32_t*)a.union_len, a.union_cap);
+    const int64_t n_b = ceil_div(n_ctx, r.B);
+    if (n_b <= kUnionBitmapBlocks)
+      hipLaunchKernelGGL(tree_union_bitmap_kernel, dim3(h_kv), dim3(kPlanThreads), 0, st,
+                         block_idx, n_draft, h_kv, r.topk, (int)n_b, (int32_t*)a.union_blk,
+                         (uint64_t*)a.union_mask, (int32_t*)a.union_len, a.union_cap);
+    else
+      hipLaunchKernelGGL(tree_union_kernel, dim3(h_kv), dim3(kPlanThreads), 0, st, block_idx,
+                         n_draft, h_kv, r.topk, n_b, (int32_t*)a.union_blk,
+                         (uint64_t*)a.union_mask, (int32_t*)a.union_len, a.union_cap);
     if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
   }
   dim3 grid((unsigned)n_split, h_kv, (unsigned)ceil_div(n_draft, TT));
