@@ -1856,33 +1856,49 @@ template <int D, typename TOut>
 __global__ __launch_bounds__(64) void combine_kernel(const float* ws, int n_split, TOut* out,
                                                      float* lse) {
   constexpr int kMaxSplit = 64;
-  __shared__ float wsh[kMaxSplit];
+  constexpr int kBatch = 16;                 // splits whose o values are loaded together
   const int rh = blockIdx.x;   // row * h_q + head
   const int lane = threadIdx.x;
   const float* base = ws + (int64_t)rh * n_split * (D + 2);
-  // lane s holds split s (n_split <= 64): max, weights and normaliser in
-  // parallel over the splits
+  // lane s holds split s (n_split <= 64) for the weights; every lane holds
+  // d = lane + 64 i of each split for the sums.  The o loads of a batch of
+  // splits are issued together with the (m, l) loads, so the merge waits for
+  // memory about once per kBatch splits instead of once per split.
   float m = kNoMax, l = 0.0f;
   if (lane < n_split) {
     l = base[lane * (D + 2) + D + 1];
-    m = l > 0.0f ? base[lane * (D + 2) + D] : kNoMax;
+    m = base[lane * (D + 2) + D];
   }
-  const float M = wave_max(m);
-  const float w = l > 0.0f ? fast_exp2(m - M) : 0.0f;
-  const float L = wave_sum(w * l);
-  if (lane < kMaxSplit) wsh[lane] = w;
-  __syncthreads();
   float acc[D / 64];
 #pragma unroll
   for (int i = 0; i < D / 64; ++i) acc[i] = 0.0f;
-  // no branch in the loop, so the loads of all splits can be in flight
-  // together (empty splits have weight 0 and finite partials)
-#pragma unroll 4
-  for (int s = 0; s < n_split; ++s) {
-    const float ww = wsh[s];
-    const float* p = base + s * (D + 2);
+  float ov[kBatch][D / 64];
+  const int nb0 = n_split < kBatch ? n_split : kBatch;
 #pragma unroll
-    for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(ww, p[lane + 64 * i], acc[i]);
+  for (int s2 = 0; s2 < kBatch; ++s2)
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i)
+      ov[s2][i] = s2 < nb0 ? base[s2 * (D + 2) + lane + 64 * i] : 0.0f;
+  m = l > 0.0f ? m : kNoMax;
+  const float M = wave_max(m);
+  const float w = l > 0.0f ? fast_exp2(m - M) : 0.0f;
+  const float L = wave_sum(w * l);
+  for (int sb = 0; sb < n_split; sb += kBatch) {
+    if (sb > 0) {
+#pragma unroll
+      for (int s2 = 0; s2 < kBatch; ++s2)
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i)
+          ov[s2][i] = sb + s2 < n_split ? base[(sb + s2) * (D + 2) + lane + 64 * i] : 0.0f;
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < kBatch; ++s2) {
+      const int sp = sb + s2 < kMaxSplit ? sb + s2 : kMaxSplit - 1;
+      // weight of split sp (0 for splits past n_split: lanes >= n_split hold w = 0)
+      const float ww = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp));
+#pragma unroll
+      for (int i = 0; i < D / 64; ++i) acc[i] = __builtin_fmaf(ww, ov[s2][i], acc[i]);
+    }
   }
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
 #pragma unroll
