@@ -169,6 +169,7 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(TopkArgs a) {
 // ---------------------------------------------------------------------------
 // Keys a wave keeps in LDS for the threshold search after the lower-bound filter.
 constexpr int kSurvivors = 256;
+constexpr int kMaxTopk = 128;          // the host rejects larger topk
 
 // k-th largest (1 <= k <= 64) of one value per lane: bitonic sort across the
 // wave (ascending), then the value at lane 64 - k.
@@ -225,7 +226,10 @@ __device__ __forceinline__ uint32_t threshold_search(const uint32_t (&key)[N], i
 
 template <int KPL>
 __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n_units) {
-  __shared__ uint32_t surv[4][kSurvivors];
+  // per wave: survivors (+ one dummy slot per lane) and the ordered selection
+  // (+ one dummy slot per lane), so that no lane needs a branch to write
+  __shared__ uint32_t surv[4][kSurvivors + 64];
+  __shared__ int32_t sel_lds[4][kMaxTopk + 64];
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= n_units) return;                   // whole wave leaves
   const int lane = threadIdx.x & 63;
@@ -254,17 +258,18 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   const int need = a.topk - n_forced;
   const float* S = a.scores + ((int64_t)r * a.h_kv + g) * a.nb_cap;
 
-  // 0 = not a candidate (forced or past the eligible range); candidates >= 1
+  // 0 = not a candidate (forced or past the eligible range); candidates >= 1.
+  // Every lane loads (an in-range index), then selects: no divergent branch.
+  // forced blocks are bit j of a per-lane mask (one VGPR, not a lane mask per j)
   uint32_t key[KPL];
+  uint32_t forced_bits = 0u;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane + 64 * j;
-    uint32_t k = 0;
-    if (b < n_elig && b >= f_init && b < f_lo) {
-      k = orderable_key(S[b]);
-      k = k == 0 ? 1u : k;
-    }
-    key[j] = k;
+    const float x = S[b < n_elig ? b : n_elig - 1];
+    const uint32_t k = orderable_key(x);
+    key[j] = (b < n_elig && b >= f_init && b < f_lo) ? (k == 0 ? 1u : k) : 0u;
+    forced_bits |= (b < n_elig && (b < f_init || b >= f_lo)) ? (1u << j) : 0u;
   }
   // T = largest value with #(key >= T) >= need (the need-th largest key)
   uint32_t T = 0;
@@ -292,8 +297,11 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
       __builtin_amdgcn_wave_barrier();
       int o = off;
 #pragma unroll
-      for (int j = 0; j < KPL; ++j)
-        if (key[j] >= lo && key[j] != 0u) sv[o++] = key[j];
+      for (int j = 0; j < KPL; ++j) {
+        const bool keep = key[j] >= lo && key[j] != 0u;
+        sv[keep ? o : kSurvivors + lane] = key[j];
+        o += keep ? 1 : 0;
+      }
       __builtin_amdgcn_wave_barrier();
       uint32_t sk[kSurvivors / 64];
 #pragma unroll
@@ -312,10 +320,11 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
     take = need - gt;
   }
   int base = 0, eq_seen = 0;
+  const int wv = threadIdx.x >> 6;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane + 64 * j;
-    const bool forced = b < n_elig && (b < f_init || b >= f_lo);
+    const bool forced = (forced_bits >> j) & 1u;
     bool sel;
     if (need <= 0) {
       sel = forced;
@@ -328,13 +337,12 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
       sel = forced || key[j] > T || (key[j] == T && rank < take);
     }
     const uint64_t selm = __ballot(sel);
-    if (sel) {
-      const int slot = base + __popcll(selm & below);
-      if (slot < a.topk) out[slot] = b;
-    }
+    const int slot = base + __popcll(selm & below);
+    sel_lds[wv][(sel && slot < a.topk) ? slot : kMaxTopk + lane] = b;
     base += __popcll(selm);
   }
-  for (int i = base + lane; i < a.topk; i += 64) out[i] = -1;
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < a.topk; i += 64) out[i] = i < base ? sel_lds[wv][i] : -1;
 }
 
 }  // namespace infllmv2
