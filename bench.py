@@ -11,9 +11,12 @@ Other workloads (for reports): 1 = 32K decode, 3 = 128K tree verification
 with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
 6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence).
 
-Prints one JSON line: tokens/s over K timed steps, per-stage times from HIP
-events recorded on the library's stream, the dominant kernel's roofline
-fraction, and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
+HIP graph and replayed once; --eager times individual launches), per-stage
+times from HIP events recorded between the library calls of eager steps, the
+dominant call's roofline fraction (its time = HIP-event time of the K-step
+graph minus that of the same K steps without the call, events on the graph's
+stream), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -146,8 +149,9 @@ class Workload:
         else:
             raise SystemExit(f"workload {wid} is a parity case, not a bench workload")
 
-    # one step, with optional per-stage event recording
-    def step(self, ev=None):
+    # one step, with optional per-stage event recording; skip_dominant leaves
+    # out the attention call (to time that call inside real steps by difference)
+    def step(self, ev=None, skip_dominant=False):
         def mark(name):
             if ev is not None:
                 e = self.torch.cuda.Event(enable_timing=True)
@@ -162,20 +166,33 @@ class Workload:
             mark("block_scores")
             pl.topk()
             mark("select_topk")
-            pl.attend(self.q, self.k, self.v)
+            if not skip_dominant:
+                pl.attend(self.q, self.k, self.v)
             mark("sparse_attn_prefill")
         elif self.kind == "decode":
             mark("start")
             pl.select(self.q, self.ck, self.seqlens)
             mark("scores_topk")
-            pl.attend(self.q, self.k, self.v, self.seqlens)
+            if not skip_dominant:
+                pl.attend(self.q, self.k, self.v, self.seqlens)
             mark("sparse_attn_decode")
         else:
             mark("start")
             pl.select(self.q, self.ck)
             mark("scores_topk")
-            pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
+            if not skip_dominant:
+                pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
             mark("tree_verify")
+
+    # the dominant call alone (the attention call of the step)
+    def dominant_call(self):
+        pl = self.plan
+        if self.kind == "prefill":
+            pl.attend(self.q, self.k, self.v)
+        elif self.kind == "decode":
+            pl.attend(self.q, self.k, self.v, self.seqlens)
+        else:
+            pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
 
     # ---- algorithmic work (what the method must touch / compute) ----------
     def work(self):
@@ -266,6 +283,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--eager", action="store_true",
+                    help="time steps as individual launches instead of HIP graph replays")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -293,6 +312,7 @@ def main():
         wl.step()
     torch.cuda.synchronize()
 
+    # per-stage times: eager steps with HIP events between the library calls
     evs = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -301,20 +321,54 @@ def main():
         wl.step(ev)
         evs.append(ev)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    print(f"[bench] {args.steps} steps in {wall:.4f} s", file=sys.stderr, flush=True)
-
+    wall_eager = time.perf_counter() - t0
     stages = {}
     for ev in evs:
         for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:]):
             stages.setdefault(n1, []).append(e0.elapsed_time(e1))
     stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
-    ms_per_step = wall * 1e3 / args.steps
-    value = wl.tokens / (ms_per_step / 1e3)
 
     w = wl.work()
     dom = w["dominant"]
-    dom_ms = stage_ms[dom]
+    if args.eager:
+        wall = wall_eager
+        dom_ms = stage_ms[dom]
+        mode = "eager"
+    else:
+        # The K timed steps as one HIP graph (the library only launches kernels
+        # on the caller's stream and allocates nothing, so steps capture whole):
+        # the GPU runs them back to back with no host launch gaps, which
+        # otherwise dominate the small decode steps.  One untimed replay first.
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(args.steps):
+                wl.step()
+        # the same K steps without the dominant call: the difference is that
+        # call's cost inside real steps (same neighbours, same cache state)
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for _ in range(args.steps):
+                wl.step(skip_dominant=True)
+        g.replay()
+        gr.replay()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        g.replay()
+        ev[1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev[2].record()
+        gr.replay()
+        ev[3].record()
+        torch.cuda.synchronize()
+        dom_ms = (ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) / args.steps
+        mode = "hip_graph"
+    print(f"[bench] {args.steps} steps in {wall:.4f} s ({mode}); eager {wall_eager:.4f} s",
+          file=sys.stderr, flush=True)
+    ms_per_step = wall * 1e3 / args.steps
+    value = wl.tokens / (ms_per_step / 1e3)
     src = os.path.join(ROOT, "block_sparse_long_infllmv2_amd", "csrc", w["src"])
     if w["bound"] == "mfma":
         achieved = w["flop"] / (dom_ms * 1e-3) / 1e12
@@ -348,8 +402,9 @@ def main():
     out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic", "config": cfg, "roofline": roof,
-           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()}}
+           "data": "synthetic", "config": cfg, "roofline": roof, "launch": mode,
+           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+           "eager_ms_per_step": round(wall_eager * 1e3 / args.steps, 4)}
     if w["bound"] == "mfma":
         out["scoring_gflop"] = round(w["score_flop"] / 1e9, 2)
     if not args.no_cpu_baseline:

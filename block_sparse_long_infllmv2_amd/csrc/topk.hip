@@ -170,6 +170,8 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(TopkArgs a) {
 // Keys a wave keeps in LDS for the threshold search after the lower-bound filter.
 constexpr int kSurvivors = 256;
 constexpr int kMaxTopk = 128;          // the host rejects larger topk
+// up to this many (row, KV head) units a workgroup per row beats a wave per row
+constexpr int kFewRows = 512;
 
 // k-th largest (1 <= k <= 64) of one value per lane: bitonic sort across the
 // wave (ascending), then the value at lane 64 - k.
@@ -260,16 +262,17 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
 
   // 0 = not a candidate (forced or past the eligible range); candidates >= 1.
   // Every lane loads (an in-range index), then selects: no divergent branch.
-  // forced blocks are bit j of a per-lane mask (one VGPR, not a lane mask per j)
+  // forced blocks are bit j of a per-lane mask (VGPRs, not a lane mask per j)
+  static_assert(KPL <= 64, "forced-block mask holds 64 bits");
   uint32_t key[KPL];
-  uint32_t forced_bits = 0u;
+  uint64_t forced_bits = 0ull;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane + 64 * j;
     const float x = S[b < n_elig ? b : n_elig - 1];
     const uint32_t k = orderable_key(x);
     key[j] = (b < n_elig && b >= f_init && b < f_lo) ? (k == 0 ? 1u : k) : 0u;
-    forced_bits |= (b < n_elig && (b < f_init || b >= f_lo)) ? (1u << j) : 0u;
+    forced_bits |= (b < n_elig && (b < f_init || b >= f_lo)) ? (1ull << j) : 0ull;
   }
   // T = largest value with #(key >= T) >= need (the need-th largest key)
   uint32_t T = 0;
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
     const int b = lane + 64 * j;
-    const bool forced = (forced_bits >> j) & 1u;
+    const bool forced = (forced_bits >> j) & 1ull;
     bool sel;
     if (need <= 0) {
       sel = forced;
@@ -343,6 +346,162 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   }
   __builtin_amdgcn_wave_barrier();
   for (int i = lane; i < a.topk; i += 64) out[i] = i < base ? sel_lds[wv][i] : -1;
+}
+
+// ---------------------------------------------------------------------------
+// Few rows (decode, tree verification): one 256-thread workgroup per (row,
+// KV head), so a row's work is spread over four waves instead of one.
+// Thread t owns the KPT consecutive blocks [KPT t, KPT t + KPT) (coalesced
+// loads; ascending block order = thread order, so ties and the output order
+// come from block prefix scans).
+//   lower bound: each wave's need-th largest lane maximum is a lower bound of
+//     the threshold (that wave alone holds `need` keys at or above it), so is
+//     their maximum;
+//   keys at or above it (<= kSurvivors) go to LDS and wave 0 runs the bitwise
+//     threshold search on them; a full block-wide search is the fallback.
+// ---------------------------------------------------------------------------
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArgs a) {
+  __shared__ uint32_t surv[kSurvivors];
+  __shared__ int scan4[kTopkThreads / 64];
+  __shared__ uint32_t wave_lo[kTopkThreads / 64];
+  __shared__ uint32_t sh_T;
+  __shared__ int sh_exact;
+  const int r = blockIdx.x / a.h_kv, g = blockIdx.x % a.h_kv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int32_t* out = a.block_idx + ((int64_t)r * a.h_kv + g) * a.topk;
+  const int seq = a.row_seq ? a.row_seq[r] : 0;
+  bool skip = seq < 0 || seq >= a.batch;
+  const int64_t L = skip ? 0 : a.seqlens[seq];
+  const int64_t pos = a.row_pos ? a.row_pos[r] : L - 1;
+  skip = skip || L < a.dense_len || pos < 0 || pos >= L || pos / a.B + 1 > a.nb_cap;
+  if (skip) {
+    for (int i = tid; i < a.topk; i += kTopkThreads) out[i] = -1;
+    return;
+  }
+  const int b_own = (int)(pos / a.B);
+  const int n_elig = b_own + 1;
+  if (n_elig <= a.topk) {
+    for (int i = tid; i < a.topk; i += kTopkThreads) out[i] = i < n_elig ? i : -1;
+    return;
+  }
+  const int f_init = a.init < n_elig ? a.init : n_elig;
+  const int f_lo = b_own - a.local + 1 > 0 ? b_own - a.local + 1 : 0;
+  const int overlap = f_init > f_lo ? f_init - f_lo : 0;
+  const int n_forced = f_init + (n_elig - f_lo) - overlap;
+  const int need = a.topk - n_forced;
+  const float* S = a.scores + ((int64_t)r * a.h_kv + g) * a.nb_cap;
+
+  uint32_t key[KPT];
+  uint32_t forced_bits = 0u, mx = 0u;
+  const int b0 = KPT * tid;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int b = b0 + j;
+    const float x = S[b < n_elig ? b : n_elig - 1];
+    const uint32_t k = orderable_key(x);
+    key[j] = (b < n_elig && b >= f_init && b < f_lo) ? (k == 0 ? 1u : k) : 0u;
+    forced_bits |= (b < n_elig && (b < f_init || b >= f_lo)) ? (1u << j) : 0u;
+    mx = key[j] > mx ? key[j] : mx;
+  }
+
+  uint32_t T = 0u;
+  bool exact = need <= 0;
+  if (need > 0) {
+    uint32_t lo = 0u;
+    if (need <= 64) {
+      const uint32_t wl = wave_kth_largest(mx, need, lane);
+      if (lane == 0) wave_lo[wv] = wl;
+      __syncthreads();
+#pragma unroll
+      for (int w = 0; w < kTopkThreads / 64; ++w) lo = wave_lo[w] > lo ? wave_lo[w] : lo;
+    }
+    int mine = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) mine += key[j] >= lo && key[j] != 0u;
+    int total;
+    const int off = block_exclusive_scan(mine, &total, scan4);
+    if (lo != 0u && total <= kSurvivors) {
+      for (int i = tid; i < kSurvivors; i += kTopkThreads) surv[i] = 0u;
+      __syncthreads();
+      int o = off;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (key[j] >= lo && key[j] != 0u) surv[o++] = key[j];
+      __syncthreads();
+      if (wv == 0) {
+        uint32_t sk[kSurvivors / 64];
+#pragma unroll
+        for (int j = 0; j < kSurvivors / 64; ++j) sk[j] = surv[lane + 64 * j];
+        bool ex = false;
+        const uint32_t t = threshold_search<kSurvivors / 64>(sk, need, lo, &ex);
+        if (lane == 0) { sh_T = t; sh_exact = ex ? 1 : 0; }
+      }
+    } else {
+      // block-wide bitwise search over all keys
+      if (tid == 0) { sh_T = 0u; sh_exact = 0; }
+      __syncthreads();
+      uint32_t t = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = t | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) c += key[j] >= cand;
+        int cnt;
+        (void)block_exclusive_scan(c, &cnt, scan4);
+        if (cnt >= need) {
+          t = cand;
+          if (cnt == need) { if (tid == 0) sh_exact = 1; break; }
+        }
+      }
+      if (tid == 0) sh_T = t;
+    }
+    __syncthreads();
+    T = sh_T;
+    exact = sh_exact != 0;
+  }
+  // selection: forced, keys > T, and of the keys == T the lowest-indexed
+  // `take` ones (rank from a block scan of the per-thread tie counts)
+  int take = 0;
+  int eq_before = 0;
+  if (!exact) {
+    int gt = 0, eq = 0;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      gt += key[j] > T;
+      eq += key[j] == T;
+    }
+    int gt_tot, eq_tot;
+    (void)block_exclusive_scan(gt, &gt_tot, scan4);
+    eq_before = block_exclusive_scan(eq, &eq_tot, scan4);
+    take = need - gt_tot;
+  }
+  uint32_t sel_bits = 0u;
+  int rank = eq_before;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const bool forced = (forced_bits >> j) & 1u;
+    bool sel;
+    if (need <= 0) {
+      sel = forced;
+    } else if (exact) {
+      sel = forced || key[j] >= T;
+    } else {
+      const bool tie = key[j] == T;
+      sel = forced || key[j] > T || (tie && rank < take);
+      rank += tie ? 1 : 0;
+    }
+    sel_bits |= sel ? (1u << j) : 0u;
+  }
+  int n_sel;
+  int slot = block_exclusive_scan(__popc(sel_bits), &n_sel, scan4);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j)
+    if ((sel_bits >> j) & 1u) {
+      if (slot < a.topk) out[slot] = b0 + j;
+      ++slot;
+    }
+  for (int i = n_sel + tid; i < a.topk; i += kTopkThreads) out[i] = -1;
 }
 
 }  // namespace infllmv2
@@ -366,6 +525,16 @@ extern "C" int infllmv2_select_topk(const float* scores, int32_t rows,
   a.init = r.init; a.local = r.local; a.dense_len = r.dense_len; a.batch = batch;
   const int n_units = rows * h_kv;
   hipStream_t st = (hipStream_t)stream;
+  // few rows: a workgroup per row (KPT consecutive blocks per thread)
+  if (n_units <= kFewRows && nb_cap <= (int64_t)kTopkThreads * 16) {
+    if (nb_cap <= kTopkThreads * 8)
+      hipLaunchKernelGGL(select_topk_block_kernel<8>, dim3((unsigned)n_units),
+                         dim3(kTopkThreads), 0, st, a);
+    else
+      hipLaunchKernelGGL(select_topk_block_kernel<16>, dim3((unsigned)n_units),
+                         dim3(kTopkThreads), 0, st, a);
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   // eligible blocks per row <= nb_cap: registers hold 64 * KPL keys per wave
   if (nb_cap <= 64 * 32)
     hipLaunchKernelGGL(select_topk_wave_kernel<32>, dim3((unsigned)((n_units + 3) / 4)),

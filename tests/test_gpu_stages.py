@@ -123,18 +123,18 @@ def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv, rows):
 
 
 # ----------------------------------------------------------------- topk ----
-def test_select_topk_matches_oracle_exactly(B):
-    _say("topk exact")
+@pytest.mark.parametrize("rows", [24, 300])   # few rows: workgroup per row; many: wave per row
+def test_select_topk_matches_oracle_exactly(B, rows):
+    _say(f"topk exact rows={rows}")
     rng = np.random.default_rng(4)
     cases = []
     for topk, init, local, nb, ties in [(8, 1, 2, 40, True), (64, 1, 2, 2048, False),
                                         (64, 1, 2, 2048, True), (6, 0, 0, 30, True),
                                         (16, 2, 3, 700, False), (64, 1, 2, 65, False),
-                                        (64, 1, 2, 10000, False)]:
+                                        (64, 1, 2, 3000, True), (64, 1, 2, 10000, False)]:
         cases.append((Params(topk=topk, init_blocks=init, local_blocks=local, dense_len=0),
                       nb, ties))
     for p, nb, ties in cases:
-        rows = 24
         n_k = nb * 64
         pos = rng.integers(0, n_k, rows).astype(np.int32)
         pos[0] = n_k - 1
@@ -142,6 +142,7 @@ def test_select_topk_matches_oracle_exactly(B):
         S = rng.standard_normal((rows, 2, nb)).astype(np.float32)
         if ties:
             S = np.round(S * 2).astype(np.float32)
+            S[2] = 1.0                      # a row of equal scores
         S[rng.random(S.shape) < 0.05] = -np.inf
         s_t = torch.from_numpy(S).cuda()
         idx = torch.full((rows, 2, p.topk), -7, dtype=torch.int32, device="cuda")
