@@ -15,8 +15,8 @@ Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
 HIP graph and replayed once; --eager times individual launches), per-stage
 times from HIP events recorded between the library calls of eager steps, the
 dominant call's roofline fraction (its time = HIP-event time of the K-step
-graph minus that of the same K steps without the call, events on the graph's
-stream), and the CPU oracle timed on a bounded sample of the same workload.
+graph minus that of the same K steps without the call, median of 5 such pairs,
+events on the graph's stream), and the CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -275,6 +275,17 @@ def cpu_baseline(wl, budget_s=20.0):
                 "sample": f"{n} of {T} drafts, float64 numpy, 1 thread"}
 
 
+def _keep_busy(fn, seconds, torch):
+    """Call fn (one step or one graph replay) at least once and until
+    `seconds` of wall time have passed; synchronises at the end."""
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            break
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -285,6 +296,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--eager", action="store_true",
                     help="time steps as individual launches instead of HIP graph replays")
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="untimed work after the warm-up steps and after graph capture, "
+                         "so that timing starts at steady clocks")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -311,6 +325,10 @@ def main():
     for _ in range(args.warmup):
         wl.step()
     torch.cuda.synchronize()
+    # The clocks ramp up under sustained load and fall back while the GPU idles
+    # (a kernel's duration drifts down by ~20% over the first ~100 ms of work):
+    # keep stepping, untimed, for at least --warm-seconds before any timing.
+    _keep_busy(wl.step, args.warm_seconds, torch)
 
     # per-stage times: eager steps with HIP events between the library calls
     evs = []
@@ -349,9 +367,11 @@ def main():
         with torch.cuda.graph(gr):
             for _ in range(args.steps):
                 wl.step(skip_dominant=True)
-        g.replay()
+        # capturing left the GPU idle: untimed replays until it is warm again
+        _keep_busy(g.replay, args.warm_seconds, torch)
         gr.replay()
         torch.cuda.synchronize()
+        # the timed K steps: one replay, wall clock and events
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         t0 = time.perf_counter()
         ev[0].record()
@@ -359,11 +379,19 @@ def main():
         ev[1].record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ev[2].record()
-        gr.replay()
-        ev[3].record()
-        torch.cuda.synchronize()
-        dom_ms = (ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3])) / args.steps
+        # dominant call: median over 5 (full, without-the-call) replay pairs
+        diffs = []
+        for i in range(5):
+            if i:
+                ev[0].record()
+                g.replay()
+                ev[1].record()
+            ev[2].record()
+            gr.replay()
+            ev[3].record()
+            torch.cuda.synchronize()
+            diffs.append(ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3]))
+        dom_ms = float(np.median(diffs)) / args.steps
         mode = "hip_graph"
     print(f"[bench] {args.steps} steps in {wall:.4f} s ({mode}); eager {wall_eager:.4f} s",
           file=sys.stderr, flush=True)
@@ -390,7 +418,8 @@ def main():
     if wl.kind == "prefill":
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": int(c.n_q)})
     elif wl.kind == "decode":
-        cfg.update({"batch": int(len(c.seqlens)), "seqlens": [int(x) for x in c.seqlens]})
+        lens = [int(x) for x in np.tile(np.asarray(c.seqlens), wl.rep)]
+        cfg.update({"batch": len(lens), "seqlens": lens})
     else:
         cfg.update({"context": int(c.k.shape[1]), "drafts": int(c.q.shape[0])})
     cfg.update({"h_q": int(c.q.shape[1]), "h_kv": 2, "head_dim": int(c.q.shape[2]),
