@@ -136,9 +136,10 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 //
 // sigma^T = CK . qsum^T on v_mfma_f32_32x32x16_bf16: the A operand is 32
 // windows x 16 dims of compressed keys, the B operand 16 dims x 32 rows of
-// the group-summed query.  qsum (float32) is split into hi + lo bfloat16
-// parts and both are multiplied, which keeps ~16 significant bits of the
-// query sum so the scores match a float32 dot product to ~1e-5 relative.
+// the group-summed query times the softmax scale.  That float32 sum is split
+// into hi + lo bfloat16 parts and both are multiplied, which keeps ~16
+// significant bits so the scores match a float32 dot product to ~1e-5
+// relative.
 // In the 32x32 accumulator a lane (row j, half h) holds windows 8q + 4h + e
 // (e = 0..3), i.e. exactly the four own windows of block 2q + h of the tile;
 // the fifth (halo) window comes from the other half-wave or the previous tile.
@@ -150,6 +151,11 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 constexpr int kMfmaRG = 2;               // 32-row groups per wave (share A fragments)
 constexpr int kMfmaRows = 32 * kMfmaRG;  // rows per workgroup
 constexpr int kMfmaWaves = 8;            // waves per workgroup, splitting the windows
+// Pooled block scores of kStageTiles consecutive 8-block tiles are gathered
+// per wave in LDS and written out as whole 32-block (128-byte) row pieces.
+constexpr int kStageTiles = 4;
+constexpr int kStageBlocks = 8 * kStageTiles;
+constexpr int kStageStride = kStageBlocks + 4;   // floats per staged row (16-byte pad)
 
 template <int D>
 __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
@@ -157,6 +163,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   constexpr int RG = kMfmaRG;
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
   __shared__ int pos_lds[kMfmaRows];
+  __shared__ __attribute__((aligned(16))) float stage[kMfmaWaves][kMfmaRows * kStageStride];
 
   const int w = xcd_contiguous_index(blockIdx.x, gridDim.x);
   const int g = w / n_row_tiles, tile = w % n_row_tiles;
@@ -176,15 +183,15 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
     if (row < a.rows) {
       const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.h_q + (int64_t)g * G) * D + c * 8;
-      // heads in batches of 8 loads issued together (the head count is a
+      // heads in batches of 16 loads issued together (the head count is a
       // run-time value; a plain loop would wait for each load in turn)
-      for (int h0 = 0; h0 < G; h0 += 8) {
-        u32x4 w[8];
+      for (int h0 = 0; h0 < G; h0 += 16) {
+        u32x4 w[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 16; ++j)
           if (h0 + j < G) w[j] = ldg16(qp + (int64_t)(h0 + j) * D);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 16; ++j)
           if (h0 + j < G) {
             float x[8];
             Elem<uint16_t>::unpack(w[j], x);
@@ -193,12 +200,14 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
           }
       }
     }
+    // the softmax scale goes into the query sum, so accumulators hold sigma
     u32x4 hi, lo;
     uint32_t hb[8], lb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      hb[e] = float_to_bf16_bits(acc[e]);
-      lb[e] = float_to_bf16_bits(acc[e] - bf16_bits_to_float(hb[e]));
+      const float v = acc[e] * a.scale;
+      hb[e] = float_to_bf16_bits(v);
+      lb[e] = float_to_bf16_bits(v - bf16_bits_to_float(hb[e]));
     }
     hi.x = hb[0] | (hb[1] << 16); hi.y = hb[2] | (hb[3] << 16);
     hi.z = hb[4] | (hb[5] << 16); hi.w = hb[6] | (hb[7] << 16);
@@ -220,8 +229,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
 
   // this lane: column `col` of row groups rg = 0..RG-1 (row r0 + 32 rg + col)
   bf16x8 qh[RG][KS], ql[RG][KS];
-  int pos[RG], n_vis[RG], b_own[RG];
-  float* out[RG];
+  int pos[RG], n_vis[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg) {
     const int rr = 32 * rg + col;
@@ -233,8 +241,6 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     pos[rg] = pos_lds[rr];
     // visible windows: m*s + ks - 1 <= pos (32-bit: the host bounds max_pos)
     n_vis[rg] = pos[rg] >= a.ks - 1 ? (pos[rg] - a.ks + 1) / a.s + 1 : 0;
-    b_own[rg] = pos[rg] >= 0 ? pos[rg] / a.B : -1;
-    out[rg] = a.scores + ((int64_t)(r0 + rr) * a.h_kv + g) * a.nb_cap;
   }
   int tile_max_pos = -1, tile_min_vis = 0x7fffffff;
   for (int j = 0; j < kMfmaRows; ++j) {
@@ -242,11 +248,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     tile_max_pos = max(tile_max_pos, pj);
     if (pj >= 0) tile_min_vis = min(tile_min_vis, pj >= a.ks - 1 ? (pj - a.ks + 1) / a.s + 1 : 0);
   }
+  tile_max_pos = __builtin_amdgcn_readfirstlane(tile_max_pos);   // same in every lane
+  tile_min_vis = __builtin_amdgcn_readfirstlane(tile_min_vis);
   const int nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
   const int n_tiles8 = (nb_tile + 7) / 8;
   const uint16_t* ckb = (const uint16_t*)a.ck + (int64_t)g * a.nc_cap * D;
   const int nc_cap = (int)min(a.nc_cap, (int64_t)0x7fffffff);
-  const float sc = a.scale;
 
   // dot of this lane's query half with one compressed key (VALU), combined
   // over the two half-waves: the halo window before a wave's first tile
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       }
     }
     const float full = part + swap_halves(part);
-    return (m >= 0 && m < n_vis[rg]) ? full * sc : -INFINITY;
+    return (m >= 0 && m < n_vis[rg]) ? full : -INFINITY;
   };
 
   // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
@@ -280,6 +287,12 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   // A-operand fragments of a tile: window 32 tt + col, dims 16ks + 8half
   auto load_tile = [&](int tt, u32x4* fr) {
     const int mrow = tt * 32 + col;
+    if (tt * 32 + 31 < nc_cap) {               // whole tile inside the buffer (uniform)
+      const uint16_t* crow = ckb + (int64_t)mrow * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) fr[ks] = ldg16(crow + 16 * ks);
+      return;
+    }
     const bool in = mrow < nc_cap;
     const uint16_t* crow = ckb + (int64_t)(in ? mrow : 0) * D + 8 * half;
 #pragma unroll
@@ -287,6 +300,35 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       const u32x4 wv = ldg16(crow + 16 * ks);
       const u32x4 z = {0u, 0u, 0u, 0u};
       fr[ks] = in ? wv : z;
+    }
+  };
+  // Write the staged group that tile t closes: lane l takes row 8 i + l / 8
+  // and blocks 4 (l % 8) .. + 3 of the group, so each store instruction
+  // covers 8 rows x 128 contiguous bytes.  Only this wave's tiles of the
+  // group are written, and only blocks up to the row's own block.
+  float* sw = stage[wave];
+  auto flush = [&](int t) {
+    const int g0 = (t / kStageTiles) * kStageTiles;          // first tile of the group
+    const int tb = max(g0, t_begin), te = t;                 // staged tiles tb .. te
+    const int piece = lane & 7, sub = lane >> 3;
+    const int blk = 8 * g0 + 4 * piece;                      // first block of the piece
+    const bool in = blk >= 8 * tb && blk < 8 * (te + 1);
+#pragma unroll 1
+    for (int i = 0; i < kMfmaRows / 8; ++i) {
+      const int rr = 8 * i + sub;
+      const int p = pos_lds[rr];
+      if (!in || p < 0) continue;
+      const int bo = p / a.B;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&sw[rr * kStageStride + 4 * piece]);
+      float* o = a.scores + ((int64_t)(r0 + rr) * a.h_kv + g) * a.nb_cap + blk;
+      if (blk + 3 <= bo && a.vec_store) {
+        *reinterpret_cast<f32x4*>(o) = v;
+      } else {
+        if (blk + 0 <= bo) o[0] = v.x;
+        if (blk + 1 <= bo) o[1] = v.y;
+        if (blk + 2 <= bo) o[2] = v.z;
+        if (blk + 3 <= bo) o[3] = v.w;
+      }
     }
   };
   u32x4 frag[KS];
@@ -321,9 +363,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       if (full_vis) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          own[q] = sc * fmaxf(fmaxf(acc[rg][4 * q], acc[rg][4 * q + 1]),
-                              fmaxf(acc[rg][4 * q + 2], acc[rg][4 * q + 3]));
-          last[q] = sc * acc[rg][4 * q + 3];
+          own[q] = fmaxf(fmaxf(acc[rg][4 * q], acc[rg][4 * q + 1]),
+                         fmaxf(acc[rg][4 * q + 2], acc[rg][4 * q + 3]));
+          last[q] = acc[rg][4 * q + 3];
         }
       } else {
 #pragma unroll
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int m = mt + 8 * q + 4 * half + e;
-            const float x = m < n_vis[rg] ? acc[rg][4 * q + e] * sc : -INFINITY;
+            const float x = m < n_vis[rg] ? acc[rg][4 * q + e] : -INFINITY;
             mx = fmaxf(mx, x);
             if (e == 3) last[q] = x;
           }
@@ -357,18 +399,11 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       f32x4 w4;
       if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }
       else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }
-      const int b4 = bt + 4 * half;
-      if (pos[rg] >= 0) {
-        if (b4 + 3 <= b_own[rg] && a.vec_store) {
-          *reinterpret_cast<f32x4*>(out[rg] + b4) = w4;
-        } else {
-          if (b4 + 0 <= b_own[rg]) out[rg][b4 + 0] = w4.x;
-          if (b4 + 1 <= b_own[rg]) out[rg][b4 + 1] = w4.y;
-          if (b4 + 2 <= b_own[rg]) out[rg][b4 + 2] = w4.z;
-          if (b4 + 3 <= b_own[rg]) out[rg][b4 + 3] = w4.w;
-        }
-      }
+      // staged: row 32 rg + col, blocks 8 (t % kStageTiles) + 4 half .. + 3
+      *reinterpret_cast<f32x4*>(&sw[(32 * rg + col) * kStageStride +
+                                   8 * (t % kStageTiles) + 4 * half]) = w4;
     }
+    if ((t + 1) % kStageTiles == 0 || t + 1 == t_end) flush(t);
   }
 }
 
