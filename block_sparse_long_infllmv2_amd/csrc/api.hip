@@ -2,7 +2,6 @@
 #include "attn_common.h"
 
 namespace infllmv2 {
-int64_t decode_splits(int64_t max_seqlen, const Resolved& r);
 size_t tree_workspace_bytes(int n_draft, int h_q, int h_kv, int d, int64_t n_ctx,
                             const Resolved& r);
 size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,

@@ -1918,7 +1918,12 @@ namespace {
 
 // Splits per (row, KV head): enough workgroups to cover the GPU for batched
 // decode and tree verification while keeping the float32 partials small.
+// Decode aims at one resident round of kDecodeWaves single-wave workgroups
+// (two per CU, as the 64 KB staging ring allows): a larger batch gets fewer
+// splits, so each wave streams more chunks through its ring and the combine
+// merges fewer partials.
 constexpr int kMaxDecodeSplits = 32;
+constexpr int kDecodeWaves = 512;
 constexpr int kMaxTreeSplits = 32;
 constexpr int kMaxCombineSplits = 64;      // lanes of the combine kernel
 
@@ -2041,9 +2046,12 @@ int64_t split_count(int64_t units, int64_t cpb, int64_t max_default) {
   return n < need ? need : (n < 1 ? 1 : n);
 }
 
-int64_t decode_splits(int64_t max_seqlen, const Resolved& r) {
+int64_t decode_splits(int batch, int h_kv, int64_t max_seqlen, const Resolved& r) {
   const int64_t cpb = ceil_div(r.B, kChunk);
-  return split_count(decode_max_entries(max_seqlen, r) * cpb, cpb, kMaxDecodeSplits);
+  const int64_t units = (int64_t)(batch > 0 ? batch : 1) * (h_kv > 0 ? h_kv : 1);
+  int64_t cap = ceil_div((int64_t)kDecodeWaves, units);
+  if (cap > kMaxDecodeSplits) cap = kMaxDecodeSplits;
+  return split_count(decode_max_entries(max_seqlen, r) * cpb, cpb, cap);
 }
 
 int64_t tree_union_cap(int n_draft, int64_t n_ctx, const Resolved& r) {
@@ -2131,7 +2139,7 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return INFLLMV2_ERR_INVALID_ARG;
   if (batch == 0) return INFLLMV2_OK;
-  const int64_t n_split = decode_splits(max_seqlen, r);
+  const int64_t n_split = decode_splits(batch, h_kv, max_seqlen, r);
   if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
   const size_t need = decode_workspace_bytes(batch, h_q, h_kv, d, max_seqlen, r);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
@@ -2168,8 +2176,7 @@ size_t tree_workspace_bytes(int n_draft, int h_q, int h_kv, int d, int64_t n_ctx
 }
 size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,
                               const Resolved& r) {
-  (void)h_kv;
-  return partial_bytes(batch, h_q, d, decode_splits(max_seqlen, r));
+  return partial_bytes(batch, h_q, d, decode_splits(batch, h_kv, max_seqlen, r));
 }
 }  // namespace infllmv2
 
