@@ -173,9 +173,16 @@ constexpr int kMaxTopk = 128;          // the host rejects larger topk
 // up to this many (row, KV head) units a workgroup per row beats a wave per row
 constexpr int kFewRows = 512;
 
+// Set bits of a wave mask in the lanes below this one (v_mbcnt).
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // k-th largest (1 <= k <= 64) of one value per lane: bitonic sort across the
-// wave (ascending), then the value at lane 64 - k.
-__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k, int lane) {
+// wave (ascending), then the value at lane 64 - k; *largest = the maximum.
+__device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k, int lane,
+                                                     uint32_t* largest) {
 #pragma unroll
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
@@ -187,6 +194,7 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k, int lane
       v = (low == up) ? mn : mx;
     }
   }
+  *largest = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 64 - k);
 }
 
@@ -208,12 +216,16 @@ __device__ __forceinline__ int wave_excl_scan(int v, int* total, int lane) {
 // remains to break).  The keys may be only those >= lo (a lower bound of the
 // answer): below lo the counts are too small, which never changes a
 // `cnt >= need` decision there (all of them pass), but an exact count only
-// means something at candidates >= lo.
+// means something at candidates >= lo.  T lies in [lo, hi] (hi = the largest
+// key), so it shares the bits above the highest bit where lo and hi differ:
+// the search starts there, from those common bits.
 template <int N>
 __device__ __forceinline__ uint32_t threshold_search(const uint32_t (&key)[N], int need,
-                                                     uint32_t lo, bool* exact) {
-  uint32_t T = 0;
-  for (int bit = 31; bit >= 0; --bit) {
+                                                     uint32_t lo, uint32_t hi, bool* exact) {
+  const uint32_t diff = lo ^ hi;
+  const int top = diff ? 31 - __builtin_clz(diff) : -1;
+  uint32_t T = top >= 0 ? lo & ~((2u << top) - 1u) : lo;
+  for (int bit = top; bit >= 0; --bit) {
     const uint32_t cand = T | (1u << bit);
     int cnt = 0;
 #pragma unroll
@@ -235,7 +247,6 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= n_units) return;                   // whole wave leaves
   const int lane = threadIdx.x & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
   const int r = unit / a.h_kv, g = unit % a.h_kv;
   int32_t* out = a.block_idx + ((int64_t)r * a.h_kv + g) * a.topk;
   const int seq = a.row_seq ? a.row_seq[r] : 0;
@@ -260,19 +271,30 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   const int need = a.topk - n_forced;
   const float* S = a.scores + ((int64_t)r * a.h_kv + g) * a.nb_cap;
 
-  // 0 = not a candidate (forced or past the eligible range); candidates >= 1.
-  // Every lane loads (an in-range index), then selects: no divergent branch.
-  // forced blocks are bit j of a per-lane mask (VGPRs, not a lane mask per j)
-  static_assert(KPL <= 64, "forced-block mask holds 64 bits");
+  // Here n_elig > topk >= init + local, so the forced blocks are the two
+  // disjoint runs [0, f_init) and [f_lo, n_elig), and the candidates are
+  // exactly the blocks in between: [f_init, f_lo).  The output is the first
+  // run, the chosen candidates in ascending order, then the second run.
+  // key 0 = not a candidate; candidates >= 1.  Every lane loads (an in-range
+  // index), then selects: no divergent branch.
+  // Entries past n_elig but inside the row (< nb_cap) are read as they are
+  // and never become candidates, so a row of at least 64 * KPL entries needs
+  // no index clamp.
   uint32_t key[KPL];
-  uint64_t forced_bits = 0ull;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int b = lane + 64 * j;
-    const float x = S[b < n_elig ? b : n_elig - 1];
+  const uint32_t span = (uint32_t)(f_lo - f_init);
+  auto prep = [&](int j, float x) {
     const uint32_t k = orderable_key(x);
-    key[j] = (b < n_elig && b >= f_init && b < f_lo) ? (k == 0 ? 1u : k) : 0u;
-    forced_bits |= (b < n_elig && (b < f_init || b >= f_lo)) ? (1ull << j) : 0ull;
+    key[j] = (uint32_t)(lane + 64 * j - f_init) < span ? (k > 1u ? k : 1u) : 0u;
+  };
+  if (a.nb_cap >= 64 * KPL) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) prep(j, S[lane + 64 * j]);
+  } else {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int b = lane + 64 * j;
+      prep(j, S[b < n_elig ? b : n_elig - 1]);
+    }
   }
   // T = largest value with #(key >= T) >= need (the need-th largest key)
   uint32_t T = 0;
@@ -282,12 +304,12 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
     // lane maximum, so T >= it and smaller keys cannot matter.  The keys at
     // or above it usually number a few hundred: the search then runs on them
     // (kSurvivors per wave in LDS) instead of on all 64 * KPL keys.
-    uint32_t lo = 0;
+    uint32_t lo = 0, hi = 0xffffffffu;
     if (need <= 64) {
       uint32_t mx = 0;
 #pragma unroll
       for (int j = 0; j < KPL; ++j) mx = key[j] > mx ? key[j] : mx;
-      lo = wave_kth_largest(mx, need, lane);
+      lo = wave_kth_largest(mx, need, lane, &hi);
     }
     int mine = 0;
 #pragma unroll
@@ -309,9 +331,9 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
       uint32_t sk[kSurvivors / 64];
 #pragma unroll
       for (int j = 0; j < kSurvivors / 64; ++j) sk[j] = sv[lane + 64 * j];
-      T = threshold_search<kSurvivors / 64>(sk, need, lo, &exact);
+      T = threshold_search<kSurvivors / 64>(sk, need, lo, hi, &exact);
     } else {
-      T = threshold_search<KPL>(key, need, 0u, &exact);
+      T = threshold_search<KPL>(key, need, 0u, hi, &exact);
     }
   }
   // keys > T are kept; of the keys == T the lowest-indexed ones fill the rest
@@ -322,30 +344,43 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
     for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
     take = need - gt;
   }
-  int base = 0, eq_seen = 0;
+  // chosen candidates go to slots f_init, f_init + 1, ... in ascending order;
+  // the two forced runs fill the slots around them.  Separate loops on
+  // wave-uniform conditions keep the unrolled bodies free of branches.
   const int wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) {
-    const int b = lane + 64 * j;
-    const bool forced = (forced_bits >> j) & 1ull;
-    bool sel;
-    if (need <= 0) {
-      sel = forced;
-    } else if (exact) {
-      sel = forced || key[j] >= T;
-    } else {
-      const uint64_t eqm = __ballot(key[j] == T);
-      const int rank = eq_seen + __popcll(eqm & below);
-      eq_seen += __popcll(eqm);
-      sel = forced || key[j] > T || (key[j] == T && rank < take);
-    }
+  int base = f_init;
+  const int lim = f_init + (need > 0 ? need : 0);
+  auto emit = [&](int j, bool sel) {
     const uint64_t selm = __ballot(sel);
-    const int slot = base + __popcll(selm & below);
-    sel_lds[wv][(sel && slot < a.topk) ? slot : kMaxTopk + lane] = b;
+    const int slot = base + lanes_below(selm);
+    const int ok = (int)sel & (int)(slot < lim);            // no short-circuit branch
+    sel_lds[wv][ok ? slot : kMaxTopk + lane] = lane + 64 * j;
     base += __popcll(selm);
+  };
+  const int mode = __builtin_amdgcn_readfirstlane(need <= 0 ? 0 : (exact ? 1 : 2));
+  if (mode == 1) {
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) emit(j, key[j] >= T);
+  } else if (mode == 2) {
+    int eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const uint64_t eqm = __ballot(key[j] == T);
+      const int rank = eq_seen + lanes_below(eqm);
+      eq_seen += __popcll(eqm);
+      emit(j, (int)(key[j] > T) | ((int)(key[j] == T) & (int)(rank < take)));
+    }
   }
   __builtin_amdgcn_wave_barrier();
-  for (int i = lane; i < a.topk; i += 64) out[i] = i < base ? sel_lds[wv][i] : -1;
+  // slots: [0, f_init) init run, [f_init, lim) chosen, then the local run
+  const int n_local = n_elig - f_lo;
+  for (int i = lane; i < a.topk; i += 64) {
+    int v = -1;
+    if (i < f_init) v = i;
+    else if (i < lim) v = sel_lds[wv][i];
+    else if (i < lim + n_local) v = f_lo + (i - lim);
+    out[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -364,7 +399,7 @@ template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArgs a) {
   __shared__ uint32_t surv[kSurvivors];
   __shared__ int scan4[kTopkThreads / 64];
-  __shared__ uint32_t wave_lo[kTopkThreads / 64];
+  __shared__ uint32_t wave_lo[kTopkThreads / 64], wave_hi[kTopkThreads / 64];
   __shared__ uint32_t sh_T;
   __shared__ int sh_exact;
   const int r = blockIdx.x / a.h_kv, g = blockIdx.x % a.h_kv;
@@ -408,13 +443,18 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArg
   uint32_t T = 0u;
   bool exact = need <= 0;
   if (need > 0) {
-    uint32_t lo = 0u;
+    uint32_t lo = 0u, hi = 0xffffffffu;
     if (need <= 64) {
-      const uint32_t wl = wave_kth_largest(mx, need, lane);
-      if (lane == 0) wave_lo[wv] = wl;
+      uint32_t wh;
+      const uint32_t wl = wave_kth_largest(mx, need, lane, &wh);
+      if (lane == 0) { wave_lo[wv] = wl; wave_hi[wv] = wh; }
       __syncthreads();
+      hi = 0u;
 #pragma unroll
-      for (int w = 0; w < kTopkThreads / 64; ++w) lo = wave_lo[w] > lo ? wave_lo[w] : lo;
+      for (int w = 0; w < kTopkThreads / 64; ++w) {
+        lo = wave_lo[w] > lo ? wave_lo[w] : lo;
+        hi = wave_hi[w] > hi ? wave_hi[w] : hi;
+      }
     }
     int mine = 0;
 #pragma unroll
@@ -434,7 +474,7 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArg
 #pragma unroll
         for (int j = 0; j < kSurvivors / 64; ++j) sk[j] = surv[lane + 64 * j];
         bool ex = false;
-        const uint32_t t = threshold_search<kSurvivors / 64>(sk, need, lo, &ex);
+        const uint32_t t = threshold_search<kSurvivors / 64>(sk, need, lo, hi, &ex);
         if (lane == 0) { sh_T = t; sh_exact = ex ? 1 : 0; }
       }
     } else {
