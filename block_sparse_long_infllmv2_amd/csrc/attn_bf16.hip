@@ -172,7 +172,8 @@ struct Swz {
 // before the load that reads it.
 __device__ __forceinline__ void lds_dma16(uint32_t lds_addr, const void* gbase, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_addr), "v"(voff), "s"(gbase) : "memory", "m0");
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(gbase)
+               : "memory", "m0");
 }
 
 // Wait until at most N of this wave's vector-memory operations are still in
@@ -1424,7 +1425,7 @@ void attn16_prefill_kernel(AttnArgs a) {
     n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, n_b,
                                     reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
   }
-  const int n = n_entries * cpb;
+  const int n = __builtin_amdgcn_readfirstlane(n_entries * cpb);   // same in every lane
 
   // unit u -> first key, valid keys, mask of the tile's tokens that use it
   struct Unit { int key0, nv; uint32_t tm; };

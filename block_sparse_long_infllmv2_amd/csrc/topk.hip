@@ -443,18 +443,37 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArg
   uint32_t T = 0u;
   bool exact = need <= 0;
   if (need > 0) {
+    // Lower bound: the need-th largest of the 256 thread maxima (at least
+    // `need` threads hold a key >= it).  Wave 0 finds it with the bitwise
+    // search over those 256 values (4 per lane), starting below the bits
+    // they all share.
     uint32_t lo = 0u, hi = 0xffffffffu;
-    if (need <= 64) {
-      uint32_t wh;
-      const uint32_t wl = wave_kth_largest(mx, need, lane, &wh);
-      if (lane == 0) { wave_lo[wv] = wl; wave_hi[wv] = wh; }
+    if (need <= kTopkThreads) {
+      surv[tid] = mx;                              // surv is free until the survivors
       __syncthreads();
-      hi = 0u;
+      if (wv == 0) {
+        uint32_t m4[kTopkThreads / 64];
+        uint32_t mn = 0xffffffffu, mxx = 0u;
 #pragma unroll
-      for (int w = 0; w < kTopkThreads / 64; ++w) {
-        lo = wave_lo[w] > lo ? wave_lo[w] : lo;
-        hi = wave_hi[w] > hi ? wave_hi[w] : hi;
+        for (int j = 0; j < kTopkThreads / 64; ++j) {
+          m4[j] = surv[lane + 64 * j];
+          mn = m4[j] < mn ? m4[j] : mn;
+          mxx = m4[j] > mxx ? m4[j] : mxx;
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+          const uint32_t a1 = (uint32_t)__shfl_xor((int)mn, o, 64);
+          const uint32_t a2 = (uint32_t)__shfl_xor((int)mxx, o, 64);
+          mn = a1 < mn ? a1 : mn;
+          mxx = a2 > mxx ? a2 : mxx;
+        }
+        bool ex = false;
+        const uint32_t wl = threshold_search<kTopkThreads / 64>(m4, need, mn, mxx, &ex);
+        if (lane == 0) { wave_lo[0] = wl; wave_hi[0] = mxx; }
       }
+      __syncthreads();
+      lo = wave_lo[0];
+      hi = wave_hi[0];
     }
     int mine = 0;
 #pragma unroll
