@@ -9,7 +9,9 @@ throughput for.  One step = compress the windows this chunk completes ->
 block scores -> top-k -> sparse attention, i.e. every stage of the path.
 Other workloads (for reports): 1 = 32K decode, 3 = 128K tree verification
 with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
-6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence).
+6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence),
+7 = the whole 131072-token prompt prefilled in 16 chunks of 8192 (each chunk:
+its new windows -> scores -> top-k -> attention over the keys so far).
 
 Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
 HIP graph and replayed once; --eager times individual launches), per-stage
@@ -49,6 +51,14 @@ def _visible_selected_keys(pos, p, n_sel_blocks):
     return (n_sel_blocks - 1) * B + (pos % B) + 1
 
 
+def _kept_keys(pos, p):
+    """Keys attended by the query at `pos`: every key up to it while its
+    eligible blocks fit in topk, else topk - 1 full blocks + its own prefix."""
+    if pos // p.block_size + 1 <= p.topk:
+        return pos + 1
+    return _visible_selected_keys(pos, p, p.topk)
+
+
 def _kernel_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -84,7 +94,11 @@ class Workload:
         # K/V is really read); shows the decode kernel where HBM bandwidth,
         # not launch latency, is the limit
         self.rep = 1
-        if wid == 5:
+        if wid == 7:
+            # the whole 128K prompt: queries at every position, 16 chunks of 8192
+            self.case = config(2, seed=seed, n_q=131072)
+            self.name = "sparse_prefill_bf16_128k_whole_16x8192"
+        elif wid == 5:
             self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
             self.name = "decode_bf16_128k"
         elif wid == 6:
@@ -99,7 +113,17 @@ class Workload:
         self.p = p
         bf = torch.bfloat16
         up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev, bf)
-        if wid == 2:
+        if wid == 7:
+            self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
+            h_kv, n_k, d = c.k.shape
+            self.cp = PL.ChunkedPrefill(n_k, 8192, c.q.shape[1], h_kv, d, bf, p, device=dev)
+            self.plan = self.cp.plans[-1]
+            nc = _n_windows(n_k, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((h_kv, nc, d), dtype=bf, device=dev)
+            torch.cuda.synchronize()
+            self.tokens = n_k
+            self.kind = "prefill_whole"
+        elif wid == 2:
             self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
             h_kv, n_k, d = c.k.shape
             self.plan = PL.PrefillPlan(c.n_q, n_k, c.q.shape[1], h_kv, d, bf, p, device=dev)
@@ -158,7 +182,23 @@ class Workload:
                 e.record()
                 ev.append((name, e))
         pl = self.plan
-        if self.kind == "prefill":
+        if self.kind == "prefill_whole":
+            mark("start")
+            cp = self.cp
+            for (q0, q1, _, m0, m1), pc in zip(cp.sched, cp.plans):
+                qc = self.q[q0:q1]
+                if m1 > m0:
+                    pc.compress(self.k, self.ck, m_begin=m0)
+                mark("compress_keys")
+                if not pc.dense:
+                    pc.score(qc, self.ck)
+                    mark("block_scores")
+                    pc.topk()
+                    mark("select_topk")
+                if not skip_dominant:
+                    pc.attend(qc, self.k, self.v)
+                mark("sparse_attn_prefill")
+        elif self.kind == "prefill":
             mark("start")
             pl.compress(self.k, self.ck)
             mark("compress_keys")
@@ -187,6 +227,8 @@ class Workload:
     # the dominant call alone (the attention call of the step)
     def dominant_call(self):
         pl = self.plan
+        if self.kind == "prefill_whole":
+            raise NotImplementedError("timed by graph difference only")
         if self.kind == "prefill":
             pl.attend(self.q, self.k, self.v)
         elif self.kind == "decode":
@@ -197,6 +239,14 @@ class Workload:
     # ---- algorithmic work (what the method must touch / compute) ----------
     def work(self):
         c, p = self.case, self.p
+        if self.kind == "prefill_whole":
+            h_kv, n_k, d = c.k.shape
+            h_q = c.q.shape[1]
+            keys = sum(_kept_keys(x, p) for x in range(n_k))
+            nvis = sum(_n_windows(x + 1, p.kernel_size, p.kernel_stride) for x in range(n_k))
+            return {"dominant": "sparse_attn_prefill", "bound": "mfma",
+                    "flop": 4.0 * d * h_q * keys, "score_flop": 2.0 * d * h_kv * float(nvis),
+                    "src": "attn_bf16.hip", "launches": len(self.cp.plans)}
         if self.kind == "prefill":
             h_kv, n_k, d = c.k.shape
             h_q = c.q.shape[1]
@@ -243,6 +293,23 @@ def cpu_baseline(wl, budget_s=20.0):
     c, p = wl.case, wl.p
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
+        if wl.kind == "prefill_whole":
+            # query i sees keys [0, i]: the oracle's prefill of that prefix with
+            # one query, its compressed keys cut from the whole prompt's
+            ck = O.compress_keys(c.k, p, "bf16")
+            n = c.k.shape[1]
+            rows, i = [], 0
+            step = max(1, n // 256)
+            while time.perf_counter() - t0 < budget_s and i < n:
+                nw = O.num_windows(i + 1, p.kernel_size, p.kernel_stride)
+                O.prefill(c.q[i:i + 1], c.k[:, :i + 1], c.v[:, :i + 1], p, "bf16", rows=[0],
+                          ck=ck[:, :nw])
+                rows.append(i)
+                i += step
+            dt = time.perf_counter() - t0
+            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{len(rows)} of {n} prompt positions (every {step}th) incl. "
+                              f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
         if wl.kind == "prefill":
             ck = O.compress_keys(c.k, p, "bf16")
             rows, i = [], 0
@@ -342,8 +409,11 @@ def main():
     wall_eager = time.perf_counter() - t0
     stages = {}
     for ev in evs:
+        per_step = {}
         for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:]):
-            stages.setdefault(n1, []).append(e0.elapsed_time(e1))
+            per_step[n1] = per_step.get(n1, 0.0) + e0.elapsed_time(e1)
+        for k, v in per_step.items():
+            stages.setdefault(k, []).append(v)
     stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
 
     w = wl.work()
@@ -402,9 +472,14 @@ def main():
         achieved = w["flop"] / (dom_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": _traffic(dom, src), "kernel": dom,
-                "algorithmic_gflop_per_launch": round(w["flop"] / 1e9, 2),
+                # the counter figure is per launch of the final-chunk workload
+                "traffic": _traffic(dom, src) if w.get("launches", 1) == 1 else None,
+                "kernel": dom,
+                ("algorithmic_gflop_per_step" if w.get("launches", 1) > 1
+                 else "algorithmic_gflop_per_launch"): round(w["flop"] / 1e9, 2),
                 "kernel_ms": round(dom_ms, 4)}
+        if w.get("launches", 1) > 1:
+            roof["launches_per_step"] = w["launches"]
     else:
         achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -415,7 +490,10 @@ def main():
 
     cfg = {"workload": wl.name}
     c = wl.case
-    if wl.kind == "prefill":
+    if wl.kind == "prefill_whole":
+        cfg.update({"context": int(c.k.shape[1]), "chunk_queries": 8192,
+                    "chunks": len(wl.cp.plans)})
+    elif wl.kind == "prefill":
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": int(c.n_q)})
     elif wl.kind == "decode":
         lens = [int(x) for x in np.tile(np.asarray(c.seqlens), wl.rep)]

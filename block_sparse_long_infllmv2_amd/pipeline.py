@@ -23,7 +23,12 @@ class PrefillPlan:
     select_topk -> sparse_attn_prefill.  Dense (n_k < dense_len): attention only.
     """
 
-    def __init__(self, n_q, n_k, h_q, h_kv, d, dtype, params, device="cuda"):
+    def __init__(self, n_q, n_k, h_q, h_kv, d, dtype, params, device="cuda",
+                 out=None, lse=None, score_buf=None, idx_buf=None):
+        """`out` [n_q][h_q][d] and `lse` [n_q][h_q] may be views into a larger
+        output; `score_buf` / `idx_buf` are flat float32 / int32 scratch
+        buffers, large enough, that plans run one after another on a stream
+        may share."""
         self.p = B.to_params(params)
         self.n_q, self.n_k, self.h_q, self.h_kv, self.d = n_q, n_k, h_q, h_kv, d
         self.dtype = dtype
@@ -32,12 +37,22 @@ class PrefillPlan:
         dev = torch.device(device)
         self.seqlens = torch.tensor([n_k], dtype=torch.int32, device=dev)
         self.row_pos = torch.arange(n_k - n_q, n_k, dtype=torch.int32, device=dev)
-        self.scores = None if self.dense else torch.empty(
-            (n_q, h_kv, self.nb), dtype=torch.float32, device=dev)
-        self.block_idx = None if self.dense else torch.empty(
-            (n_q, h_kv, self.p.topk), dtype=torch.int32, device=dev)
-        self.out = torch.empty((n_q, h_q, d), dtype=dtype, device=dev)
-        self.lse = torch.empty((n_q, h_q), dtype=torch.float32, device=dev)
+
+        def scratch(buf, shape, dt):
+            if buf is None:
+                return torch.empty(shape, dtype=dt, device=dev)
+            n = shape[0] * shape[1] * shape[2]
+            assert buf.dtype == dt and buf.numel() >= n
+            return buf[:n].view(shape)
+
+        self.scores = None if self.dense else scratch(score_buf, (n_q, h_kv, self.nb),
+                                                      torch.float32)
+        self.block_idx = None if self.dense else scratch(idx_buf, (n_q, h_kv, self.p.topk),
+                                                         torch.int32)
+        self.out = out if out is not None else torch.empty((n_q, h_q, d), dtype=dtype,
+                                                           device=dev)
+        self.lse = lse if lse is not None else torch.empty((n_q, h_q), dtype=torch.float32,
+                                                           device=dev)
         # windows completed by this chunk: all windows not complete before it
         self.m_begin = _windows(n_k - n_q, self.p.kernel_size, self.p.kernel_stride)
         self.m_end = _windows(n_k, self.p.kernel_size, self.p.kernel_stride)
@@ -71,6 +86,64 @@ class PrefillPlan:
             self.select(q, ck_cache)
         self.attend(q, k_cache, v_cache)
         return self.out
+
+
+def chunk_schedule(n: int, chunk: int, params) -> list:
+    """Chunks of a whole-prompt prefill: (q_begin, q_end, n_k, m_begin, m_end)
+    per chunk, queries [q_begin, q_end) over keys [0, n_k = q_end), and the
+    compressed-key windows [m_begin, m_end) that complete inside it."""
+    p = B.to_params(params)
+    out = []
+    for q0 in range(0, n, chunk):
+        q1 = min(n, q0 + chunk)
+        out.append((q0, q1, q1, _windows(q0, p.kernel_size, p.kernel_stride),
+                    _windows(q1, p.kernel_size, p.kernel_stride)))
+    return out
+
+
+class ChunkedPrefill:
+    """A whole prompt of n tokens prefilled chunk by chunk (chunk c: queries
+    [c*chunk, (c+1)*chunk) over the keys up to its end), as an engine runs a
+    long prompt.  Each chunk: compress the windows it completes, block
+    scores, top-k, sparse attention (a chunk whose keys number fewer than
+    dense_len: its windows, then dense attention only).  Plans and buffers
+    are made once; all chunks share one score and one selection scratch
+    buffer and write into one output."""
+
+    def __init__(self, n, chunk, h_q, h_kv, d, dtype, params, device="cuda"):
+        self.p = B.to_params(params)
+        self.n, self.chunk = n, chunk
+        dev = torch.device(device)
+        self.sched = chunk_schedule(n, chunk, params)
+        self.out = torch.empty((n, h_q, d), dtype=dtype, device=dev)
+        self.lse = torch.empty((n, h_q), dtype=torch.float32, device=dev)
+        nb_max = (n + self.p.block_size - 1) // self.p.block_size
+        self.score_buf = torch.empty(chunk * h_kv * nb_max, dtype=torch.float32, device=dev)
+        self.idx_buf = torch.empty(chunk * h_kv * self.p.topk, dtype=torch.int32, device=dev)
+        self.plans = [PrefillPlan(q1 - q0, n_k, h_q, h_kv, d, dtype, params, device=dev,
+                                  out=self.out[q0:q1], lse=self.lse[q0:q1],
+                                  score_buf=self.score_buf, idx_buf=self.idx_buf)
+                      for (q0, q1, n_k, _, _) in self.sched]
+
+    def run(self, q, k_cache, v_cache, ck_cache, skip_attention=False):
+        """q [n][h_q][d]; K/V caches [h_kv][cap >= n][d]; ck_cache
+        [h_kv][>= windows(n)][d] (filled here, window by window)."""
+        for (q0, q1, _, m0, m1), pl in zip(self.sched, self.plans):
+            qc = q[q0:q1]
+            # every chunk appends the windows it completes (a dense chunk too:
+            # later sparse chunks score against all of them)
+            if m1 > m0:
+                pl.compress(k_cache, ck_cache, m_begin=m0)
+            if not pl.dense:
+                pl.select(qc, ck_cache)
+            if not skip_attention:
+                pl.attend(qc, k_cache, v_cache)
+        return self.out
+
+    def attend_all(self, q, k_cache, v_cache):
+        """The attention calls of every chunk (selections from the last run)."""
+        for (q0, q1, _, _, _), pl in zip(self.sched, self.plans):
+            pl.attend(q[q0:q1], k_cache, v_cache)
 
 
 class DecodePlan:

@@ -101,3 +101,38 @@ def test_full_tree_verify_128k():
                                  (c.k_draft[:, anc], c.v_draft[:, anc]))
         check_close(out[i], o, "bf16", f"draft {i}")
         np.testing.assert_allclose(lse[i], l, atol=2e-3)
+
+
+def test_full_prefill_whole_prompt_sampled_rows():
+    """The whole 131072-token prompt in 16 chunks of 8192 (bench workload 7):
+    the compressed-key cache after the last chunk, and sampled rows of five
+    chunks against the oracle's prefill of each row's prefix."""
+    _say("full prefill: whole 128K prompt in 16 chunks")
+    wl = _workload(7)
+    c, p = wl.case, wl.p
+    ck = O.compress_keys(c.k, p, "bf16")
+    gck = _host(wl.ck)
+    assert np.count_nonzero(gck != ck) <= max(1, ck.size // 10000)
+    chunk = 8192
+    rows = [0, 8191, 8192, 40000, 65535, 65536 + 4096, 131071]
+    out = _host(wl.cp.out)
+    lse = wl.cp.lse.cpu().numpy()
+    for i in rows:
+        ci = i // chunk
+        pl = wl.cp.plans[ci]
+        # the shared selection scratch holds the last chunk's selections:
+        # select this chunk again (same inputs, same result)
+        pl.select(wl.q[ci * chunk:(ci + 1) * chunk], wl.ck)
+        torch.cuda.synchronize()
+        sel = pl.block_idx.cpu().numpy()[i - ci * chunk]
+        nw = O.num_windows(i + 1, p.kernel_size, p.kernel_stride)
+        res = O.prefill(c.q[i:i + 1], c.k[:, :i + 1], c.v[:, :i + 1], p, "bf16", rows=[0],
+                        ck=ck[:, :nw])
+        if res["dense"]:
+            o, l = res["o"][0], res["lse"][0]
+        else:
+            P = [check_selection(sel[g], res["S"][0][g], res["sel"][0][g], i, p,
+                                 f"row {i} g {g}") for g in range(2)]
+            o, l = O.attend_selected(c.q[i], c.k[:, :i + 1], c.v[:, :i + 1], P, i, p)
+        check_close(out[i], o, "bf16", f"row {i}")
+        np.testing.assert_allclose(lse[i], l, atol=2e-3)

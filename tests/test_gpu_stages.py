@@ -368,3 +368,46 @@ def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len):
             ref_o, ref_l = O.attend_selected(c.q[i], c.k, c.v, P, pos, p, extra)
         check_close(out[i], ref_o, dtype, f"draft {i}")
         np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if dtype == "bf16" else 1e-4)
+
+
+# ------------------------------------------------------ whole-prompt prefill ----
+def test_chunked_prefill_whole_prompt(B, PL):
+    """A 2560-token prompt prefilled in 5 chunks of 512 (the first, with fewer
+    keys than dense_len, dense): the compressed-key cache grows chunk by
+    chunk and every chunk's sampled rows match the oracle's prefill of the
+    whole prompt."""
+    _say("chunked prefill: 2560 tokens in chunks of 512, dense_len 1024")
+    p = Params(topk=8, dense_len=1024)
+    n, chunk = 2560, 512
+    c = make_prefill(31, n_k=n, n_q=n, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=3, alpha=1.5, beta=1.5)
+    q, k, v = dev(c.q, "bf16"), dev(c.k, "bf16"), dev(c.v, "bf16")
+    nc = O.num_windows(n, p.kernel_size, p.kernel_stride)
+    ck = torch.full((2, nc, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    cp = PL.ChunkedPrefill(n, chunk, 32, 2, 128, torch.bfloat16, p)
+    cp.run(q, k, v, ck)
+    torch.cuda.synchronize()
+    assert [pl.dense for pl in cp.plans] == [True, False, False, False, False]
+    # every window written once the whole prompt has passed
+    _check_ck(host(ck), O.compress_keys(c.k, p, "bf16"), "bf16", "compressed keys")
+    rows = sorted(set(r for q0 in range(0, n, chunk)
+                      for r in (q0, q0 + 1, q0 + 63, q0 + 64, q0 + 255, q0 + chunk - 1)))
+    res = O.prefill(c.q, c.k, c.v, p, "bf16", rows=rows)
+    out = host(cp.out)
+    lse = cp.lse.cpu().numpy()
+    for i in rows:
+        ci = i // chunk
+        pl = cp.plans[ci]
+        if pl.dense:
+            ref_o, ref_l = O.dense_attend(c.q[i], c.k, c.v, i, p)
+        else:
+            # selections of the chunk's rows are in the shared scratch of the
+            # last run only for the last chunk: recompute this chunk's selection
+            pl.select(q[ci * chunk:(ci + 1) * chunk], ck)
+            torch.cuda.synchronize()
+            sel = pl.block_idx.cpu().numpy()[i - ci * chunk]
+            P = [check_selection(sel[g], res["S"][i][g], res["sel"][i][g], i, p,
+                                 f"row {i} g {g}") for g in range(2)]
+            ref_o, ref_l = O.attend_selected(c.q[i], c.k, c.v, P, i, p)
+        check_close(out[i], ref_o, "bf16", f"row {i}")
+        np.testing.assert_allclose(lse[i], ref_l, atol=2e-3)
