@@ -136,3 +136,24 @@ def test_full_prefill_whole_prompt_sampled_rows():
             o, l = O.attend_selected(c.q[i], c.k[:, :i + 1], c.v[:, :i + 1], P, i, p)
         check_close(out[i], o, "bf16", f"row {i}")
         np.testing.assert_allclose(lse[i], l, atol=2e-3)
+
+
+def test_full_decode_128k_batch32():
+    """Bench workload 6: 32 copies of the 128K sequence, each in its own
+    memory (8 splits per row): row 0 against the oracle, every other row
+    identical to it (same inputs, deterministic kernels)."""
+    _say("full decode 128K batch 32")
+    wl = _workload(6)
+    c, p = wl.case, wl.p
+    res = O.decode(c.q, c.k, c.v, c.seqlens, p, "bf16")
+    out = _host(wl.plan.out)
+    lse = wl.plan.lse.cpu().numpy()
+    sel = wl.plan.block_idx.cpu().numpy()
+    pos = int(c.seqlens[0]) - 1
+    P = [check_selection(sel[0, g], res["S"][0][g], res["sel"][0][g], pos, p, f"g {g}")
+         for g in range(2)]
+    o, l = O.attend_selected(c.q[0], c.k[0], c.v[0], P, pos, p)
+    check_close(out[0], o, "bf16", "row 0")
+    np.testing.assert_allclose(lse[0], l, atol=2e-3)
+    for i in range(1, out.shape[0]):
+        assert np.array_equal(out[i], out[0]) and np.array_equal(sel[i], sel[0]), f"row {i}"

@@ -311,6 +311,27 @@ def test_decode_ragged(B, PL, dtype, d, h_q, h_kv):
     _check_decode(plan, c)
 
 
+def test_decode_block128(B, PL):
+    # 128-token blocks: two 64-key chunks per kept block in the split ranges
+    _say("decode bf16 block_size=128")
+    p = Params(block_size=128, topk=8, dense_len=2048)
+    c = make_decode(12, [100, 2047, 2048, 5000, 9001, 200], h_q=32, h_kv=2, d=128, params=p,
+                    dtype="bf16", planted_per_token=1 / 512)
+    plan = _run_decode(B, PL, c)
+    _check_decode(plan, c)
+
+
+def test_decode_large_batch_fewer_splits(B, PL):
+    # 40 sequences x 2 KV heads: the split count falls to ceil(512 / 80) = 7
+    _say("decode bf16 batch 40")
+    p = Params(dense_len=2048, topk=16)
+    lens = [int(x) for x in np.random.default_rng(13).integers(1, 9000, 40)]
+    c = make_decode(13, lens, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                    planted_per_token=1 / 512)
+    plan = _run_decode(B, PL, c)
+    _check_decode(plan, c)
+
+
 def test_decode_repeated_calls_reuse_workspace(B, PL):
     # a workspace holds nothing across calls: reusing it gives the same result
     _say("decode repeated calls")
@@ -328,13 +349,14 @@ def test_decode_repeated_calls_reuse_workspace(B, PL):
 
 
 # ----------------------------------------------------------------- tree ----
-@pytest.mark.parametrize("dtype,n_ctx,T,dense_len", [("bf16", 12000, 16, 8192),
-                                                     ("bf16", 5000, 16, 8192),
-                                                     ("bf16", 9000, 40, 0),
-                                                     ("f32", 3000, 7, 0)])
-def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len):
-    _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len}")
-    p = Params(dense_len=dense_len, topk=16)
+@pytest.mark.parametrize("dtype,n_ctx,T,dense_len,bs", [("bf16", 12000, 16, 8192, 64),
+                                                        ("bf16", 5000, 16, 8192, 64),
+                                                        ("bf16", 9000, 40, 0, 64),
+                                                        ("bf16", 9000, 16, 0, 128),
+                                                        ("f32", 3000, 7, 0, 64)])
+def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len, bs):
+    _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len} block={bs}")
+    p = Params(dense_len=dense_len, topk=16 if bs == 64 else 8, block_size=bs)
     h_q, h_kv, d = (32, 2, 128) if dtype == "bf16" else (4, 2, 64)
     c = make_tree(8, n_ctx=n_ctx, n_draft=T, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
                   n_planted=max(1, n_ctx // 2048))
