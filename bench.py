@@ -11,7 +11,8 @@ Other workloads (for reports): 1 = 32K decode, 3 = 128K tree verification
 with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
 6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence),
 7 = the whole 131072-token prompt prefilled in 16 chunks of 8192 (each chunk:
-its new windows -> scores -> top-k -> attention over the keys so far).
+its new windows -> scores -> top-k -> attention over the keys so far), 8 = the
+final chunk with 128-token blocks and top-6.
 
 Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
 HIP graph and replayed once; --eager times individual launches), per-stage
@@ -84,7 +85,7 @@ class Workload:
     def __init__(self, wid, torch, seed=0):
         from block_sparse_long_infllmv2_amd import binding as B
         from block_sparse_long_infllmv2_amd import pipeline as PL
-        from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, config
+        from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, Params, config
         self.torch, self.B, self.PL = torch, B, PL
         self.wid = wid
         dev = torch.device("cuda:0")
@@ -98,6 +99,11 @@ class Workload:
             # the whole 128K prompt: queries at every position, 16 chunks of 8192
             self.case = config(2, seed=seed, n_q=131072)
             self.name = "sparse_prefill_bf16_128k_whole_16x8192"
+        elif wid == 8:
+            # the final chunk again with the other variant the pages describe:
+            # 128-token blocks, top-6
+            self.case = config(2, seed=seed, params=Params(block_size=128, topk=6))
+            self.name = "sparse_prefill_bf16_128k_chunk8192_block128_top6"
         elif wid == 5:
             self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
             self.name = "decode_bf16_128k"
@@ -123,7 +129,7 @@ class Workload:
             torch.cuda.synchronize()
             self.tokens = n_k
             self.kind = "prefill_whole"
-        elif wid == 2:
+        elif wid in (2, 8):
             self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
             h_kv, n_k, d = c.k.shape
             self.plan = PL.PrefillPlan(c.n_q, n_k, c.q.shape[1], h_kv, d, bf, p, device=dev)

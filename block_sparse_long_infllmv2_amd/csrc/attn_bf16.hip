@@ -654,17 +654,20 @@ __device__ int build_union(const int32_t* block_idx, int tok0, int h_kv, int g, 
   }
   __syncthreads();
   bitonic_sort<NT>(sortbuf, N);
-  const int C = N / NT;                         // N is a multiple of NT
+  // thread t scans C consecutive sorted keys (N: a power of two, so either a
+  // multiple of NT or below it, one key per thread then)
+  const int C = N >= NT ? N / NT : 1;
   const int c0 = threadIdx.x * C;
+  const int c1 = min(c0 + C, N);
   int heads = 0;
-  for (int i = c0; i < c0 + C; ++i) {
+  for (int i = c0; i < c1; ++i) {
     const uint32_t key = sortbuf[i];
     if (key == 0xffffffffu) break;
     if (i == 0 || (sortbuf[i - 1] >> 5) != (key >> 5)) ++heads;
   }
   int total;
   int slot = block_excl_scan<NT>(heads, &total, scan_lds);
-  for (int i = c0; i < c0 + C; ++i) {
+  for (int i = c0; i < c1; ++i) {
     const uint32_t key = sortbuf[i];
     if (key == 0xffffffffu) break;
     if (i == 0 || (sortbuf[i - 1] >> 5) != (key >> 5)) {
@@ -785,7 +788,6 @@ void attn_bf16_kernel(AttnArgs a) {
     } else {
       int N = 1;
       while (N < TT * a.topk) N <<= 1;
-      if (N < NT) N = NT;
       n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, n_b,
                                       reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
     }
@@ -1421,7 +1423,6 @@ void attn16_prefill_kernel(AttnArgs a) {
   } else {
     int N = 1;
     while (N < TT * a.topk) N <<= 1;
-    if (N < NT) N = NT;
     n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, n_b,
                                     reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
   }

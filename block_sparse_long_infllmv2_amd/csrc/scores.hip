@@ -130,9 +130,10 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 
 // ---------------------------------------------------------------------------
 // Matrix-core variant for many rows of one sequence (prefill chunks, draft
-// batches) with the default window geometry: B = 4*s and ks = 2*s, so block b
-// overlaps windows 4b-1 .. 4b+3 (its four "own" windows and the last own
-// window of block b-1).
+// batches) with windows of two strides (ks = 2*s) and blocks of 4 or 8
+// strides: with B = 4*s block b overlaps windows 4b-1 .. 4b+3 (its four "own"
+// windows and the last own window of block b-1), with B = 8*s windows
+// 8b-1 .. 8b+7 (the default 64/32/16 and the 128-token-block variant).
 //
 // sigma^T = CK . qsum^T on v_mfma_f32_32x32x16_bf16: the A operand is 32
 // windows x 16 dims of compressed keys, the B operand 16 dims x 32 rows of
@@ -141,26 +142,33 @@ __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(Scor
 // significant bits so the scores match a float32 dot product to ~1e-5
 // relative.
 // In the 32x32 accumulator a lane (row j, half h) holds windows 8q + 4h + e
-// (e = 0..3), i.e. exactly the four own windows of block 2q + h of the tile;
-// the fifth (halo) window comes from the other half-wave or the previous tile.
+// (e = 0..3): with B = 4*s exactly the four own windows of block 2q + h of
+// the tile, the fifth (halo) window from the other half-wave or the previous
+// tile; with B = 8*s half of block q's own windows, the other half and the
+// halo from the other half-wave or the previous tile.
 //
 // Workgroup = 64 rows x one KV head; its 8 waves take contiguous ranges of
-// 8-block tiles, so qsum is built once (in LDS) per workgroup, and each wave
-// multiplies every compressed-key fragment it loads by two 32-row groups.
+// 32-window tiles, so qsum is built once (in LDS) per workgroup, and each
+// wave multiplies every compressed-key fragment it loads by two 32-row
+// groups.
 // ---------------------------------------------------------------------------
 constexpr int kMfmaRG = 2;               // 32-row groups per wave (share A fragments)
 constexpr int kMfmaRows = 32 * kMfmaRG;  // rows per workgroup
 constexpr int kMfmaWaves = 8;            // waves per workgroup, splitting the windows
-// Pooled block scores of kStageTiles consecutive 8-block tiles are gathered
-// per wave in LDS and written out as whole 32-block (128-byte) row pieces.
-constexpr int kStageTiles = 4;
-constexpr int kStageBlocks = 8 * kStageTiles;
+// Pooled block scores of consecutive tiles (32 windows each: 8 blocks of 4
+// windows or 4 blocks of 8) are gathered per wave in LDS and written out as
+// whole 32-block (128-byte) row pieces.
+constexpr int kStageBlocks = 32;
 constexpr int kStageStride = kStageBlocks + 4;   // floats per staged row (16-byte pad)
 
-template <int D>
+// WPB = windows per block (B / s): 4 or 8.
+template <int D, int WPB>
 __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
+  static_assert(WPB == 4 || WPB == 8, "block = 4 or 8 window strides");
   constexpr int KS = D / 16;
   constexpr int RG = kMfmaRG;
+  constexpr int BPT = 32 / WPB;                    // blocks per 32-window tile
+  constexpr int kStageTiles = kStageBlocks / BPT;  // tiles per staged group
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
   __shared__ int pos_lds[kMfmaRows];
   __shared__ __attribute__((aligned(16))) float stage[kMfmaWaves][kMfmaRows * kStageStride];
@@ -251,7 +259,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   tile_max_pos = __builtin_amdgcn_readfirstlane(tile_max_pos);   // same in every lane
   tile_min_vis = __builtin_amdgcn_readfirstlane(tile_min_vis);
   const int nb_tile = tile_max_pos < 0 ? 0 : tile_max_pos / a.B + 1;   // blocks to score
-  const int n_tiles8 = (nb_tile + 7) / 8;
+  const int n_tiles = (nb_tile + BPT - 1) / BPT;
   const uint16_t* ckb = (const uint16_t*)a.ck + (int64_t)g * a.nc_cap * D;
   const int nc_cap = (int)min(a.nc_cap, (int64_t)0x7fffffff);
 
@@ -277,9 +285,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   // each wave takes a contiguous range of tiles (8 blocks = 32 windows each);
   // the halo of a tile's first block is the previous tile's last window,
   // carried in registers (computed directly only for the range's first tile)
-  const int per_wave = (n_tiles8 + kMfmaWaves - 1) / kMfmaWaves;
+  const int per_wave = (n_tiles + kMfmaWaves - 1) / kMfmaWaves;
   const int t_begin = wave * per_wave;
-  const int t_end = min(n_tiles8, t_begin + per_wave);
+  const int t_end = min(n_tiles, t_begin + per_wave);
   float carry[RG];
 #pragma unroll
   for (int rg = 0; rg < RG; ++rg)
@@ -311,8 +319,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     const int g0 = (t / kStageTiles) * kStageTiles;          // first tile of the group
     const int tb = max(g0, t_begin), te = t;                 // staged tiles tb .. te
     const int piece = lane & 7, sub = lane >> 3;
-    const int blk = 8 * g0 + 4 * piece;                      // first block of the piece
-    const bool in = blk >= 8 * tb && blk < 8 * (te + 1);
+    const int blk = BPT * g0 + 4 * piece;                    // first block of the piece
+    const bool in = blk >= BPT * tb && blk < BPT * (te + 1);
 #pragma unroll 1
     for (int i = 0; i < kMfmaRows / 8; ++i) {
       const int rr = 8 * i + sub;
@@ -334,8 +342,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   u32x4 frag[KS];
   if (t_begin < t_end) load_tile(t_begin, frag);
   for (int t = t_begin; t < t_end; ++t) {
-    const int bt = t * 8;
-    const int mt = bt * 4;                     // first own window of the tile
+    const int mt = t * 32;                     // first own window of the tile
     u32x4 cur[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) cur[ks] = frag[ks];
@@ -357,8 +364,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
     const bool full_vis = mt + 32 <= tile_min_vis;
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-      // own maxima and last windows per block group q (block bt + 2q + half);
-      // tiles wholly visible to every row of the workgroup skip the masking
+      // per 4-window group q of the lane's half: its maximum and last window
+      // (windows 8q + 4 half .. + 3 of the tile); tiles wholly visible to
+      // every row of the workgroup skip the masking
       float own[4], last[4];
       if (full_vis) {
 #pragma unroll
@@ -384,24 +392,44 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       float other[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) other[q] = swap_halves(last[q]);
-      // halo window of block bt + 2q + half is the last own window of the
-      // block before it: half 1 <- (q, half 0); half 0 <- (q-1, half 1)
-      float bs[4];
+      if constexpr (WPB == 4) {
+        // block 2q + half of the tile: the lane's four windows; its halo
+        // window is the last own window of the block before it:
+        // half 1 <- (q, half 0); half 0 <- (q-1, half 1)
+        float bs[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry[rg]);
-        bs[q] = fmaxf(own[q], halo);
+        for (int q = 0; q < 4; ++q) {
+          const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry[rg]);
+          bs[q] = fmaxf(own[q], halo);
+        }
+        carry[rg] = other[3];     // for half-0 lanes: last window of block 7
+        // regroup: half 0 -> blocks 0..3 of the tile, half 1 -> 4..7
+        const float x0 = swap_halves(half ? bs[0] : bs[2]);
+        const float x1 = swap_halves(half ? bs[1] : bs[3]);
+        f32x4 w4;
+        if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }
+        else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }
+        // staged: row 32 rg + col, blocks 8 (t % kStageTiles) + 4 half .. + 3
+        *reinterpret_cast<f32x4*>(&sw[(32 * rg + col) * kStageStride +
+                                     8 * (t % kStageTiles) + 4 * half]) = w4;
+      } else {
+        // block q of the tile: windows 8q .. 8q+7, four in each half; its
+        // halo window 8q - 1 is the last window of block q - 1 (half 1), or
+        // of the previous tile for q = 0
+        float bs[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float both = fmaxf(own[q], swap_halves(own[q]));
+          const float halo = q > 0 ? (half ? last[q - 1] : other[q - 1]) : carry[rg];
+          bs[q] = fmaxf(both, halo);
+        }
+        carry[rg] = half ? last[3] : other[3];     // window 31 of the tile
+        if (half == 0) {
+          const f32x4 w4 = {bs[0], bs[1], bs[2], bs[3]};
+          *reinterpret_cast<f32x4*>(&sw[(32 * rg + col) * kStageStride +
+                                       4 * (t % kStageTiles)]) = w4;
+        }
       }
-      carry[rg] = other[3];     // for half-0 lanes: last window of block bt + 7
-      // regroup: half 0 -> blocks bt..bt+3, half 1 -> bt+4..bt+7
-      const float x0 = swap_halves(half ? bs[0] : bs[2]);
-      const float x1 = swap_halves(half ? bs[1] : bs[3]);
-      f32x4 w4;
-      if (half == 0) { w4.x = bs[0]; w4.y = x0; w4.z = bs[1]; w4.w = x1; }
-      else           { w4.x = x0; w4.y = bs[2]; w4.z = x1; w4.w = bs[3]; }
-      // staged: row 32 rg + col, blocks 8 (t % kStageTiles) + 4 half .. + 3
-      *reinterpret_cast<f32x4*>(&sw[(32 * rg + col) * kStageStride +
-                                   8 * (t % kStageTiles) + 4 * half]) = w4;
     }
     if ((t + 1) % kStageTiles == 0 || t + 1 == t_end) flush(t);
   }
@@ -452,16 +480,25 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.chunks_per_row = (int)ceil_div(nb_launch, bpw);
   if ((int64_t)a.chunks_per_row * rows >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
-  const bool mfma_geometry = r.B == 4 * r.s && r.ks == 2 * r.s;
+  const bool mfma_geometry = r.ks == 2 * r.s && (r.B == 4 * r.s || r.B == 8 * r.s);
   if (dtype == INFLLMV2_BF16 && batch == 1 && row_seq == nullptr && mfma_geometry &&
       rows >= kMfmaMinRows) {
     const int n_row_tiles = (int)ceil_div(rows, kMfmaRows);
     if ((int64_t)n_row_tiles * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
     dim3 grid((unsigned)(n_row_tiles * h_kv));
-    if (d == 128)
-      hipLaunchKernelGGL(block_scores_mfma_kernel<128>, grid, dim3(kMfmaWaves * 64), 0, st, a, n_row_tiles);
+    const bool wide = r.B == 8 * r.s;
+    if (d == 128 && !wide)
+      hipLaunchKernelGGL((block_scores_mfma_kernel<128, 4>), grid, dim3(kMfmaWaves * 64), 0, st, a,
+                         n_row_tiles);
+    else if (d == 128)
+      hipLaunchKernelGGL((block_scores_mfma_kernel<128, 8>), grid, dim3(kMfmaWaves * 64), 0, st, a,
+                         n_row_tiles);
+    else if (!wide)
+      hipLaunchKernelGGL((block_scores_mfma_kernel<64, 4>), grid, dim3(kMfmaWaves * 64), 0, st, a,
+                         n_row_tiles);
     else
-      hipLaunchKernelGGL(block_scores_mfma_kernel<64>, grid, dim3(kMfmaWaves * 64), 0, st, a, n_row_tiles);
+      hipLaunchKernelGGL((block_scores_mfma_kernel<64, 8>), grid, dim3(kMfmaWaves * 64), 0, st, a,
+                         n_row_tiles);
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   if (dtype == INFLLMV2_BF16)

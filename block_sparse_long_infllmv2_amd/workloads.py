@@ -265,7 +265,7 @@ def config(cfg: int, seed: int = 0, **over):
                            dtype="bf16", n_planted=over.get("n_planted", 16),
                            name=CONFIG_NAMES[1])
     if cfg == 2:
-        p = Params()
+        p = over.get("params", Params())
         n_k = over.get("n_k", 131072)
         n_q = over.get("n_q", 8192)
         return make_prefill(seed + 2, n_k=n_k, n_q=n_q, h_q=32, h_kv=2, d=128,

@@ -32,9 +32,10 @@ def _host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def test_full_prefill_128k_chunk_sampled_rows():
-    _say("full prefill 128K, final 8192-query chunk")
-    wl = _workload(2)
+@pytest.mark.parametrize("wid", [2, 8])      # 8: 128-token blocks, top-6
+def test_full_prefill_128k_chunk_sampled_rows(wid):
+    _say(f"full prefill 128K, final 8192-query chunk (workload {wid})")
+    wl = _workload(wid)
     c, p = wl.case, wl.p
     rng = np.random.default_rng(123)
     rows = sorted(set([0, 1, 7, 8, 9, 63, 64, 4095, 4096, 8183, 8184, 8190, 8191] +

@@ -87,14 +87,17 @@ def test_compress_keys(B, dtype, d):
 
 
 # --------------------------------------------------------------- scores ----
-@pytest.mark.parametrize("dtype,d,h_q,h_kv,rows", [("bf16", 128, 32, 2, 12),
-                                                   ("f32", 64, 2, 1, 12),
-                                                   ("bf16", 64, 8, 2, 12),
-                                                   ("bf16", 128, 32, 2, 300),   # MFMA path
-                                                   ("bf16", 64, 4, 1, 100)])    # MFMA path
-def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv, rows):
-    _say(f"scores {dtype} d={d} h_q={h_q} h_kv={h_kv} rows={rows}")
-    p = Params(dense_len=0)
+@pytest.mark.parametrize("dtype,d,h_q,h_kv,rows,bs", [("bf16", 128, 32, 2, 12, 64),
+                                                      ("f32", 64, 2, 1, 12, 64),
+                                                      ("bf16", 64, 8, 2, 12, 64),
+                                                      ("bf16", 128, 32, 2, 300, 64),   # MFMA
+                                                      ("bf16", 64, 4, 1, 100, 64),     # MFMA
+                                                      ("bf16", 128, 32, 2, 300, 128),  # MFMA
+                                                      ("bf16", 64, 4, 1, 100, 128),    # MFMA
+                                                      ("bf16", 128, 32, 2, 12, 128)])
+def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv, rows, bs):
+    _say(f"scores {dtype} d={d} h_q={h_q} h_kv={h_kv} rows={rows} block={bs}")
+    p = Params(dense_len=0, block_size=bs)
     n_k = 5000
     c = make_prefill(3, n_k=n_k, n_q=1, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
                      n_planted=5, alpha=1.5, beta=1.5)
@@ -103,7 +106,7 @@ def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv, rows):
     edge = [0, 15, 30, 31, 63, 64, 78, 79, 200, 4095, 4999, 2500]
     pos = np.array(edge + list(rng.integers(0, n_k, rows - len(edge))), np.int32)
     q = dev(rng.standard_normal((len(pos), h_q, d)), dtype)
-    nb = n_k // 64 + 1
+    nb = n_k // bs + 1
     scores = torch.full((len(pos), h_kv, nb), 123.0, dtype=torch.float32, device="cuda")
     B.infllmv2_block_scores(q, None, torch.from_numpy(pos).cuda(), dev(ck[None], dtype),
                             torch.tensor([n_k], dtype=torch.int32, device="cuda"), scores,
