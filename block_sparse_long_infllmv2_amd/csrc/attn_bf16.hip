@@ -1292,6 +1292,16 @@ struct Row16 {
         s[kt][r] = 16 * kt + 4 * h + r <= lim ? s[kt][r] : -INFINITY;
   }
 
+  // keys whose bit is clear in `bits` -> -inf (the chunk of draft tokens)
+  __device__ __forceinline__ void mask_bits(f32x4 (&s)[4], uint64_t bits) const {
+    const int h = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        s[kt][r] = ((bits >> (16 * kt + 4 * h + r)) & 1ull) ? s[kt][r] : -INFINITY;
+  }
+
   // online softmax (log2 domain, lazy rescale as in the 32-row kernel); rows
   // with keep == false get p = 0 and leave m, l unchanged
   __device__ __forceinline__ PFrag softmax(f32x4 (&s)[4], bool keep, float scale_log2) {
@@ -1628,16 +1638,24 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
-template <int D>
+//
+// TREE: the rows are the draft tokens of a tree over one shared context cache
+// (row = draft, all at context position n_ctx - 1, each with its own kept
+// blocks); every row has one more unit after its context units: the chunk of
+// draft tokens, of which it sees those set in its ancestor mask (and itself).
+template <int D, bool TREE>
 __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   constexpr int NS = 2;
   constexpr int TILE = Swz16<D>::TILE;
   __shared__ __attribute__((aligned(16))) uint16_t stage[NS * TILE];   // K0 K1 V0 V1
   const int lane = threadIdx.x;
-  const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;
-  // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
-  const int Lr = a.seqlens[seq];
-  const int L = Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr);
+  const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;    // seq: the row
+  int L = (int)a.n_k;
+  if constexpr (!TREE) {
+    // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
+    const int Lr = a.seqlens[seq];
+    L = Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr);
+  }
   const bool dense = L < a.dense_len || a.block_idx == nullptr;
   const int n_b = (L + a.B - 1) / a.B;
   const int cpb = (a.B + kChunk - 1) / kChunk;
@@ -1655,7 +1673,8 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
       if (bad) n_entries = 64 * half + (int)__builtin_ctzll(bad);
     }
   }
-  const int units = n_entries * cpb;
+  const int ctx_units = n_entries * cpb;
+  const int units = ctx_units + (TREE ? 1 : 0);          // + the draft chunk
   const int per = (units + a.n_split - 1) / a.n_split;
   const int u_begin = min(units, split * per);
   const int n = min(units, u_begin + per) - u_begin;
@@ -1667,6 +1686,7 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   if (!dense) blk_lane = e_base + lane < n_entries ? lst[e_base + lane] : 0;
   struct Unit { int key0, nv; };
   auto unit = [&](int u) -> Unit {
+    if (TREE && u == ctx_units) return Unit{0, (int)a.n_rows};   // the draft chunk
     int e = u, c = 0;
     if (cpb != 1) { e = u / cpb; c = u - e * cpb; }
     const int b = __builtin_amdgcn_readlane(blk_lane, e - e_base);
@@ -1677,11 +1697,23 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
     r.nv = __builtin_amdgcn_readfirstlane(r.nv);
     return r;
   };
-  const int64_t kv_off = ((int64_t)seq * a.h_kv + g) * a.cap * D;
+  const int64_t kv_off = ((int64_t)(TREE ? 0 : seq) * a.h_kv + g) * a.cap * D;
   const uint16_t* kseq = a.k + kv_off;
   const uint16_t* vseq = a.v + kv_off;
-  auto kp = [&](const Unit& un) { return kseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
-  auto vp = [&](const Unit& un) { return vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0); };
+  // the draft chunk is unit ctx_units (its Unit has key0 0, nv = drafts)
+  const uint16_t* kdr = TREE ? a.k_draft + (int64_t)g * a.n_rows * D : nullptr;
+  const uint16_t* vdr = TREE ? a.v_draft + (int64_t)g * a.n_rows * D : nullptr;
+  uint64_t dbits = 0ull;
+  if constexpr (TREE) {
+    const uint64_t full = a.n_rows >= 64 ? ~0ull : ((1ull << a.n_rows) - 1ull);
+    dbits = (a.tree_mask[seq] & full) | (1ull << seq);
+  }
+  auto kp = [&](const Unit& un, bool isd) {
+    return isd ? kdr : kseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0);
+  };
+  auto vp = [&](const Unit& un, bool isd) {
+    return isd ? vdr : vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0);
+  };
 
   const int head = g * 16 + (lane & 15);
   Row16<D> st;
@@ -1704,23 +1736,26 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   dmak.init(lane);
   dmav.init(lane);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
-  auto issue = [&](const Unit& un, int slot) {
-    dmak.issue(lds0 + slot * TILE, kp(un), un.nv, lane, 0);
-    dmav.issue(lds0 + (NS + slot) * TILE, vp(un), un.nv, lane, 0);
+  auto is_draft = [&](int u) { return TREE && u == ctx_units; };
+  auto issue = [&](const Unit& un, int slot, bool isd) {
+    dmak.issue(lds0 + slot * TILE, kp(un, isd), un.nv, lane, 0);
+    dmav.issue(lds0 + (NS + slot) * TILE, vp(un, isd), un.nv, lane, 0);
   };
   Unit cur = {0, 0}, nxt = {0, 0};
-  if (n > 0) { cur = unit(u_begin); issue(cur, 0); }
-  if (n > 1) { nxt = unit(u_begin + 1); issue(nxt, 1); }
+  if (n > 0) { cur = unit(u_begin); issue(cur, 0, is_draft(u_begin)); }
+  if (n > 1) { nxt = unit(u_begin + 1); issue(nxt, 1, is_draft(u_begin + 1)); }
   const int pos = L - 1;
   auto step = [&](int i, auto slot_tag) {
     constexpr int S = decltype(slot_tag)::value;
     // the copy of chunk i+1 (if any) was issued after chunk i's
     if (i + 1 < n) wait_vm<2 * KL>(); else wait_vm<0>();
-    const int lim = min(pos - cur.key0, cur.nv - 1);
+    const bool isd = is_draft(u_begin + i);
+    const int lim = isd ? cur.nv - 1 : min(pos - cur.key0, cur.nv - 1);
     if (lim >= 0) {
       f32x4 sc[4];
       st.qk(lds0 + S * TILE, sc);
-      if (lim < kChunk - 1) st.mask(sc, lim);
+      if (isd) st.mask_bits(sc, dbits);
+      else if (lim < kChunk - 1) st.mask(sc, lim);
       const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
       st.pv(lds0 + (NS + S) * TILE, pf);
     }
@@ -1728,7 +1763,7 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
       // slot S is free once this wave's reads of it have returned
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       const Unit far = unit(u_begin + i + 2);
-      issue(far, S);
+      issue(far, S, is_draft(u_begin + i + 2));
       cur = nxt;
       nxt = far;
     } else {
@@ -2014,7 +2049,7 @@ int tree_tile_tokens(int G) {
 template <int D>
 int dispatch_decode(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
   if (G == 16) {
-    hipLaunchKernelGGL((attn16_decode_kernel<D>), grid, dim3(64), 0, st, a);
+    hipLaunchKernelGGL((attn16_decode_kernel<D, false>), grid, dim3(64), 0, st, a);
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   switch (G) {
@@ -2226,6 +2261,32 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   if (dtype == INFLLMV2_F32) return tree_f32(a, d, st);
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
+  if (G == 16) {
+    // 16-head groups: each draft is a row of the decode kernel over the
+    // shared context (its own kept blocks, then the draft chunk); splits as
+    // for decode (one resident round of waves), within the workspace's count
+    const int64_t cpb = ceil_div(r.B, kChunk);
+    const int64_t n_b = ceil_div(n_ctx, r.B);
+    const int64_t row_units = (dense ? n_b : r.topk) * cpb + 1;
+    int64_t ns = ceil_div((int64_t)kDecodeWaves, (int64_t)n_draft * h_kv);
+    ns = std::min<int64_t>(ns, n_split);
+    ns = std::max<int64_t>(ns, ceil_div(row_units, (int64_t)(kSplitEntryCap - 1) * cpb));
+    if (ns > n_split) return INFLLMV2_ERR_UNSUPPORTED;     // cannot happen: see tree_splits
+    a.n_split = (int)ns;
+    dim3 grid16((unsigned)ns, h_kv, (unsigned)n_draft);
+    if (d == 128)
+      hipLaunchKernelGGL((attn16_decode_kernel<128, true>), grid16, dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((attn16_decode_kernel<64, true>), grid16, dim3(64), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
+    if (d == 128)
+      hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(n_draft * h_q), dim3(64), 0, st,
+                         a.ws, a.n_split, (uint16_t*)out, lse);
+    else
+      hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(n_draft * h_q), dim3(64), 0, st,
+                         a.ws, a.n_split, (uint16_t*)out, lse);
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   const int TT = tree_tile_tokens(G);
   if (!dense) {
     const int64_t n_b = ceil_div(n_ctx, r.B);
