@@ -32,7 +32,8 @@ class Params(ctypes.Structure):
     _fields_ = [("block_size", ctypes.c_int32), ("kernel_size", ctypes.c_int32),
                 ("kernel_stride", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("init_blocks", ctypes.c_int32), ("local_blocks", ctypes.c_int32),
-                ("dense_len", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("dense_len", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("score_mode", ctypes.c_int32)]
 
 
 def _load():

@@ -23,6 +23,7 @@ extern "C" void infllmv2_default_params(infllmv2_params* p) {
   p->local_blocks = 2;
   p->dense_len = 8192;
   p->scale = 0.0f;
+  p->score_mode = 0;         // summed-query reading of the group score
 }
 
 extern "C" const char* infllmv2_status_string(int status) {

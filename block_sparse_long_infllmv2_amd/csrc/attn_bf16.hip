@@ -1893,7 +1893,7 @@ template <int D, typename TOut>
 __global__ __launch_bounds__(64) void combine_kernel(const float* ws, int n_split, TOut* out,
                                                      float* lse) {
   constexpr int kMaxSplit = 64;
-  constexpr int kBatch = 16;                 // splits whose o values are loaded together
+  constexpr int kBatch = 32;                 // splits whose o values are loaded together
   const int rh = blockIdx.x;   // row * h_q + head
   const int lane = threadIdx.x;
   const float* base = ws + (int64_t)rh * n_split * (D + 2);

@@ -12,7 +12,7 @@ namespace infllmv2 {
 
 // Parameters after defaults are applied (scale resolved for head_dim d).
 struct Resolved {
-  int B, ks, s, topk, init, local, dense_len;
+  int B, ks, s, topk, init, local, dense_len, score_mode;
   float scale;
 };
 
@@ -26,6 +26,7 @@ inline int check_params(const infllmv2_params* p, int d, Resolved* r) {
   if (p->kernel_stride > p->kernel_size) return INFLLMV2_ERR_UNSUPPORTED;
   if (p->block_size % 32 != 0 || p->block_size > 256) return INFLLMV2_ERR_UNSUPPORTED;
   if (p->topk > 128) return INFLLMV2_ERR_UNSUPPORTED;
+  if (p->score_mode != 0 && p->score_mode != 1) return INFLLMV2_ERR_INVALID_ARG;
   r->B = p->block_size;
   r->ks = p->kernel_size;
   r->s = p->kernel_stride;
@@ -33,6 +34,7 @@ inline int check_params(const infllmv2_params* p, int d, Resolved* r) {
   r->init = p->init_blocks;
   r->local = p->local_blocks;
   r->dense_len = p->dense_len;
+  r->score_mode = p->score_mode;
   r->scale = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)d);
   return INFLLMV2_OK;
 }

@@ -463,6 +463,7 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   if ((int64_t)max_pos / r.B + 1 > nb_cap) return INFLLMV2_ERR_INVALID_ARG;
   if (num_windows((int64_t)max_pos + 1, r.ks, r.s) > nc_cap) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(ck) || !aligned16(q)) return INFLLMV2_ERR_INVALID_ARG;
+  if (r.score_mode != 0) return INFLLMV2_ERR_UNSUPPORTED;
   if (rows == 0) return INFLLMV2_OK;
   ScoreArgs a;
   a.q = q; a.row_seq = row_seq; a.row_pos = row_pos; a.ck = ck; a.seqlens = seqlens;

@@ -48,6 +48,7 @@ class Params:
     local_blocks: int = 2
     dense_len: int = 8192
     scale: float = 0.0          # 0 -> 1/sqrt(head_dim)
+    score_mode: int = 0         # 0: summed-query group score; 1: sum of per-head softmaxes
 
     def replace(self, **kw) -> "Params":
         return dataclasses.replace(self, **kw)

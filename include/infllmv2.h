@@ -88,9 +88,14 @@ typedef struct {
   int32_t dense_len;      /* a sequence with fewer than dense_len keys uses dense
                              causal attention (default 8192)                      */
   float scale;            /* softmax scale; 0 selects 1/sqrt(d)                  */
+  int32_t score_mode;     /* how a KV group's query heads make one window score
+                             (the pages do not say; see infllmv2_block_scores):
+                             0 = scaled dot product with the group's summed
+                             query (default), 1 = sum over the group's heads of
+                             each head's softmax over the visible windows     */
 } infllmv2_params;
 
-/* host: fill *p with the defaults 64 / 32 / 16 / 64 / 1 / 2 / 8192 / 0. */
+/* host: fill *p with the defaults 64 / 32 / 16 / 64 / 1 / 2 / 8192 / 0 / 0. */
 void infllmv2_default_params(infllmv2_params* p);
 
 /* host: static string for a status code (never NULL). */
@@ -126,6 +131,11 @@ int infllmv2_compress_keys(int dtype, const void* k, int32_t batch, int32_t h_kv
  *
  *   sigma[m] = scale * sum_{h in group g} q[r][h] . ck[seq][g][m]
  *              for windows that end at or before row_pos[r]
+ *   (score_mode 1: sigma[m] = sum_{h in group g} softmax over the visible
+ *              windows m' of scale * q[r][h] . ck[seq][g][m'], taken at m;
+ *              with one query head per group it orders the windows as mode 0
+ *              does.  Mode 1 runs one workgroup per (row, KV head) and needs
+ *              h_q / h_kv <= 16 and at most 16384 visible windows.)
  *   scores[r][g][b] = max of sigma[m] over the visible windows m whose token
  *              span overlaps block b, or -inf if there is none,
  *

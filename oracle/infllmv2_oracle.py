@@ -30,7 +30,12 @@ Readings where the pages leave a step open (each one listed in the design doc):
   R5  only full kernel windows exist (no padded tail window).
   R6  a window is visible to a query at position p iff it ends at or before p.
   R7  group score = sum over the group's heads of scale * q_h . ck
-      -- parity unpinned by the pages (no worked example exists).
+      -- parity unpinned by the pages (no worked example exists).  With
+      score_mode = 1 the other plain reading: the sum over the group's
+      heads of each head's softmax over the windows visible to the query
+      (pinned by invariants: each head's share sums to 1; one head per
+      group selects what mode 0 selects; identical kernels give a uniform
+      share).
   R8  block score = max over every visible window that overlaps the block
       -- parity unpinned by the pages.
   R9  forced blocks count toward top-k.
@@ -146,7 +151,9 @@ def windows_of_block(b: int, params, n_c: int) -> range:
 def kernel_scores(q_row: np.ndarray, ck: np.ndarray, pos: int, params,
                   h_kv: int) -> np.ndarray:
     """sigma[g, m] = scale * sum_{h in g} q_h . ck[g, m] for windows that end
-    at or before pos (R6, R7); -inf for the others.
+    at or before pos (R6, R7); -inf for the others.  score_mode 1 (the other
+    reading of R7): sigma[g, m] = sum_{h in g} of head h's softmax over the
+    visible windows of scale * q_h . ck[g, m'], taken at m.
 
     q_row: [h_q][d] (one query token), ck: [h_kv][n_c][d].
     """
@@ -155,13 +162,22 @@ def kernel_scores(q_row: np.ndarray, ck: np.ndarray, pos: int, params,
     n_c = ck.shape[1]
     scale = _scale(params, d)
     ks, s = params.kernel_size, params.kernel_stride
+    mode = getattr(params, "score_mode", 0)
     sigma = np.full((h_kv, n_c), -np.inf)
     visible = np.array([m * s + ks - 1 <= pos for m in range(n_c)], dtype=bool)
     for g in range(h_kv):
         heads = [h for h in range(h_q) if _group_of_head(h, h_q, h_kv) == g]
-        qsum = q_row[heads].sum(axis=0)
-        vals = scale * (ck[g] @ qsum)
-        sigma[g, visible] = vals[visible]
+        if mode == 0:
+            qsum = q_row[heads].sum(axis=0)
+            vals = scale * (ck[g] @ qsum)
+            sigma[g, visible] = vals[visible]
+        elif visible.any():
+            total = np.zeros(int(visible.sum()))
+            for h in heads:
+                logits = scale * (ck[g][visible] @ q_row[h])
+                w = np.exp(logits - logits.max())
+                total += w / w.sum()
+            sigma[g, visible] = total
     return sigma
 
 

@@ -76,7 +76,8 @@ def test_defaults_status_version(lib):
     p = lib.Params()
     lib.infllmv2_default_params(ctypes.byref(p))
     assert (p.block_size, p.kernel_size, p.kernel_stride, p.topk, p.init_blocks,
-            p.local_blocks, p.dense_len, p.scale) == (64, 32, 16, 64, 1, 2, 8192, 0.0)
+            p.local_blocks, p.dense_len, p.scale, p.score_mode) == (64, 32, 16, 64, 1, 2,
+                                                                    8192, 0.0, 0)
     assert lib.infllmv2_status_string(0) == b"ok"
     assert b"workspace" in lib.infllmv2_status_string(3)
     assert lib.infllmv2_status_string(99) == b"unknown status"
@@ -110,6 +111,8 @@ def test_compress_validation(lib):
              params(lib, topk=2, init_blocks=1, local_blocks=2), None) == INVALID
     assert f(1, FAKE, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63,
              params(lib, kernel_stride=64), None) == UNSUPPORTED
+    assert f(1, FAKE, 1, 2, 1024, 128, seq, 0, 10, FAKE, 63,
+             params(lib, score_mode=2), None) == INVALID
     assert f(1, FAKE, 1, 2, 1024, 128, seq, 5, 5, FAKE, 63, params(lib), None) == OK  # empty
 
 

@@ -134,6 +134,66 @@ def test_kernel_scores_group_sum_and_scale_by_hand():
     assert sig[0, 0] == 2.5
 
 
+def test_score_mode1_by_hand():
+    # the same two groups as above, each head's softmax over the two windows
+    p = Params(scale=0.5, score_mode=1)
+    q = np.array([[1.0, 0.0], [2.0, 1.0], [0.0, 3.0], [1.0, -1.0]])
+    ck = np.array([[[1.0, 2.0], [3.0, -1.0]],
+                   [[2.0, 2.0], [-1.0, 4.0]]])
+    sig = O.kernel_scores(q, ck, pos=100, params=p, h_kv=2)
+    # group 0: head 0 logits (0.5, 1.5), head 1 logits (2.0, 2.5)
+    e1, eh = math.e, math.exp(0.5)
+    g0 = [1 / (1 + e1) + 1 / (1 + eh), e1 / (1 + e1) + eh / (1 + eh)]
+    # group 1: head 2 logits (3.0, 6.0), head 3 logits (0.0, -2.5)
+    e3, e25 = math.exp(3.0), math.exp(2.5)
+    g1 = [1 / (1 + e3) + e25 / (1 + e25), e3 / (1 + e3) + 1 / (1 + e25)]
+    np.testing.assert_allclose(sig, [g0, g1], rtol=1e-14)
+    # only window 0 visible at position 40: each head gives it all of its share
+    sig = O.kernel_scores(q, ck, pos=40, params=p, h_kv=2)
+    np.testing.assert_allclose(sig[:, 0], [2.0, 2.0], rtol=1e-15)
+    assert sig[0, 1] == -np.inf and sig[1, 1] == -np.inf
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(2, 1), (32, 2), (8, 8)])
+def test_score_mode1_shares_sum_to_group_size(h_q, h_kv):
+    rng = np.random.default_rng(7)
+    d, n_c = 16, 50
+    q = rng.standard_normal((h_q, d)) * 3
+    ck = rng.standard_normal((h_kv, n_c, d))
+    p = Params(score_mode=1)
+    for pos in (31, 300, 815):
+        sig = O.kernel_scores(q, ck, pos, p, h_kv)
+        vis = np.isfinite(sig[0])
+        assert vis.sum() == O.num_windows(pos + 1, 32, 16)
+        np.testing.assert_allclose(sig[:, vis].sum(axis=1), h_q // h_kv, rtol=1e-12)
+        assert np.all(sig[:, vis] > 0)
+
+
+def test_score_mode1_uniform_when_kernels_are_identical():
+    rng = np.random.default_rng(8)
+    q = rng.standard_normal((32, 16))
+    ck = np.broadcast_to(rng.standard_normal((2, 1, 16)), (2, 40, 16)).copy()
+    sig = O.kernel_scores(q, ck, 500, Params(score_mode=1), 2)
+    n_vis = O.num_windows(501, 32, 16)
+    np.testing.assert_allclose(sig[:, :n_vis], 16.0 / n_vis, rtol=1e-13)
+
+
+def test_score_mode1_single_head_per_group_selects_as_mode0():
+    # one query head per group: each group's mode-1 score is an increasing
+    # function of its mode-0 score, so block maxima and selections agree
+    rng = np.random.default_rng(9)
+    h, d, n_k = 4, 16, 3000
+    p0, p1 = Params(topk=8), Params(topk=8, score_mode=1)
+    ck = rng.standard_normal((h, O.num_windows(n_k, 32, 16), d))
+    for pos in (700, 1500, 2999):
+        q = rng.standard_normal((h, d)) * 2
+        s0 = O.block_scores(O.kernel_scores(q, ck, pos, p0, h), pos, p0)
+        s1 = O.block_scores(O.kernel_scores(q, ck, pos, p1, h), pos, p1)
+        for g in range(h):
+            assert np.array_equal(O.select_blocks(s0[g], pos, p0),
+                                  O.select_blocks(s1[g], pos, p1))
+
+
 def test_block_scores_are_overlap_max_brute_force():
     rng = np.random.default_rng(3)
     p = Params()
