@@ -82,7 +82,7 @@ def _traffic(kernel_name, src_file):
 class Workload:
     """Builds inputs on the GPU and exposes step() plus algorithmic work."""
 
-    def __init__(self, wid, torch, seed=0):
+    def __init__(self, wid, torch, seed=0, score_mode=None):
         from block_sparse_long_infllmv2_amd import binding as B
         from block_sparse_long_infllmv2_amd import pipeline as PL
         from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, Params, config
@@ -115,6 +115,8 @@ class Workload:
             self.case = config(wid, seed=seed)
             self.name = CONFIG_NAMES[wid]
         c = self.case
+        if score_mode is not None:
+            c.params = c.params.replace(score_mode=score_mode)
         p = c.params
         self.p = p
         bf = torch.bfloat16
@@ -369,6 +371,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--eager", action="store_true",
                     help="time steps as individual launches instead of HIP graph replays")
+    ap.add_argument("--score-mode", type=int, default=None, choices=[0, 1],
+                    help="group score reading: 0 summed query (default), 1 sum of "
+                         "per-head softmaxes over the visible windows")
     ap.add_argument("--warm-seconds", type=float, default=0.3,
                     help="untimed work after the warm-up steps and after graph capture, "
                          "so that timing starts at steady clocks")
@@ -392,7 +397,7 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": a.numel() * 4,
                           "bytes_written": b.numel() * 4, "launches": 3}))
         return
-    wl = Workload(args.workload, torch)
+    wl = Workload(args.workload, torch, score_mode=args.score_mode)
     print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -516,6 +521,7 @@ def main():
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": cfg, "roofline": roof, "launch": mode,
+           "score_mode": wl.p.score_mode,
            "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
            "eager_ms_per_step": round(wall_eager * 1e3 / args.steps, 4)}
     if w["bound"] == "mfma":

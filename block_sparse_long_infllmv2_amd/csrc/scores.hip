@@ -435,6 +435,171 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   }
 }
 
+// ---------------------------------------------------------------------------
+// score_mode 1: sigma[m] = sum over the group's heads of each head's softmax
+// over the windows visible to the row (the other plain reading of the group
+// score).  One workgroup (4 waves) per (row, KV head): a wave takes tiles of
+// 16 windows; on v_mfma_f32_16x16x32_bf16 the tile's logits for the group's
+// (up to 16) heads land as D[window][head] (lane (head j, group q) holds
+// windows 4q .. 4q+3 of the tile); float32 inputs compute the same logits
+// on the VALU in the same lane layout.
+//   pass 1: per head, the online max and sum of exp over the visible windows
+//           (log2 domain), merged over lanes and waves;
+//   pass 2: the logits again, each head's normalised share, summed over the
+//           16 head lanes into sig[m] (LDS, one float per visible window);
+// then every block takes the max of sig over its visible windows.
+// ---------------------------------------------------------------------------
+constexpr int kSoftmaxWaves = 4;
+constexpr int kSoftmaxMaxWindows = 16384;    // LDS: one float per visible window
+
+template <typename T, int D>
+__global__ __launch_bounds__(kSoftmaxWaves * 64) void block_scores_softmax_kernel(ScoreArgs a) {
+  __shared__ float sig[kSoftmaxMaxWindows];
+  __shared__ float st_m[kSoftmaxWaves][16], st_s[kSoftmaxWaves][16];
+  const int r = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int j = lane & 15, qg = lane >> 4;               // head, 4-window group
+  const int seq = a.row_seq ? a.row_seq[r] : 0;
+  if (seq < 0 || seq >= a.batch) return;
+  const int64_t L = a.seqlens[seq];
+  if (L < a.dense_len) return;
+  const int64_t pos = a.row_pos ? a.row_pos[r] : L - 1;
+  if (pos < 0 || pos >= L || pos > a.max_pos) return;
+  const int b_own = (int)(pos / a.B);
+  const int n_vis = pos >= a.ks - 1 ? (int)((pos - a.ks + 1) / a.s) + 1 : 0;
+  const int G = a.h_q / a.h_kv;
+  const bool head_ok = j < G;
+  const float c = a.scale * kLog2e;                      // logits in log2 units
+  const T* qrow = (const T*)a.q + ((int64_t)r * a.h_q + (int64_t)g * G + (head_ok ? j : 0)) * D;
+  const T* ckb = (const T*)a.ck + ((int64_t)seq * a.h_kv + g) * a.nc_cap * D;
+  const int n_tiles = (n_vis + 15) / 16;
+
+  // bf16: this lane's query slices (B operand: head j, dims 32 ks + 8 qg ..
+  // + 8); float32: the group's queries in LDS (each lane computes full dots)
+  constexpr int KS = D / 32;
+  bf16x8 qb[KS];
+  __shared__ __attribute__((aligned(16))) float qs[sizeof(T) == 2 ? 1 : 16][D];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (head_ok) w = ldg16(qrow + 32 * ks + 8 * qg);
+      qb[ks] = *reinterpret_cast<const bf16x8*>(&w);
+    }
+  } else {
+    const T* qg0 = (const T*)a.q + ((int64_t)r * a.h_q + (int64_t)g * G) * D;
+    for (int i = tid; i < 16 * D; i += kSoftmaxWaves * 64)
+      qs[i / D][i % D] = i / D < G ? Elem<T>::load(qg0 + i) : 0.0f;
+    __syncthreads();
+  }
+
+  // logits (log2 units) of tile t for head j at windows 16 t + 4 qg + e
+  auto tile_logits = [&](int t, float (&lg)[4]) {
+    const int w0 = 16 * t;
+    if constexpr (sizeof(T) == 2) {
+      const int wi = w0 + j;                             // A row of this lane: window w0 + j
+      const bool in = wi < n_vis;
+      const T* crow = ckb + (int64_t)(in ? wi : 0) * D + 8 * qg;
+      f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 w = ldg16(crow + 32 * ks);
+        if (!in) w = u32x4{0u, 0u, 0u, 0u};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(&w),
+                                                      qb[ks], acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lg[e] = acc[e] * c;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = w0 + 4 * qg + e;
+        const T* crow = ckb + (int64_t)(m < n_vis ? m : 0) * D;
+        float dot = 0.0f;
+#pragma unroll 4
+        for (int d = 0; d < D; d += 4) {
+          float x[4];
+          Elem<T>::unpack(ldg16(crow + d), x);
+          const f32x4 qv = *reinterpret_cast<const f32x4*>(&qs[j][d]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dot = __builtin_fmaf(qv[u], x[u], dot);
+        }
+        lg[e] = dot * c;
+      }
+    }
+  };
+
+  // pass 1: per head, running max and sum of 2^(logit - max)
+  float hm = -INFINITY, hs = 0.0f;
+  for (int t = wave; t < n_tiles; t += kSoftmaxWaves) {
+    float lg[4];
+    tile_logits(t, lg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * t + 4 * qg + e;
+      if (m < n_vis) {
+        const float nm = fmaxf(hm, lg[e]);
+        hs = hs * fast_exp2(hm - nm) + fast_exp2(lg[e] - nm);
+        hm = nm;
+      }
+    }
+  }
+  // merge the four lanes of head j (lanes j + 16 q), then the waves
+#pragma unroll
+  for (int o = 16; o <= 32; o <<= 1) {
+    const float om = __shfl_xor(hm, o, 64), os = __shfl_xor(hs, o, 64);
+    const float nm = fmaxf(hm, om);
+    hs = (hm == -INFINITY ? 0.0f : hs * fast_exp2(hm - nm)) +
+         (om == -INFINITY ? 0.0f : os * fast_exp2(om - nm));
+    hm = nm;
+  }
+  if (lane < 16) { st_m[wave][lane] = hm; st_s[wave][lane] = hs; }
+  __syncthreads();
+  float M = -INFINITY, S = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kSoftmaxWaves; ++w) {
+    const float om = st_m[w][j], os = st_s[w][j];
+    const float nm = fmaxf(M, om);
+    S = (M == -INFINITY ? 0.0f : S * fast_exp2(M - nm)) +
+        (om == -INFINITY ? 0.0f : os * fast_exp2(om - nm));
+    M = nm;
+  }
+  const float inv = S > 0.0f ? 1.0f / S : 0.0f;
+
+  // pass 2: each head's share, summed over the 16 head lanes
+  for (int t = wave; t < n_tiles; t += kSoftmaxWaves) {
+    float lg[4];
+    tile_logits(t, lg);
+    float sh[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 16 * t + 4 * qg + e;
+      float v = (head_ok && m < n_vis) ? fast_exp2(lg[e] - M) * inv : 0.0f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+      sh[e] = v;
+    }
+    if (j == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int m = 16 * t + 4 * qg + e;
+        if (m < n_vis) sig[m] = sh[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  // block b: max of sig over its visible windows (-inf if none)
+  float* out = a.scores + ((int64_t)r * a.h_kv + g) * a.nb_cap;
+  for (int b = tid; b <= b_own; b += kSoftmaxWaves * 64) {
+    const int64_t lo = first_window_of_block(b, a.B, a.ks, a.s);
+    const int64_t hi = min(last_window_of_block(b, a.B, a.s), (int64_t)n_vis - 1);
+    float v = -INFINITY;
+    for (int64_t m = lo; m <= hi; ++m) v = fmaxf(v, sig[m]);
+    out[b] = v;
+  }
+}
+
 template <typename T, int D>
 static int launch_scores(const ScoreArgs& a, int rows, hipStream_t st) {
   dim3 grid((unsigned)((int64_t)a.chunks_per_row * rows), a.h_kv, 1);
@@ -463,7 +628,11 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   if ((int64_t)max_pos / r.B + 1 > nb_cap) return INFLLMV2_ERR_INVALID_ARG;
   if (num_windows((int64_t)max_pos + 1, r.ks, r.s) > nc_cap) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(ck) || !aligned16(q)) return INFLLMV2_ERR_INVALID_ARG;
-  if (r.score_mode != 0) return INFLLMV2_ERR_UNSUPPORTED;
+  if (r.score_mode == 1) {
+    if (h_q / h_kv > 16) return INFLLMV2_ERR_UNSUPPORTED;
+    if (num_windows((int64_t)max_pos + 1, r.ks, r.s) > kSoftmaxMaxWindows)
+      return INFLLMV2_ERR_UNSUPPORTED;
+  }
   if (rows == 0) return INFLLMV2_OK;
   ScoreArgs a;
   a.q = q; a.row_seq = row_seq; a.row_pos = row_pos; a.ck = ck; a.seqlens = seqlens;
@@ -481,6 +650,25 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.chunks_per_row = (int)ceil_div(nb_launch, bpw);
   if ((int64_t)a.chunks_per_row * rows >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
+  if (r.score_mode == 1) {
+    dim3 grid((unsigned)rows, (unsigned)h_kv);
+    if (dtype == INFLLMV2_BF16) {
+      if (d == 128)
+        hipLaunchKernelGGL((block_scores_softmax_kernel<uint16_t, 128>), grid,
+                           dim3(kSoftmaxWaves * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL((block_scores_softmax_kernel<uint16_t, 64>), grid,
+                           dim3(kSoftmaxWaves * 64), 0, st, a);
+    } else {
+      if (d == 128)
+        hipLaunchKernelGGL((block_scores_softmax_kernel<float, 128>), grid,
+                           dim3(kSoftmaxWaves * 64), 0, st, a);
+      else
+        hipLaunchKernelGGL((block_scores_softmax_kernel<float, 64>), grid,
+                           dim3(kSoftmaxWaves * 64), 0, st, a);
+    }
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   const bool mfma_geometry = r.ks == 2 * r.s && (r.B == 4 * r.s || r.B == 8 * r.s);
   if (dtype == INFLLMV2_BF16 && batch == 1 && row_seq == nullptr && mfma_geometry &&
       rows >= kMfmaMinRows) {
