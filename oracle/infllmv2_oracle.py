@@ -64,7 +64,7 @@ __all__ = [
     "bf16_round", "store_round", "num_windows", "compress_keys",
     "windows_of_block", "kernel_scores", "block_scores", "select_blocks",
     "attend", "attend_selected", "dense_attend", "forced_blocks", "prefill",
-    "decode", "tree_verify",
+    "decode", "tree_verify", "attend_backward", "prefill_backward",
 ]
 
 
@@ -280,6 +280,64 @@ def attend_selected(q_row, k, v, sel, pos, params, extra=None):
             vals = np.concatenate([vals, np.asarray(extra[1][g], np.float64)], axis=0)
         o[h], lse[h] = attend(q_row[h], keys, vals, scale)
     return o, lse
+
+
+# --------------------------------------------------------------------------
+# Step 7 (training): gradients through the kept keys, the selection fixed
+# (top-k is not differentiable; "trainable" sparse attention trains the
+# attention over the blocks it keeps)
+# --------------------------------------------------------------------------
+def attend_backward(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float,
+                    d_o: np.ndarray):
+    """Gradients of o = softmax(scale * keys @ q) @ values with respect to
+    q, keys and values, given d_o = dL/do.  q, d_o: [d]; keys/values: [n][d].
+    Returns (dq [d], dkeys [n][d], dvalues [n][d])."""
+    q = np.asarray(q, np.float64)
+    keys = np.asarray(keys, np.float64)
+    values = np.asarray(values, np.float64)
+    d_o = np.asarray(d_o, np.float64)
+    logits = scale * (keys @ q)
+    p = np.exp(logits - logits.max())
+    p /= p.sum()                                   # attention weights
+    o = p @ values
+    dvalues = np.outer(p, d_o)                     # o = sum_j p_j v_j
+    dp = values @ d_o                              # dL/dp_j = v_j . d_o
+    ds = p * (dp - d_o @ o)                        # through the softmax
+    dq = scale * (ds @ keys)
+    dkeys = scale * np.outer(ds, q)
+    return dq, dkeys, dvalues
+
+
+def prefill_backward(q, k, v, sel_rows, params, d_out):
+    """Gradients of the prefill attention (queries = the last n_q positions
+    of n_k keys) with each row's kept blocks fixed: sel_rows[i][g] are row
+    i's kept blocks for KV head g, or sel_rows[i] is None for a dense row
+    (every key up to its position).  q, d_out: [n_q][h_q][d]; k, v:
+    [h_kv][n_k][d].  Returns (dq [n_q][h_q][d], dk, dv [h_kv][n_k][d]);
+    dk / dv sum the contributions of every row that attends a key."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    d_out = np.asarray(d_out, np.float64)
+    n_q, h_q, d = q.shape
+    h_kv, n_k, _ = k.shape
+    scale = _scale(params, d)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for i in range(n_q):
+        pos = n_k - n_q + i
+        for h in range(h_q):
+            g = _group_of_head(h, h_q, h_kv)
+            if sel_rows[i] is None:
+                toks = np.arange(pos + 1)
+            else:
+                toks = _block_tokens(sel_rows[i][g], pos, params.block_size)
+            gq, gk, gv = attend_backward(q[i, h], k[g, toks], v[g, toks], scale, d_out[i, h])
+            dq[i, h] = gq
+            dk[g, toks] += gk
+            dv[g, toks] += gv
+    return dq, dk, dv
 
 
 def _sparse_row(q_row, k, v, ck, pos, params, extra=None):

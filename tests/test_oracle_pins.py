@@ -435,3 +435,97 @@ def test_tree_non_ancestor_drafts_do_not_matter_and_self_only():
         assert list(r3["sel"][i][0]) == list(r["sel"][i][0])
     np.testing.assert_array_equal(r3["o"][0], r["o"][0])  # root: same keys
     assert np.abs(r3["o"][3] - r["o"][3]).max() > 1e-6
+
+
+# ----------------------------------------------------- backward (training) ----
+def _torch_selected_grads(q, k, v, sel_rows, p, d_out):
+    """torch autograd (float64) of the same attention, row by row."""
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(k, dtype=torch.float64, requires_grad=True)
+    vt = torch.tensor(v, dtype=torch.float64, requires_grad=True)
+    n_q, h_q, d = q.shape
+    h_kv, n_k, _ = k.shape
+    scale = 1.0 / math.sqrt(d)
+    loss = 0.0
+    for i in range(n_q):
+        pos = n_k - n_q + i
+        for h in range(h_q):
+            g = h * h_kv // h_q
+            if sel_rows[i] is None:
+                toks = list(range(pos + 1))
+            else:
+                toks = [t for b in sel_rows[i][g] for t in range(b * p.block_size,
+                                                                 (b + 1) * p.block_size)
+                        if t <= pos]
+            idx = torch.tensor(toks)
+            w = torch.softmax(scale * (kt[g, idx] @ qt[i, h]), dim=0)
+            o = w @ vt[g, idx]
+            loss = loss + (o * torch.tensor(d_out[i, h])).sum()
+    loss.backward()
+    return qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy()
+
+
+def test_prefill_backward_matches_torch_autograd():
+    rng = np.random.default_rng(21)
+    p = Params(block_size=16, topk=3, init_blocks=1, local_blocks=1)
+    n_k, n_q, h_q, h_kv, d = 90, 40, 4, 2, 8
+    q = rng.standard_normal((n_q, h_q, d))
+    k = rng.standard_normal((h_kv, n_k, d))
+    v = rng.standard_normal((h_kv, n_k, d))
+    d_out = rng.standard_normal((n_q, h_q, d))
+    sel_rows = []
+    for i in range(n_q):
+        pos = n_k - n_q + i
+        own = pos // p.block_size
+        if i % 7 == 0:
+            sel_rows.append(None)                 # a dense row
+        else:
+            cand = [b for b in range(1, own)]
+            pick = sorted(rng.choice(cand, size=min(1, len(cand)), replace=False).tolist())
+            sel_rows.append([sorted({0, own} | set(pick)) for _ in range(h_kv)])
+    dq, dk, dv = O.prefill_backward(q, k, v, sel_rows, p, d_out)
+    tq, tk, tv = _torch_selected_grads(q, k, v, sel_rows, p, d_out)
+    np.testing.assert_allclose(dq, tq, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, tk, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, tv, rtol=1e-10, atol=1e-12)
+
+
+def test_attend_backward_finite_differences():
+    rng = np.random.default_rng(22)
+    n, d, scale = 7, 5, 0.6
+    q, keys, vals, d_o = (rng.standard_normal(d), rng.standard_normal((n, d)),
+                          rng.standard_normal((n, d)), rng.standard_normal(d))
+    dq, dk, dv = O.attend_backward(q, keys, vals, scale, d_o)
+
+    def loss(q_, k_, v_):
+        return float(O.attend(q_, k_, v_, scale)[0] @ d_o)
+
+    eps = 1e-6
+    for arr, grad, which in ((q, dq, 0), (keys, dk, 1), (vals, dv, 2)):
+        num = np.zeros_like(arr)
+        for ix in np.ndindex(arr.shape):
+            plus, minus = arr.copy(), arr.copy()
+            plus[ix] += eps
+            minus[ix] -= eps
+            args_p = [q, keys, vals]
+            args_m = [q, keys, vals]
+            args_p[which], args_m[which] = plus, minus
+            num[ix] = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=1e-6, atol=1e-8)
+
+
+def test_prefill_backward_dense_equals_sdpa_backward():
+    # every row dense: the gradients of causal scaled-dot-product attention
+    rng = np.random.default_rng(23)
+    n, h, d = 24, 2, 8
+    q, k, v, d_out = (rng.standard_normal((n, h, d)), rng.standard_normal((h, n, d)),
+                      rng.standard_normal((h, n, d)), rng.standard_normal((n, h, d)))
+    dq, dk, dv = O.prefill_backward(q, k, v, [None] * n, Params(), d_out)
+    qt = torch.tensor(q.transpose(1, 0, 2), requires_grad=True)     # [h][n][d]
+    kt = torch.tensor(k, requires_grad=True)
+    vt = torch.tensor(v, requires_grad=True)
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    (o * torch.tensor(d_out.transpose(1, 0, 2))).sum().backward()
+    np.testing.assert_allclose(dq, qt.grad.numpy().transpose(1, 0, 2), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dk, kt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dv, vt.grad.numpy(), rtol=1e-10, atol=1e-12)
