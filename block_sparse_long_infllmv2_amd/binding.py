@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("INFLLMV2_LIB") or os.path.join(_HERE, "libinfllmv2.so")
 
 F32, BF16 = 0, 1
-OP_DECODE, OP_TREE = 0, 1
+OP_DECODE, OP_TREE, OP_PREFILL_BWD = 0, 1, 2
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing, misaligned or too small", 4: "HIP launch failed"}
 
@@ -60,6 +60,10 @@ def _load():
                                                        i32, i32, i32, P, P, P, P, sz, PP, P]),
         "infllmv2_tree_verify": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P,
                                                 i32, i32, i32, P, P, P, P, sz, PP, P]),
+        "infllmv2_sparse_attn_prefill_backward": (ctypes.c_int, [ctypes.c_int, P, i32, P, P,
+                                                                 i64, i64, i32, i32, i32, P,
+                                                                 P, P, P, P, P, P, P, sz, PP,
+                                                                 P]),
         "infllmv2_workspace_size": (sz, [ctypes.c_int, i32, i32, i32, i32, i64, PP]),
     }
     for name, (res, args) in sigs.items():
@@ -209,3 +213,20 @@ def infllmv2_tree_verify(q, k_cache, v_cache, n_ctx, k_draft, v_draft, tree_mask
                                     _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     ctypes.byref(p), _stream()),
            "infllmv2_tree_verify")
+
+
+def infllmv2_sparse_attn_prefill_backward(q, k_cache, v_cache, n_k, block_idx, out, lse, d_out,
+                                          dq, dk, dv, ws, params):
+    """Gradients of the prefill attention, kept blocks fixed.  q, out, d_out,
+    dq [n_q][h_q][d] (bf16); k/v [h_kv][cap][d]; lse float32 [n_q][h_q];
+    dk, dv float32 [h_kv][cap][d] are accumulated into; ws: uint8 workspace."""
+    n_q, h_q, d = q.shape
+    h_kv, cap, _ = k_cache.shape
+    p = to_params(params)
+    if dk.dtype != torch.float32 or dv.dtype != torch.float32:
+        raise TypeError("dk and dv must be float32")
+    _check(LIB.infllmv2_sparse_attn_prefill_backward(
+        _dt(q), _ptr(q), n_q, _ptr(k_cache), _ptr(v_cache), cap, int(n_k), h_q, h_kv, d,
+        _i32(block_idx, "block_idx"), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), ctypes.byref(p), _stream()),
+        "infllmv2_sparse_attn_prefill_backward")

@@ -6,6 +6,7 @@ size_t tree_workspace_bytes(int n_draft, int h_q, int h_kv, int d, int64_t n_ctx
                             const Resolved& r);
 size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_seqlen,
                               const Resolved& r);
+size_t prefill_bwd_workspace_bytes(int n_q, int h_q, int h_kv, int64_t n_k, const Resolved& r);
 }  // namespace infllmv2
 
 using namespace infllmv2;
@@ -37,7 +38,7 @@ extern "C" const char* infllmv2_status_string(int status) {
   return "unknown status";
 }
 
-extern "C" int infllmv2_version(void) { return 100; }
+extern "C" int infllmv2_version(void) { return 101; }
 
 extern "C" size_t infllmv2_workspace_size(int op, int32_t n, int32_t h_q, int32_t h_kv,
                                           int32_t d, int64_t max_len,
@@ -50,6 +51,10 @@ extern "C" size_t infllmv2_workspace_size(int op, int32_t n, int32_t h_q, int32_
   if (op == INFLLMV2_OP_TREE) {
     if (n > 64) return 0;
     return tree_workspace_bytes(n, h_q, h_kv, d, max_len, r);
+  }
+  if (op == INFLLMV2_OP_PREFILL_BWD) {
+    if (max_len > INT32_MAX || n > max_len) return 0;
+    return prefill_bwd_workspace_bytes(n, h_q, h_kv, max_len, r);
   }
   return 0;
 }

@@ -1,0 +1,736 @@
+// Gradients of the block-sparse prefill attention with the kept blocks fixed
+// (block selection is a top-k and has no gradient), bf16 inputs, float32
+// accumulation, on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
+// Sources: "MiniCPM 4.0" blog (shadowrocket9.top), InfLLM v2 section (the
+// sparse attention is trainable: the model is trained with it); "MiniCPM4:
+// running LLMs on phones and PCs" (xugj520.cn), section 1.1 (attention over
+// the selected blocks only).  For one (query row, head) with weights
+// p = softmax(scale * K q) over its kept keys and output o = p V, given the
+// upstream gradient do:
+//   dV_j += p_j do                  dP_j = do . v_j
+//   dS_j  = p_j (dP_j - do . o)     dq = scale * sum_j dS_j k_j
+//   dK_j += scale * dS_j q
+// The backward recomputes p from the forward's log-sum-exp, so nothing of
+// size keys x rows is stored.
+//
+// Kernels (in launch order):
+//   bwd_dsum    dsum[row][h] = do . o (float32), one per (row, head)
+//   fill        clears the row bitmap (sparse chunks only)
+//   bwd_mark    bitmap[g][b] bit i set when row i kept block b for KV head g
+//   bwd_count   per (g, block): segments of at most kSegPairs (row, head)
+//               pairs, so that block 0, which every row keeps, is spread over
+//               many workgroups
+//   bwd_plan    one workgroup scans the segment counts into a list of work
+//               items (KV head, 64-key chunk, segment)
+//   bwd_dkdv    key-major: a workgroup of two waves owns one item; each wave
+//               holds 32 keys of K and V as MFMA operands and their dK^T, dV^T
+//               accumulators in registers, and walks the segment's rows 32
+//               (row, head) pairs at a time through an LDS double buffer:
+//                 S = Q K^T, dP = dO V^T            (pairs x keys)
+//                 P = exp(scale S - lse), dS = P (dP - dsum)
+//                 dV^T += dO^T P, dK^T += Q^T dS    (reduction over pairs)
+//               The two products over pairs take P and dS straight from the
+//               accumulator registers (element e of the B operand is pair
+//               4h+e or 16+4h+e-4, the order of lane h's accumulator rows;
+//               the A operands dO^T and Q^T are read in the same order with
+//               transposing LDS reads).  Results are added to float32 dK, dV
+//               with atomics, since several segments may share a chunk.
+//   bwd_dq      query-major, like the forward kernel: a workgroup owns the
+//               (row, head) pairs of a tile of tokens and one KV head, walks
+//               the union of the tokens' kept blocks (K and V tiles staged in
+//               LDS by direct loads), and per 64-key chunk computes
+//               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+#include "lds_tiles.h"
+
+namespace infllmv2 {
+
+struct BwdArgs {
+  const uint16_t* q;          // [n_q][h_q][D]
+  const uint16_t* k;          // [h_kv][cap][D]
+  const uint16_t* v;
+  const int32_t* block_idx;   // [n_q][h_kv][topk], NULL when dense
+  const uint16_t* out;        // forward output [n_q][h_q][D]
+  const float* lse;           // forward log-sum-exp [n_q][h_q] (natural log)
+  const uint16_t* d_out;      // upstream gradient [n_q][h_q][D]
+  uint16_t* dq;               // [n_q][h_q][D]
+  float* dk;                  // [h_kv][cap][D], accumulated
+  float* dv;
+  float* dsum;                // workspace [n_q][h_q]
+  uint32_t* bitmap;           // workspace [h_kv][n_b][nw]
+  int32_t* nseg;              // workspace [h_kv][n_b]
+  int2* items;                // workspace [max_items]: (g * n_chunks + chunk, segment)
+  int32_t* n_items;           // workspace [1]
+  int64_t cap, n_k;
+  int n_q, h_q, h_kv, topk, B, n_b, nw, n_chunks, seg_rows, max_items, n_tiles;
+  int dense;
+  float scale, scale_log2;
+};
+
+// (row, head) pairs per dK/dV work item: bounds a workgroup's work
+constexpr int kSegPairs = 2048;
+constexpr int kPlanThreads1 = 1024;
+
+// ---------------------------------------------------------------------------
+// dsum[row][h] = sum_d do[row][h][d] * o[row][h][d]; D/8 lanes per pair.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
+  constexpr int L = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pair = gid / L;
+  const int part = (int)(gid % L);
+  const int64_t n_pairs = (int64_t)a.n_q * a.h_q;
+  float acc = 0.0f;
+  if (pair < n_pairs) {
+    float x[8], y[8];
+    Elem<uint16_t>::unpack(ldg16(a.d_out + pair * D + 8 * part), x);
+    Elem<uint16_t>::unpack(ldg16(a.out + pair * D + 8 * part), y);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(x[i], y[i], acc);
+  }
+#pragma unroll
+  for (int o = L / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if (pair < n_pairs && part == 0) a.dsum[pair] = acc;
+}
+
+__global__ __launch_bounds__(256) void bwd_fill_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = 0u;
+}
+
+// bit (row % 32) of bitmap[g][b][row / 32] <- row kept block b for KV head g
+__global__ __launch_bounds__(256) void bwd_mark_kernel(BwdArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.n_q * a.h_kv * a.topk;
+  if (gid >= total) return;
+  const int row = (int)(gid / ((int64_t)a.h_kv * a.topk));
+  const int g = (int)((gid / a.topk) % a.h_kv);
+  const int32_t b = a.block_idx[gid];
+  if (b < 0 || b >= a.n_b) return;
+  atomicOr(a.bitmap + ((int64_t)g * a.n_b + b) * a.nw + (row >> 5), 1u << (row & 31));
+}
+
+// one wave per (g, block): rows that kept it -> segments of seg_rows rows
+__global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= a.h_kv * a.n_b) return;
+  const uint32_t* w = a.bitmap + (int64_t)e * a.nw;
+  int c = 0;
+  for (int i = lane; i < a.nw; i += 64) c += __popc(w[i]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+  if (lane == 0) a.nseg[e] = (c + a.seg_rows - 1) / a.seg_rows;
+}
+
+__device__ __forceinline__ int dense_first_row(const BwdArgs& a, int chunk) {
+  // rows at positions >= the chunk's first key: row i sits at n_k - n_q + i
+  const int64_t r0 = (int64_t)chunk * kChunk - (a.n_k - a.n_q);
+  return r0 < 0 ? 0 : (int)(r0 < a.n_q ? r0 : a.n_q);
+}
+
+// One workgroup: exclusive scan of the per-unit item counts, items written in
+// (KV head, chunk, segment) order.
+__global__ __launch_bounds__(kPlanThreads1) void bwd_plan_kernel(BwdArgs a) {
+  __shared__ int scan_lds[kPlanThreads1 / 64];
+  const int tid = threadIdx.x;
+  const int cpb = a.B / kChunk;
+  const int units = a.dense ? a.n_chunks : a.n_b;
+  const int total_e = a.h_kv * units;
+  int carry = 0;
+  for (int base = 0; base < total_e; base += kPlanThreads1) {
+    const int e = base + tid;
+    int nseg = 0, nch = 0, c0 = 0, g = 0;
+    if (e < total_e) {
+      g = e / units;
+      const int u = e % units;
+      if (a.dense) {
+        const int cnt = a.n_q - dense_first_row(a, u);
+        nseg = (cnt + a.seg_rows - 1) / a.seg_rows;
+        nch = 1;
+        c0 = u;
+      } else {
+        nseg = a.nseg[e];
+        c0 = u * cpb;
+        nch = min(cpb, a.n_chunks - c0);
+      }
+    }
+    const int cnt_items = nseg * nch;
+    int tot;
+    const int off = carry + block_excl_scan<kPlanThreads1>(cnt_items, &tot, scan_lds);
+    for (int i = 0; i < cnt_items; ++i) {
+      if (off + i >= a.max_items) break;
+      a.items[off + i] = make_int2(g * a.n_chunks + c0 + i / nseg, i % nseg);
+    }
+    carry += tot;
+  }
+  if (tid == 0) a.n_items[0] = min(carry, a.max_items);
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV, key-major.  Tiles of 32 (row, head) pairs of the item's segment
+// are staged as [pair][d] rows with the chunk swizzle of Swz16V (16-byte row
+// reads and transposing reads both free of bank conflicts).
+// ---------------------------------------------------------------------------
+template <int D>
+struct PairTile {
+  static constexpr int RB = 2 * D;                  // bytes per pair row
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int BYTES = 32 * RB;             // one tensor (Q or dO)
+  __device__ static __forceinline__ int f(int r) { return Swz16V<D>::f(r); }
+  // byte offset of logical chunk c of pair row r
+  __device__ static __forceinline__ uint32_t at(int r, int c) {
+    return (uint32_t)(r * RB + ((c ^ f(r)) * 16));
+  }
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
+void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int NT = 128;
+  constexpr int NKS = D / 32, NDT = D / 16;
+  constexpr int SEG_ROWS = (kSegPairs / G) > 0 ? kSegPairs / G : 1;
+  constexpr int SLOTS = 2 * 32 * (D / 8);            // 16-byte pieces of Q and dO per tile
+  constexpr int PER = SLOTS / NT;
+  using PT = PairTile<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2 * PT::BYTES];   // [buf][Q | dO]
+  __shared__ float m_lse[2][32], m_dsum[2][32];
+  __shared__ int m_pos[2][32];
+  __shared__ int rows_lds[SEG_ROWS];
+  __shared__ int scan_lds[NT / 64];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if ((int)blockIdx.x >= a.n_items[0]) return;
+  const int2 item = a.items[blockIdx.x];
+  const int g = item.x / a.n_chunks, chunk = item.x % a.n_chunks, seg = item.y;
+  const int key0 = chunk * kChunk;
+
+  // ---- the segment's rows, ascending, into rows_lds
+  int n_rows;
+  if (a.dense) {
+    const int r0 = dense_first_row(a, chunk) + seg * SEG_ROWS;
+    n_rows = min(SEG_ROWS, a.n_q - r0);
+    for (int i = tid; i < n_rows; i += NT) rows_lds[i] = r0 + i;
+  } else {
+    const int b = key0 / a.B;
+    const uint32_t* words = a.bitmap + ((int64_t)g * a.n_b + b) * a.nw;
+    const int per = (a.nw + NT - 1) / NT;
+    const int w0 = tid * per, w1 = min(w0 + per, a.nw);
+    int c = 0;
+    for (int w = w0; w < w1; ++w) c += __popc(words[w]);
+    int total;
+    const int base = block_excl_scan<NT>(c, &total, scan_lds);
+    const int lo = seg * SEG_ROWS, hi = min(lo + SEG_ROWS, total);
+    if (base < hi && base + c > lo) {
+      int r = base;
+      for (int w = w0; w < w1 && r < hi; ++w) {
+        uint32_t m = words[w];
+        while (m) {
+          const int bit = __builtin_ctz(m);
+          m &= m - 1u;
+          if (r >= lo && r < hi) rows_lds[r - lo] = w * 32 + bit;
+          ++r;
+        }
+      }
+    }
+    n_rows = max(0, hi - lo);
+  }
+  __syncthreads();
+  const int n_pairs = n_rows * G;
+  const int n_tiles = (n_pairs + 31) / 32;
+  if (n_tiles <= 0) return;
+
+  // ---- this wave's 32 keys of K and V as B operands (key j of tile kt in
+  // lane column j, dims 32 ks + 8 h .. +8); keys past n_k repeat the last key
+  const int jj = lane & 15, hh = lane >> 4;
+  const int kw0 = key0 + 32 * wave;
+  bf16x8 kf[2][NKS], vf[2][NKS];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = min(kw0 + 16 * kt + jj, (int)a.n_k - 1);
+    const uint16_t* kr = a.k + ((int64_t)g * a.cap + key) * D + 8 * hh;
+    const uint16_t* vr = a.v + ((int64_t)g * a.cap + key) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      u32x4 wk = ldg16(kr + 32 * ks), wv = ldg16(vr + 32 * ks);
+      kf[kt][ks] = *reinterpret_cast<const bf16x8*>(&wk);
+      vf[kt][ks] = *reinterpret_cast<const bf16x8*>(&wv);
+    }
+  }
+  f32x4 dk[2][NDT], dv[2][NDT];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      dk[kt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      dv[kt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+  // ---- tile staging through registers: slot s -> tensor s / (32 CPR),
+  // pair (s / CPR) % 32, chunk s % CPR
+  const int64_t qoff = (int64_t)a.n_k - a.n_q;
+  u32x4 pre[PER];
+  float pre_lse = 0.0f, pre_dsum = 0.0f;
+  int pre_pos = -1;
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int s = i * NT + tid;
+      const int tensor = s / (32 * PT::CPR);
+      const int pr = (s / PT::CPR) % 32, c = s % PT::CPR;
+      const int p = t * 32 + pr;
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (p < n_pairs) {
+        const int row = rows_lds[p / G], head = g * G + p % G;
+        const uint16_t* src = (tensor == 0 ? a.q : a.d_out) + ((int64_t)row * a.h_q + head) * D;
+        w = ldg16(src + 8 * c);
+      }
+      pre[i] = w;
+    }
+    if (tid < 32) {
+      const int p = t * 32 + tid;
+      pre_lse = INFINITY;
+      pre_dsum = 0.0f;
+      pre_pos = -1;
+      if (p < n_pairs) {
+        const int row = rows_lds[p / G], head = g * G + p % G;
+        const int64_t ph = (int64_t)row * a.h_q + head;
+        pre_lse = a.lse[ph] * kLog2e;
+        pre_dsum = a.dsum[ph];
+        pre_pos = (int)(qoff + row);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int s = i * NT + tid;
+      const int tensor = s / (32 * PT::CPR);
+      const int pr = (s / PT::CPR) % 32, c = s % PT::CPR;
+      *reinterpret_cast<u32x4*>(&tiles[buf][tensor * PT::BYTES + PT::at(pr, c)]) = pre[i];
+    }
+    if (tid < 32) {
+      m_lse[buf][tid] = pre_lse;
+      m_dsum[buf][tid] = pre_dsum;
+      m_pos[buf][tid] = pre_pos;
+    }
+  };
+
+  const uint32_t lds_tiles0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tiles;
+  // 16-byte row reads: lane (jj, hh) reads pair row 16 pt + jj, logical chunk 4 ks + hh
+  // transposing reads (d-tile dt, half c): pair row 16 c + 4 hh + jj / 4, d 16 dt + 4 (jj % 4)
+  const int tr_row = 4 * hh + (jj >> 2), tr_q = jj & 3;
+  const int key_lane[2] = {kw0 + jj, kw0 + 16 + jj};
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < n_tiles) load_tile(t + 1);
+    const uint32_t qb = lds_tiles0 + (uint32_t)(buf * 2 * PT::BYTES);
+    const uint32_t ob = qb + (uint32_t)PT::BYTES;
+    // S = Q K^T and dP = dO V^T: [pair tile pt][key tile kt]
+    f32x4 s[2][2], dp[2][2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[pt][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        dp[pt][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const bf16x8 aq = lds_read16(qb + PT::at(16 * pt + jj, 4 * ks + hh));
+        const bf16x8 ao = lds_read16(ob + PT::at(16 * pt + jj, 4 * ks + hh));
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          s[pt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kt][ks], s[pt][kt], 0, 0, 0);
+          dp[pt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kt][ks], dp[pt][kt], 0, 0, 0);
+        }
+      }
+    // P and dS; lane (jj, hh) holds pairs 16 pt + 4 hh + r of key 16 kt + jj
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int pr = 16 * pt + 4 * hh + r;
+        const float l2 = m_lse[buf][pr], ds = m_dsum[buf][pr];
+        const int pos = m_pos[buf][pr];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const float p = key_lane[kt] <= pos
+                              ? fast_exp2(__builtin_fmaf(s[pt][kt][r], a.scale_log2, -l2))
+                              : 0.0f;
+          pb[kt][4 * pt + r] = (__bf16)p;
+          sb[kt][4 * pt + r] = (__bf16)(p * (dp[pt][kt][r] - ds));
+        }
+      }
+    // dV^T += dO^T P, dK^T += Q^T dS: A rows d of d-tile dt, reduction over
+    // pairs in the order 4 hh + e (e < 4), 16 + 4 hh + e - 4 (e >= 4)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const uint32_t lo = PT::at(tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
+      const uint32_t hi = PT::at(16 + tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
+      const bf16x4 o0 = lds_read_tr8(ob + lo), o1 = lds_read_tr8(ob + hi);
+      const bf16x4 q0 = lds_read_tr8(qb + lo), q1 = lds_read_tr8(qb + hi);
+      const bf16x8 aot = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const bf16x8 aqt = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        dv[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aot, pb[kt], dv[kt][dt], 0, 0, 0);
+        dk[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqt, sb[kt], dk[kt][dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < n_tiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- accumulate: lane (jj, hh) holds key 16 kt + jj, d = 16 dt + 4 hh + r
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int key = key_lane[kt];
+    if (key >= a.n_k) continue;
+    float* dkr = a.dk + ((int64_t)g * a.cap + key) * D + 4 * hh;
+    float* dvr = a.dv + ((int64_t)g * a.cap + key) * D + 4 * hh;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        unsafeAtomicAdd(dkr + 16 * dt + r, a.scale * dk[kt][dt][r]);
+        unsafeAtomicAdd(dvr + 16 * dt + r, dv[kt][dt][r]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dQ, query-major.  W waves of 16 (row, head) pairs: pair p of the workgroup
+// is token p / G, head p % G of KV group g.  K and V tiles (Swz16V chunk
+// swizzle) serve 16-byte row reads (S^T and dP^T) and, for K, transposing
+// reads (dQ^T = K^T dS^T).
+// ---------------------------------------------------------------------------
+template <int D, int G, int W>
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dq_kernel(BwdArgs a) {
+  constexpr int NT = W * 64;
+  constexpr int TT = (16 * W) / G;                 // tokens per workgroup
+  static_assert(TT >= 1 && TT <= 32, "token bitmask is 32 bits");
+  constexpr int NKS = D / 32, NDT = D / 16;
+  constexpr int TILE = Swz16V<D>::TILE;
+  constexpr int RB = Swz16V<D>::RB;
+  constexpr int SORT_N = TT * kSortCap;
+  __shared__ __attribute__((aligned(16))) uint16_t stage[2 * 2 * TILE / 2];   // K[2] V[2]
+  __shared__ int2 ents[TT * kSortCap];
+  __shared__ int scan_lds[NT / 64];
+  static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wi = xcd_contiguous_index(blockIdx.x, gridDim.x);
+  const int g = wi / a.n_tiles, tile = wi % a.n_tiles;
+  const int n_keys = (int)a.n_k;
+  const int tok0 = tile * TT;
+  const int n_tok = min(TT, a.n_q - tok0);
+  const bool dense = a.dense != 0;
+  const int cpb = a.B / kChunk;
+  const uint32_t full_mask = n_tok >= 32 ? 0xffffffffu : ((1u << n_tok) - 1u);
+  const int p0 = (int)(a.n_k - a.n_q) + tok0;
+
+  int n_entries;
+  if (dense) {
+    n_entries = (p0 + n_tok - 1) / a.B + 1;
+  } else {
+    int N = 1;
+    while (N < TT * a.topk) N <<= 1;
+    n_entries = build_union<NT, TT>(a.block_idx, tok0, a.h_kv, g, n_tok, a.topk, a.n_b,
+                                    reinterpret_cast<uint32_t*>(stage), N, ents, scan_lds);
+  }
+  const int n = __builtin_amdgcn_readfirstlane(n_entries * cpb);
+
+  struct Unit { int key0, nv; uint32_t tm; };
+  auto unit_of = [&](int u) -> Unit {
+    Unit r = {0, 0, 0u};
+    if (u >= n) return r;
+    const int e = u / cpb, c = u - e * cpb;
+    int b;
+    if (dense) {
+      b = e;
+      const int t_min = b * a.B - p0;
+      r.tm = t_min <= 0 ? full_mask : (t_min >= 32 ? 0u : (full_mask & (0xffffffffu << t_min)));
+    } else {
+      const int2 en = ents[e];
+      b = en.x;
+      r.tm = (uint32_t)en.y;
+    }
+    r.key0 = b * a.B + c * kChunk;
+    r.nv = max(0, min(kChunk, min((b + 1) * a.B, n_keys) - r.key0));
+    return r;
+  };
+
+  // this lane's pair: column jj of the wave's 16
+  const int jj = lane & 15, hh = lane >> 4;
+  const int pw = 16 * wave + jj;
+  const int my_t = pw / G, my_head = g * G + pw % G;
+  const bool my_ok = my_t < n_tok;
+  const int my_row = tok0 + (my_ok ? my_t : 0);
+  const int64_t ph = (int64_t)my_row * a.h_q + my_head;
+  bf16x8 qf[NKS], of[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    u32x4 wq = {0u, 0u, 0u, 0u}, wo = {0u, 0u, 0u, 0u};
+    if (my_ok) {
+      wq = ldg16(a.q + ph * D + 32 * ks + 8 * hh);
+      wo = ldg16(a.d_out + ph * D + 32 * ks + 8 * hh);
+    }
+    qf[ks] = *reinterpret_cast<const bf16x8*>(&wq);
+    of[ks] = *reinterpret_cast<const bf16x8*>(&wo);
+  }
+  const float my_l2 = my_ok ? a.lse[ph] * kLog2e : INFINITY;
+  const float my_ds = my_ok ? a.dsum[ph] : 0.0f;
+  f32x4 dq[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) dq[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // the wave's tokens: a unit is skipped unless one of them kept it
+  const int wt0 = (16 * wave) / G, wt1 = (16 * wave + 15) / G;
+  const uint32_t wave_tok_mask =
+      wt0 >= 32 ? 0u : (((wt1 - wt0 + 1) >= 32 ? 0xffffffffu : ((1u << (wt1 - wt0 + 1)) - 1u)) << wt0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+
+  using DT = DmaTile<D, NT, Swz16V<D>>;
+  constexpr int KL = DT::kLoads;
+  DT dma;
+  dma.init(tid);
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
+  const uint16_t* kseq = a.k + (int64_t)g * a.cap * D;
+  const uint16_t* vseq = a.v + (int64_t)g * a.cap * D;
+  // K of slot s at lds0 + s TILE, V at lds0 + (2 + s) TILE
+  auto issue = [&](const Unit& un, int slot) {
+    const int64_t off = un.nv > 0 ? (int64_t)un.key0 * D : 0;
+    dma.issue(lds0 + slot * TILE, kseq + off, un.nv, tid, wave_u);
+    dma.issue(lds0 + (2 + slot) * TILE, vseq + off, un.nv, tid, wave_u);
+  };
+  // fragment addresses (Swz16V): 16-byte reads, row 16 kt + jj, chunk 4 ks + hh
+  auto row_addr = [&](int r, int c) -> uint32_t {
+    return (uint32_t)(r * RB + ((c ^ Swz16V<D>::f(r)) * 16));
+  };
+  const int tr_row = 4 * hh + (jj >> 2), tr_q = jj & 3;
+
+  Unit cur = unit_of(0);
+  if (n > 0) issue(cur, 0);
+  for (int i = 0; i < n; ++i) {
+    const int slot = i & 1;
+    wait_vm_barrier<0>();
+    const Unit nxt = unit_of(i + 1);
+    if (i + 1 < n) issue(nxt, slot ^ 1);
+    if (cur.tm & wave_tok_mask) {
+      const uint32_t kb = lds0 + slot * TILE, vb = lds0 + (2 + slot) * TILE;
+      int lim = -1;
+      if (my_ok && ((cur.tm >> my_t) & 1u)) lim = min(p0 + my_t - cur.key0, cur.nv - 1);
+      f32x4 s[4], dp[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        s[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        dp[kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          const uint32_t ra = row_addr(16 * kt + jj, 4 * ks + hh);
+          s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(kb + ra), qf[ks], s[kt], 0, 0, 0);
+          dp[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(vb + ra), of[ks], dp[kt], 0, 0, 0);
+        }
+      // lane (jj, hh): pair jj, keys 16 kt + 4 hh + r; B operand of k-step
+      // sidx, element e <-> key 16 (2 sidx + e / 4) + 4 hh + e % 4
+      bf16x8 sb[2];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int off = 16 * kt + 4 * hh + r;
+          const float p = off <= lim
+                              ? fast_exp2(__builtin_fmaf(s[kt][r], a.scale_log2, -my_l2))
+                              : 0.0f;
+          sb[kt >> 1][4 * (kt & 1) + r] = (__bf16)(p * (dp[kt][r] - my_ds));
+        }
+#pragma unroll
+      for (int sidx = 0; sidx < 2; ++sidx)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t base = row_addr(32 * sidx + tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
+          const bf16x4 lo = lds_read_tr8(kb + base);
+          const bf16x4 hi = lds_read_tr8(kb + base + 16u * RB);
+          const bf16x8 ak = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sb[sidx], dq[dt], 0, 0, 0);
+        }
+    }
+    cur = nxt;
+  }
+  if (my_ok) {
+    uint16_t* orow = a.dq + ph * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      u32x2 wv;
+      wv.x = pack_bf16x2(a.scale * dq[dt][0], a.scale * dq[dt][1]);
+      wv.y = pack_bf16x2(a.scale * dq[dt][2], a.scale * dq[dt][3]);
+      *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * hh) = wv;
+    }
+  }
+  (void)KL;
+}
+
+}  // namespace infllmv2
+
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+using namespace infllmv2;
+
+namespace {
+
+int dq_waves(int G) { return G == 1 ? 2 : (G == 2 ? 4 : 8); }
+int dq_tile_tokens(int G) { return 16 * dq_waves(G) / G; }
+
+struct BwdPlan {
+  int n_b, nw, n_chunks, seg_rows, max_items;
+  bool dense;
+  size_t off_dsum, off_bitmap, off_nseg, off_items, off_count, bytes;
+};
+
+size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdPlan bwd_plan(int n_q, int h_q, int h_kv, int64_t n_k, const Resolved& r) {
+  BwdPlan p;
+  const int G = h_q / h_kv;
+  p.dense = n_k < r.dense_len;
+  p.n_b = (int)ceil_div(n_k, r.B);
+  p.n_chunks = (int)ceil_div(n_k, kChunk);
+  p.nw = (int)ceil_div(n_q, 32);
+  p.seg_rows = kSegPairs / G > 0 ? kSegPairs / G : 1;
+  const int64_t cpb = r.B / kChunk;
+  int64_t items;
+  if (p.dense) {
+    items = (int64_t)h_kv * p.n_chunks * ceil_div(n_q, p.seg_rows);
+  } else {
+    const int64_t kept = (int64_t)n_q * h_kv * (r.topk < p.n_b ? r.topk : p.n_b);
+    items = cpb * ((int64_t)h_kv * p.n_b + ceil_div(kept, p.seg_rows));
+  }
+  p.max_items = items > INT32_MAX ? INT32_MAX : (int)items;
+  size_t o = 0;
+  p.off_dsum = o;   o += al256((size_t)n_q * h_q * 4);
+  p.off_bitmap = o; o += p.dense ? 0 : al256((size_t)h_kv * p.n_b * p.nw * 4);
+  p.off_nseg = o;   o += p.dense ? 0 : al256((size_t)h_kv * p.n_b * 4);
+  p.off_items = o;  o += al256((size_t)p.max_items * 8);
+  p.off_count = o;  o += 256;
+  p.bytes = o;
+  return p;
+}
+
+template <int D>
+int launch_dkdv(int G, const BwdArgs& a, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), grid, dim3(128), 0, st, a); break;
+    case 2:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
+    case 4:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4>), grid, dim3(128), 0, st, a); break;
+    case 8:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8>), grid, dim3(128), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 16>), grid, dim3(128), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 32>), grid, dim3(128), 0, st, a); break;
+    default: return INFLLMV2_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+template <int D>
+int launch_dq(int G, const BwdArgs& a, dim3 grid, hipStream_t st) {
+  switch (G) {
+    case 1:  hipLaunchKernelGGL((bwd_dq_kernel<D, 1, 2>), grid, dim3(128), 0, st, a); break;
+    case 2:  hipLaunchKernelGGL((bwd_dq_kernel<D, 2, 4>), grid, dim3(256), 0, st, a); break;
+    case 4:  hipLaunchKernelGGL((bwd_dq_kernel<D, 4, 8>), grid, dim3(512), 0, st, a); break;
+    case 8:  hipLaunchKernelGGL((bwd_dq_kernel<D, 8, 8>), grid, dim3(512), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((bwd_dq_kernel<D, 16, 8>), grid, dim3(512), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((bwd_dq_kernel<D, 32, 8>), grid, dim3(512), 0, st, a); break;
+    default: return INFLLMV2_ERR_UNSUPPORTED;
+  }
+  return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+}  // namespace
+
+namespace infllmv2 {
+size_t prefill_bwd_workspace_bytes(int n_q, int h_q, int h_kv, int64_t n_k, const Resolved& r) {
+  return bwd_plan(n_q, h_q, h_kv, n_k, r).bytes;
+}
+}  // namespace infllmv2
+
+extern "C" int infllmv2_sparse_attn_prefill_backward(
+    int dtype, const void* q, int32_t n_q, const void* k, const void* v, int64_t cap,
+    int64_t n_k, int32_t h_q, int32_t h_kv, int32_t d, const int32_t* block_idx,
+    const void* out, const float* lse, const void* d_out, void* dq, float* dk, float* dv,
+    void* ws, size_t ws_bytes, const infllmv2_params* p, void* stream) {
+  if (!dtype_ok(dtype)) return INFLLMV2_ERR_INVALID_ARG;
+  INFLLMV2_TRY(check_heads(h_q, h_kv));
+  if (!head_dim_ok(d)) return INFLLMV2_ERR_UNSUPPORTED;
+  Resolved r;
+  INFLLMV2_TRY(check_params(p, d, &r));
+  if (!q || !k || !v || !out || !lse || !d_out || !dq || !dk || !dv)
+    return INFLLMV2_ERR_INVALID_ARG;
+  if (n_q < 0 || n_k <= 0 || cap < n_k || n_q > n_k) return INFLLMV2_ERR_INVALID_ARG;
+  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
+  const bool dense = n_k < r.dense_len;
+  if (!dense && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !aligned16(d_out) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return INFLLMV2_ERR_INVALID_ARG;
+  if (dtype != INFLLMV2_BF16) return INFLLMV2_ERR_UNSUPPORTED;
+  const int G = h_q / h_kv;
+  if (!group_ok_for_mfma(G) || r.B % kChunk != 0) return INFLLMV2_ERR_UNSUPPORTED;
+  const BwdPlan pl = bwd_plan(n_q, h_q, h_kv, n_k, r);
+  if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
+  if (n_q == 0) return INFLLMV2_OK;
+
+  BwdArgs a = {};
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.block_idx = dense ? nullptr : block_idx;
+  a.out = (const uint16_t*)out; a.lse = lse; a.d_out = (const uint16_t*)d_out;
+  a.dq = (uint16_t*)dq; a.dk = dk; a.dv = dv;
+  char* w = (char*)ws;
+  a.dsum = (float*)(w + pl.off_dsum);
+  a.bitmap = (uint32_t*)(w + pl.off_bitmap);
+  a.nseg = (int32_t*)(w + pl.off_nseg);
+  a.items = (int2*)(w + pl.off_items);
+  a.n_items = (int32_t*)(w + pl.off_count);
+  a.cap = cap; a.n_k = n_k; a.n_q = n_q; a.h_q = h_q; a.h_kv = h_kv; a.topk = r.topk;
+  a.B = r.B; a.n_b = pl.n_b; a.nw = pl.nw; a.n_chunks = pl.n_chunks; a.seg_rows = pl.seg_rows;
+  a.max_items = pl.max_items; a.dense = dense ? 1 : 0;
+  a.scale = r.scale; a.scale_log2 = r.scale * kLog2e;
+  const int TT = dq_tile_tokens(G);
+  a.n_tiles = (int)ceil_div(n_q, TT);
+  if ((int64_t)a.n_tiles * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+
+  const int64_t dsum_threads = (int64_t)n_q * h_q * (d / 8);
+  const unsigned dsum_blocks = (unsigned)ceil_div(dsum_threads, 256);
+  if (d == 128) hipLaunchKernelGGL((bwd_dsum_kernel<128>), dim3(dsum_blocks), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((bwd_dsum_kernel<64>), dim3(dsum_blocks), dim3(256), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
+  if (!dense) {
+    const int64_t words = (int64_t)h_kv * pl.n_b * pl.nw;
+    const int64_t fb = ceil_div(words, 256);
+    hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)(fb < 4096 ? fb : 4096)), dim3(256), 0, st,
+                       a.bitmap, words);
+    const int64_t marks = (int64_t)n_q * h_kv * r.topk;
+    hipLaunchKernelGGL(bwd_mark_kernel, dim3((unsigned)ceil_div(marks, 256)), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)ceil_div((int64_t)h_kv * pl.n_b, 4)),
+                       dim3(256), 0, st, a);
+    if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
+  }
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(kPlanThreads1), 0, st, a);
+  if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
+  INFLLMV2_TRY(d == 128 ? launch_dkdv<128>(G, a, dim3((unsigned)pl.max_items), st)
+                        : launch_dkdv<64>(G, a, dim3((unsigned)pl.max_items), st));
+  const dim3 gq((unsigned)(a.n_tiles * h_kv));
+  return d == 128 ? launch_dq<128>(G, a, gq, st) : launch_dq<64>(G, a, gq, st);
+}

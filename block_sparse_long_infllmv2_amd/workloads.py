@@ -32,7 +32,7 @@ import numpy as np
 
 __all__ = [
     "Params", "PrefillCase", "DecodeCase", "TreeCase",
-    "round_to_bf16", "make_prefill", "make_decode", "make_tree",
+    "round_to_bf16", "make_prefill", "make_decode", "make_tree", "make_upstream_grad",
     "config", "CONFIG_NAMES",
 ]
 
@@ -166,6 +166,12 @@ def make_prefill(seed: int, n_k: int, n_q: int, h_q: int, h_kv: int, d: int,
     q += alpha * u
     return PrefillCase(name, dtype, _to_dtype(q, dtype), _to_dtype(k, dtype),
                        _to_dtype(v, dtype), params, planted)
+
+
+def make_upstream_grad(seed: int, n_q: int, h_q: int, d: int, dtype: str) -> np.ndarray:
+    """Gradient arriving at the attention output, [n_q][h_q][d]: N(0, 1)."""
+    g = _rng(seed, 9).standard_normal((n_q, h_q, d), dtype=np.float32)
+    return _to_dtype(g, dtype)
 
 
 def make_decode(seed: int, seqlens, h_q: int, h_kv: int, d: int, params: Params,

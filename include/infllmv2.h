@@ -240,11 +240,50 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
                          void* ws, size_t ws_bytes, const infllmv2_params* p,
                          void* stream);
 
-enum { INFLLMV2_OP_DECODE = 0, INFLLMV2_OP_TREE = 1 };
+/*
+ * Gradients of infllmv2_sparse_attn_prefill with each query's kept blocks
+ * held fixed (selection is a top-k and passes no gradient; the sparse
+ * attention is trained through the blocks it keeps: shadowrocket9.top,
+ * InfLLM v2 section, on the trainable sparse attention).  For query row i,
+ * head h (KV head g) with kept keys J (those of its kept blocks at positions
+ * <= its own, or all keys up to it when dense), p = softmax over j in J of
+ * scale * q.k_j, and upstream gradient do = d_out[i][h]:
+ *   dq[i][h]  = scale * sum_j p_j (do.v_j - do.o) k_j
+ *   dk[g][j] += scale * p_j (do.v_j - do.o) q[i][h]
+ *   dv[g][j] += p_j do
+ * with o = out[i][h] and p recomputed from lse.
+ *   q, k, v, cap, n_k, n_q, h_q, h_kv, d, block_idx: as for
+ *        infllmv2_sparse_attn_prefill (block_idx may be NULL when dense; a
+ *        block listed twice counts once)
+ *   out  [n_q][h_q][d]  the forward output     lse float32 [n_q][h_q] its
+ *        log-sum-exp (natural log), both as written by the forward call
+ *   d_out [n_q][h_q][d] upstream gradient
+ *   dq   [n_q][h_q][d]  written
+ *   dk, dv float32 [h_kv][cap][d]: ACCUMULATED (+=) at the keys the chunk's
+ *        rows attend, so the chunks of a long prompt can add into the same
+ *        buffers; zero them before the first chunk.  Additions from
+ *        different workgroups are float32 atomics, so the rounding of dk and
+ *        dv may differ between runs.
+ *   ws >= infllmv2_workspace_size(INFLLMV2_OP_PREFILL_BWD, n_q, h_q, h_kv, d,
+ *        n_k, p) bytes, 256-byte aligned.
+ * bf16 only (INFLLMV2_F32 returns INFLLMV2_ERR_UNSUPPORTED), block_size a
+ * multiple of 64, G in {1, 2, 4, 8, 16, 32}.
+ */
+int infllmv2_sparse_attn_prefill_backward(int dtype, const void* q, int32_t n_q,
+                                          const void* k, const void* v, int64_t cap,
+                                          int64_t n_k, int32_t h_q, int32_t h_kv,
+                                          int32_t d, const int32_t* block_idx,
+                                          const void* out, const float* lse,
+                                          const void* d_out, void* dq, float* dk,
+                                          float* dv, void* ws, size_t ws_bytes,
+                                          const infllmv2_params* p, void* stream);
+
+enum { INFLLMV2_OP_DECODE = 0, INFLLMV2_OP_TREE = 1, INFLLMV2_OP_PREFILL_BWD = 2 };
 
 /* host: workspace bytes needed by infllmv2_sparse_attn_decode (op DECODE,
- * n = batch, max_len = max_seqlen) or infllmv2_tree_verify (op TREE,
- * n = n_draft, max_len = n_ctx).  0 on invalid arguments. */
+ * n = batch, max_len = max_seqlen), infllmv2_tree_verify (op TREE,
+ * n = n_draft, max_len = n_ctx) or infllmv2_sparse_attn_prefill_backward
+ * (op PREFILL_BWD, n = n_q, max_len = n_k).  0 on invalid arguments. */
 size_t infllmv2_workspace_size(int op, int32_t n, int32_t h_q, int32_t h_kv,
                                int32_t d, int64_t max_len, const infllmv2_params* p);
 

@@ -308,13 +308,15 @@ def attend_backward(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: 
     return dq, dkeys, dvalues
 
 
-def prefill_backward(q, k, v, sel_rows, params, d_out):
+def prefill_backward(q, k, v, sel_rows, params, d_out, rows=None):
     """Gradients of the prefill attention (queries = the last n_q positions
     of n_k keys) with each row's kept blocks fixed: sel_rows[i][g] are row
     i's kept blocks for KV head g, or sel_rows[i] is None for a dense row
     (every key up to its position).  q, d_out: [n_q][h_q][d]; k, v:
     [h_kv][n_k][d].  Returns (dq [n_q][h_q][d], dk, dv [h_kv][n_k][d]);
-    dk / dv sum the contributions of every row that attends a key."""
+    dk / dv sum the contributions of every row that attends a key.  `rows`
+    restricts the work to those query rows (dq of the others stays 0, and
+    dk / dv hold only the listed rows' contributions)."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -325,7 +327,7 @@ def prefill_backward(q, k, v, sel_rows, params, d_out):
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
-    for i in range(n_q):
+    for i in (range(n_q) if rows is None else rows):
         pos = n_k - n_q + i
         for h in range(h_q):
             g = _group_of_head(h, h_q, h_kv)
