@@ -12,7 +12,9 @@ with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
 6 = 128K decode of a batch of 32 sequences (copies of workload 5's sequence),
 7 = the whole 131072-token prompt prefilled in 16 chunks of 8192 (each chunk:
 its new windows -> scores -> top-k -> attention over the keys so far), 8 = the
-final chunk with 128-token blocks and top-6.
+final chunk with 128-token blocks and top-6, 9 = the backward of workload 2's
+attention (dQ, dK, dV through the kept blocks, selections and forward
+outputs resident), one training step's attention gradient for the chunk.
 
 Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
 HIP graph and replayed once; --eager times individual launches), per-stage
@@ -104,6 +106,9 @@ class Workload:
             # 128-token blocks, top-6
             self.case = config(2, seed=seed, params=Params(block_size=128, topk=6))
             self.name = "sparse_prefill_bf16_128k_chunk8192_block128_top6"
+        elif wid == 9:
+            self.case = config(2, seed=seed)
+            self.name = "sparse_prefill_backward_bf16_128k_chunk8192"
         elif wid == 5:
             self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
             self.name = "decode_bf16_128k"
@@ -131,6 +136,23 @@ class Workload:
             torch.cuda.synchronize()
             self.tokens = n_k
             self.kind = "prefill_whole"
+        elif wid == 9:
+            from block_sparse_long_infllmv2_amd.workloads import make_upstream_grad
+            self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
+            h_kv, n_k, d = c.k.shape
+            self.plan = PL.PrefillPlan(c.n_q, n_k, c.q.shape[1], h_kv, d, bf, p, device=dev)
+            nc = _n_windows(n_k, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((h_kv, nc, d), dtype=bf, device=dev)
+            # the forward of the chunk (selections, output, log-sum-exp) is
+            # resident, as after a training forward pass
+            self.plan.run(self.q, self.k, self.v, self.ck, m_begin=0)
+            self.d_out = up(make_upstream_grad(seed, c.n_q, c.q.shape[1], d, "bf16"))
+            self.dq = torch.empty_like(self.q)
+            self.dk = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device=dev)
+            self.dv = torch.zeros_like(self.dk)
+            torch.cuda.synchronize()
+            self.tokens = c.n_q
+            self.kind = "prefill_bwd"
         elif wid in (2, 8):
             self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
             h_kv, n_k, d = c.k.shape
@@ -206,6 +228,11 @@ class Workload:
                 if not skip_dominant:
                     pc.attend(qc, self.k, self.v)
                 mark("sparse_attn_prefill")
+        elif self.kind == "prefill_bwd":
+            mark("start")
+            if not skip_dominant:
+                self.backward()
+            mark("sparse_attn_prefill_backward")
         elif self.kind == "prefill":
             mark("start")
             pl.compress(self.k, self.ck)
@@ -232,11 +259,17 @@ class Workload:
                 pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
             mark("tree_verify")
 
+    def backward(self):
+        self.plan.backward(self.q, self.k, self.v, self.d_out, self.dq, self.dk, self.dv)
+
     # the dominant call alone (the attention call of the step)
     def dominant_call(self):
         pl = self.plan
         if self.kind == "prefill_whole":
             raise NotImplementedError("timed by graph difference only")
+        if self.kind == "prefill_bwd":
+            self.backward()
+            return
         if self.kind == "prefill":
             pl.attend(self.q, self.k, self.v)
         elif self.kind == "decode":
@@ -255,6 +288,16 @@ class Workload:
             return {"dominant": "sparse_attn_prefill", "bound": "mfma",
                     "flop": 4.0 * d * h_q * keys, "score_flop": 2.0 * d * h_kv * float(nvis),
                     "src": "attn_bf16.hip", "launches": len(self.cp.plans)}
+        if self.kind == "prefill_bwd":
+            # five products over the kept keys (S, dP, dV, dK, dQ), 2 d flop
+            # per (row, head, key) each: 2.5 times the forward's two
+            h_kv, n_k, d = c.k.shape
+            h_q = c.q.shape[1]
+            pos = np.arange(n_k - c.n_q, n_k)
+            keys = sum(_visible_selected_keys(int(x), p, p.topk) for x in pos)
+            return {"dominant": "sparse_attn_prefill_backward", "bound": "mfma",
+                    "flop": 10.0 * d * h_q * keys, "score_flop": 0.0,
+                    "src": "attn_bwd.hip", "launches_in_call": 7}
         if self.kind == "prefill":
             h_kv, n_k, d = c.k.shape
             h_q = c.q.shape[1]
@@ -318,6 +361,22 @@ def cpu_baseline(wl, budget_s=20.0):
             return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                     "sample": f"{len(rows)} of {n} prompt positions (every {step}th) incl. "
                               f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
+        if wl.kind == "prefill_bwd":
+            # gradients of single rows, selections taken from the GPU forward
+            sel = wl.plan.block_idx.cpu().numpy()
+            d_out = wl.d_out.float().cpu().numpy()
+            sel_rows = [None] * c.n_q
+            rows, i = [], 0
+            step = max(1, c.n_q // 256)
+            while time.perf_counter() - t0 < budget_s and i < c.n_q:
+                sel_rows[i] = [s[s >= 0] for s in sel[i]]
+                O.prefill_backward(c.q, c.k, c.v, sel_rows, p, d_out, rows=[i])
+                rows.append(i)
+                i += step
+            dt = time.perf_counter() - t0
+            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                    "sample": f"{len(rows)} of {c.n_q} chunk queries (every {step}th): dq of "
+                              f"the row and its dk/dv contributions, float64 numpy, 1 thread"}
         if wl.kind == "prefill":
             ck = O.compress_keys(c.k, p, "bf16")
             rows, i = [], 0
@@ -491,6 +550,11 @@ def main():
                 "kernel_ms": round(dom_ms, 4)}
         if w.get("launches", 1) > 1:
             roof["launches_per_step"] = w["launches"]
+        if "launches_in_call" in w:
+            # a call of several kernels: no single-launch counter figure
+            roof["traffic"] = None
+            roof["kernels_in_call"] = w["launches_in_call"]
+            roof["algorithmic_gflop_per_call"] = roof.pop("algorithmic_gflop_per_launch")
     else:
         achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -504,8 +568,10 @@ def main():
     if wl.kind == "prefill_whole":
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": 8192,
                     "chunks": len(wl.cp.plans)})
-    elif wl.kind == "prefill":
+    elif wl.kind in ("prefill", "prefill_bwd"):
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": int(c.n_q)})
+        if wl.kind == "prefill_bwd":
+            cfg["pass"] = "backward (dq, dk, dv)"
     elif wl.kind == "decode":
         lens = [int(x) for x in np.tile(np.asarray(c.seqlens), wl.rep)]
         cfg.update({"batch": len(lens), "seqlens": lens})

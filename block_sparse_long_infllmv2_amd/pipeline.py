@@ -80,6 +80,18 @@ class PrefillPlan:
         B.infllmv2_sparse_attn_prefill(q, k_cache, v_cache, self.n_k, self.block_idx, self.out,
                                        self.lse, self.p)
 
+    def backward(self, q, k_cache, v_cache, d_out, dq, dk, dv):
+        """Gradients of the last attend() with its selection fixed: dq
+        [n_q][h_q][d] written, float32 dk / dv [h_kv][cap][d] added into.
+        The workspace is allocated on the first call."""
+        if getattr(self, "bwd_ws", None) is None:
+            n = B.infllmv2_workspace_size(B.OP_PREFILL_BWD, self.n_q, self.h_q, self.h_kv,
+                                          self.d, self.n_k, self.p)
+            self.bwd_ws = torch.empty(n, dtype=torch.uint8, device=self.out.device)
+        B.infllmv2_sparse_attn_prefill_backward(q, k_cache, v_cache, self.n_k, self.block_idx,
+                                                self.out, self.lse, d_out, dq, dk, dv,
+                                                self.bwd_ws, self.p)
+
     def run(self, q, k_cache, v_cache, ck_cache, m_begin=None):
         if not self.dense:
             self.compress(k_cache, ck_cache, m_begin)

@@ -7,11 +7,8 @@ kernel path sees irregular patterns; the full-size case uses the selections
 of the forward pipeline.  The forward's own output and log-sum-exp feed the
 backward, as in training.
 
-Tolerance: the gradients are sums of many bf16-rounded products whose size
-grows with the number of rows that attend a key, so errors are measured
-relative to the reference's largest magnitude: max-abs / max|ref| <= 2e-2 and
-mean-abs / max|ref| <= 2e-3 (the bf16 output bar of the forward, applied to
-the gradient scaled to unit size).
+Tolerance (parity.check_grad): the bf16 output bars of the forward, applied
+relative to the reference gradient's largest magnitude.
 """
 import sys
 
@@ -21,11 +18,9 @@ import torch
 
 import oracle as O
 from block_sparse_long_infllmv2_amd.workloads import Params, make_prefill, make_upstream_grad
+from parity import check_grad
 
 pytestmark = pytest.mark.gpu
-
-REL_MAX, REL_MEAN = 2e-2, 2e-3
-
 
 def _say(msg):
     print(f"[case] {msg}", flush=True)
@@ -65,18 +60,6 @@ def random_selection(seed, n_q, n_k, h_kv, p):
             sel = sorted(forced | set(int(b) for b in extra))
             out[i, g, :len(sel)] = sel
     return out
-
-
-def check_grad(got, ref, where):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    assert np.all(np.isfinite(got)), f"{where}: non-finite"
-    scale = max(np.abs(ref).max(), 1e-30)
-    err = np.abs(got - ref)
-    print(f"  {where}: max|ref| {scale:.3g} max-abs {err.max():.3g} "
-          f"mean-abs {err.mean():.3g}", flush=True)
-    assert err.max() <= REL_MAX * scale, f"{where}: max-abs {err.max():.3g} vs {scale:.3g}"
-    assert err.mean() <= REL_MEAN * scale, f"{where}: mean-abs {err.mean():.3g} vs {scale:.3g}"
 
 
 def run_backward(B, c, sel, d_out, dk0=None, dv0=None):

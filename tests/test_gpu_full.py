@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle as O
-from parity import check_close, check_selection
+from parity import check_close, check_grad, check_selection
 
 pytestmark = pytest.mark.gpu
 
@@ -158,3 +158,40 @@ def test_full_decode_128k_batch32():
     np.testing.assert_allclose(lse[0], l, atol=2e-3)
     for i in range(1, out.shape[0]):
         assert np.array_equal(out[i], out[0]) and np.array_equal(sel[i], sel[0]), f"row {i}"
+
+
+def test_full_prefill_backward_sampled():
+    _say("full prefill backward 128K, final 8192-query chunk (workload 9)")
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import bench
+    wl = bench.Workload(9, torch)
+    wl.dk.zero_()
+    wl.dv.zero_()
+    wl.backward()
+    torch.cuda.synchronize()
+    c, p = wl.case, wl.p
+    sel = wl.plan.block_idx.cpu().numpy()
+    d_out = wl.d_out.float().cpu().numpy().astype(np.float64)
+    dq = _host(wl.dq)
+    dk = wl.dk.cpu().numpy().astype(np.float64)
+    dv = wl.dv.cpu().numpy().astype(np.float64)
+    sel_rows = [[s[s >= 0] for s in row] for row in sel]
+    rng = np.random.default_rng(321)
+    rows = sorted(set([0, 1, 63, 64, 4095, 8190, 8191] + list(rng.integers(0, c.n_q, 5))))
+    rq, _, _ = O.prefill_backward(c.q, c.k, c.v, sel_rows, p, d_out, rows=rows)
+    check_grad(dq[rows], rq[rows], "dq sampled rows")
+    # dk / dv at one scored (not forced) block of KV head 0: all rows that kept
+    # it (the oracle takes ~0.7 s per row here, so a block kept by few rows)
+    counts = np.bincount(sel[:, 0][sel[:, 0] >= 0].ravel(), minlength=c.n_k // p.block_size)
+    own0 = (c.n_k - c.n_q) // p.block_size
+    cand = [b for b in range(1, own0 - 1) if 8 <= counts[b] <= 48]
+    if not cand:
+        cand = [b for b in range(1, own0 - 1) if counts[b] > 0]
+    b = max(cand, key=lambda x: counts[x]) if counts[cand].max() <= 48 else \
+        min(cand, key=lambda x: counts[x])
+    krows = list(np.nonzero((sel[:, 0] == b).any(axis=1))[0])
+    _say(f"dk/dv of block {b} (kept by {len(krows)} rows)")
+    _, rk, rv = O.prefill_backward(c.q, c.k, c.v, sel_rows, p, d_out, rows=krows)
+    span = slice(b * p.block_size, (b + 1) * p.block_size)
+    check_grad(dk[0, span], rk[0, span], f"dk block {b}")
+    check_grad(dv[0, span], rv[0, span], f"dv block {b}")
