@@ -14,7 +14,7 @@
 // size keys x rows is stored.
 //
 // Kernels (in launch order):
-//   bwd_dsum    dsum[row][h] = do . o (float32), one per (row, head)
+//   bwd_dsum    per (row, head): lse * log2(e) and dsum = do . o (float32)
 //   fill        clears the row bitmap (sparse chunks only)
 //   bwd_mark    bitmap[g][b] bit i set when row i kept block b for KV head g
 //   bwd_count   per (g, block): segments of at most kSegPairs (row, head)
@@ -22,10 +22,11 @@
 //               many workgroups
 //   bwd_plan    one workgroup scans the segment counts into a list of work
 //               items (KV head, 64-key chunk, segment)
-//   bwd_dkdv    key-major: a workgroup of two waves owns one item; each wave
-//               holds 32 keys of K and V as MFMA operands and their dK^T, dV^T
-//               accumulators in registers, and walks the segment's rows 32
-//               (row, head) pairs at a time through an LDS double buffer:
+//   bwd_dkdv    key-major: a workgroup of four waves owns one item; each wave
+//               holds 16 keys of K and V as MFMA operands and their dK^T, dV^T
+//               accumulators in registers (two waves per SIMD), and walks the
+//               segment's rows 32 (row, head) pairs at a time through a
+//               four-slot LDS ring filled by direct global->LDS copies:
 //                 S = Q K^T, dP = dO V^T            (pairs x keys)
 //                 P = exp(scale S - lse), dS = P (dP - dsum)
 //                 dV^T += dO^T P, dK^T += Q^T dS    (reduction over pairs)
@@ -55,7 +56,7 @@ struct BwdArgs {
   uint16_t* dq;               // [n_q][h_q][D]
   float* dk;                  // [h_kv][cap][D], accumulated
   float* dv;
-  float* dsum;                // workspace [n_q][h_q]
+  float* meta;                // workspace [n_q][h_q][2]: lse * log2(e), do . o
   uint32_t* bitmap;           // workspace [h_kv][n_b][nw]
   int32_t* nseg;              // workspace [h_kv][n_b]
   int2* items;                // workspace [max_items]: (g * n_chunks + chunk, segment)
@@ -71,7 +72,8 @@ constexpr int kSegPairs = 2048;
 constexpr int kPlanThreads1 = 1024;
 
 // ---------------------------------------------------------------------------
-// dsum[row][h] = sum_d do[row][h][d] * o[row][h][d]; D/8 lanes per pair.
+// meta[row][h] = (lse * log2 e, sum_d do[row][h][d] * o[row][h][d]); D/8
+// lanes per pair.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
@@ -90,7 +92,8 @@ __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
   }
 #pragma unroll
   for (int o = L / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (pair < n_pairs && part == 0) a.dsum[pair] = acc;
+  if (pair < n_pairs && part == 0)
+    *reinterpret_cast<float2*>(a.meta + 2 * pair) = make_float2(a.lse[pair] * kLog2e, acc);
 }
 
 __global__ __launch_bounds__(256) void bwd_fill_kernel(uint32_t* p, int64_t n) {
@@ -184,18 +187,40 @@ struct PairTile {
   }
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1)))
+// One 4-byte-per-lane copy global -> LDS (lane l lands at lds_addr + 4 l).
+__device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+
+// Staging ring of the dK/dV kernel: per slot the Q and dO tiles of 32 pairs
+// and, per wave, its own copy of the 32 pairs' (lse * log2 e, dsum).
+constexpr int kDkdvStages = 4;
+template <int D, int NW>
+struct DkdvRing {
+  static constexpr int TB = PairTile<D>::BYTES;
+  static constexpr int META = 32 * 8;
+  static constexpr int SLOT = 2 * TB + NW * META;
+  // 16-byte copies per tile (Q then dO), split evenly over the NW waves
+  static constexpr int INSTR = 2 * 32 * PairTile<D>::CPR / 64;
+  static constexpr int PER_WAVE = INSTR / NW;
+  static constexpr int KL = PER_WAVE + 1;           // + the meta copy
+  static_assert(INSTR % NW == 0, "copies per wave");
+};
+
+// KT: 16-key tiles per wave; the workgroup's 4 / KT waves cover 64 keys.
+template <int D, int G, int KT>
+__global__ __launch_bounds__(256 / KT) __attribute__((amdgpu_waves_per_eu(KT == 1 ? 2 : 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int NT = 128;
+  constexpr int NW = 4 / KT, NT = NW * 64, NS = kDkdvStages;
   constexpr int NKS = D / 32, NDT = D / 16;
   constexpr int SEG_ROWS = (kSegPairs / G) > 0 ? kSegPairs / G : 1;
-  constexpr int SLOTS = 2 * 32 * (D / 8);            // 16-byte pieces of Q and dO per tile
-  constexpr int PER = SLOTS / NT;
   using PT = PairTile<D>;
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2][2 * PT::BYTES];   // [buf][Q | dO]
-  __shared__ float m_lse[2][32], m_dsum[2][32];
-  __shared__ int m_pos[2][32];
+  using RG = DkdvRing<D, NW>;
+  constexpr int KL = RG::KL;
+  static_assert(KL * (NS - 2) <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t ring[NS * RG::SLOT];
   __shared__ int rows_lds[SEG_ROWS];
   __shared__ int scan_lds[NT / 64];
 
@@ -237,16 +262,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
   }
   __syncthreads();
   const int n_pairs = n_rows * G;
-  const int n_tiles = (n_pairs + 31) / 32;
+  const int n_tiles = __builtin_amdgcn_readfirstlane((n_pairs + 31) / 32);
   if (n_tiles <= 0) return;
 
-  // ---- this wave's 32 keys of K and V as B operands (key j of tile kt in
+  // ---- this wave's 16 KT keys of K and V as B operands (key j of tile kt in
   // lane column j, dims 32 ks + 8 h .. +8); keys past n_k repeat the last key
   const int jj = lane & 15, hh = lane >> 4;
-  const int kw0 = key0 + 32 * wave;
-  bf16x8 kf[2][NKS], vf[2][NKS];
+  const int kw0 = key0 + 16 * KT * wave;
+  bf16x8 kf[KT][NKS], vf[KT][NKS];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = min(kw0 + 16 * kt + jj, (int)a.n_k - 1);
     const uint16_t* kr = a.k + ((int64_t)g * a.cap + key) * D + 8 * hh;
     const uint16_t* vr = a.v + ((int64_t)g * a.cap + key) * D + 8 * hh;
@@ -257,85 +282,79 @@ void bwd_dkdv_kernel(BwdArgs a) {
       vf[kt][ks] = *reinterpret_cast<const bf16x8*>(&wv);
     }
   }
-  f32x4 dk[2][NDT], dv[2][NDT];
+  f32x4 dk[KT][NDT], dv[KT][NDT];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt)
+  for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       dk[kt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       dv[kt][dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+  // K and V have arrived before the direct copies start (the compiler's own
+  // waits do not see those copies)
+  __builtin_amdgcn_s_waitcnt(0x0f70);
 
-  // ---- tile staging through registers: slot s -> tensor s / (32 CPR),
-  // pair (s / CPR) % 32, chunk s % CPR
-  const int64_t qoff = (int64_t)a.n_k - a.n_q;
-  u32x4 pre[PER];
-  float pre_lse = 0.0f, pre_dsum = 0.0f;
-  int pre_pos = -1;
-  auto load_tile = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int s = i * NT + tid;
-      const int tensor = s / (32 * PT::CPR);
-      const int pr = (s / PT::CPR) % 32, c = s % PT::CPR;
-      const int p = t * 32 + pr;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (p < n_pairs) {
-        const int row = rows_lds[p / G], head = g * G + p % G;
-        const uint16_t* src = (tensor == 0 ? a.q : a.d_out) + ((int64_t)row * a.h_q + head) * D;
-        w = ldg16(src + 8 * c);
-      }
-      pre[i] = w;
-    }
-    if (tid < 32) {
-      const int p = t * 32 + tid;
-      pre_lse = INFINITY;
-      pre_dsum = 0.0f;
-      pre_pos = -1;
-      if (p < n_pairs) {
-        const int row = rows_lds[p / G], head = g * G + p % G;
-        const int64_t ph = (int64_t)row * a.h_q + head;
-        pre_lse = a.lse[ph] * kLog2e;
-        pre_dsum = a.dsum[ph];
-        pre_pos = (int)(qoff + row);
-      }
-    }
+  // ---- direct copies of tile t into slot `slot`.  Pairs past the segment
+  // repeat its last pair (finite data, masked by position).  Byte offsets
+  // are 32-bit: the host keeps n_q * h_q * D * 2 below 4 GiB.
+  const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // (row * h_q + head) of pair p (clamped to the segment), 32-bit: the host
+  // keeps n_q * h_q * D * 2 below 4 GiB
+  const uint32_t n_pairs_u = (uint32_t)n_pairs, hq_u = (uint32_t)a.h_q, hg = (uint32_t)(g * G);
+  auto pair_index = [&](uint32_t p) -> uint32_t {
+    p = min(p, n_pairs_u - 1u);
+    return __umul24((uint32_t)rows_lds[p / G], hq_u) + hg + p % G;
   };
-  auto store_tile = [&](int buf) {
+  // per lane and copy: pair row r and logical chunk c do not depend on the tile
+  uint32_t cp_r[RG::PER_WAVE], cp_c16[RG::PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int s = i * NT + tid;
-      const int tensor = s / (32 * PT::CPR);
-      const int pr = (s / PT::CPR) % 32, c = s % PT::CPR;
-      *reinterpret_cast<u32x4*>(&tiles[buf][tensor * PT::BYTES + PT::at(pr, c)]) = pre[i];
+  for (int i = 0; i < RG::PER_WAVE; ++i) {
+    const int s = (wave_u * RG::PER_WAVE + i) * 64 + lane;
+    const int r = (s / PT::CPR) % 32, pc = s % PT::CPR;
+    cp_r[i] = (uint32_t)r;
+    cp_c16[i] = (uint32_t)(16 * (pc ^ PT::f(r)));
+  }
+  auto issue = [&](int t, int slot) {
+    const uint32_t sb = ring0 + (uint32_t)(slot * RG::SLOT);
+    const uint32_t p0 = (uint32_t)t * 32u;
+#pragma unroll
+    for (int i = 0; i < RG::PER_WAVE; ++i) {
+      const int j = wave_u * RG::PER_WAVE + i;              // copy index in the tile
+      // the 64 slots of copy j lie in one tensor (a tensor is 32 CPR slots)
+      const bool is_q = j * 64 < 32 * PT::CPR;
+      const uint32_t voff = pair_index(p0 + cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
+      lds_dma16(sb + (uint32_t)(j * 1024), is_q ? (const void*)a.q : (const void*)a.d_out, voff);
     }
-    if (tid < 32) {
-      m_lse[buf][tid] = pre_lse;
-      m_dsum[buf][tid] = pre_dsum;
-      m_pos[buf][tid] = pre_pos;
-    }
+    const uint32_t moff = pair_index(p0 + (uint32_t)(lane >> 1)) * 8u + 4u * (uint32_t)(lane & 1);
+    lds_dma4(sb + (uint32_t)(2 * RG::TB + wave_u * RG::META), a.meta, moff);
   };
 
-  const uint32_t lds_tiles0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)tiles;
-  // 16-byte row reads: lane (jj, hh) reads pair row 16 pt + jj, logical chunk 4 ks + hh
-  // transposing reads (d-tile dt, half c): pair row 16 c + 4 hh + jj / 4, d 16 dt + 4 (jj % 4)
+  // 16-byte row reads: lane (jj, hh) reads pair row 16 pt + jj, logical chunk
+  // 4 ks + hh.  The chunk bits never overlap the row bits and f depends on the
+  // row mod 16, so k-step ks is an XOR of 64 ks on one per-lane base and pair
+  // tile pt adds 16 rows (an immediate offset).
+  // Transposing reads (d-tile dt, half c): pair row 16 c + 4 hh + jj / 4,
+  // d 16 dt + 4 (jj % 4): an XOR of 32 dt on one base, half c adds 16 rows.
+  const uint32_t rd_base = (uint32_t)(jj * PT::RB + ((hh ^ PT::f(jj)) * 16));
   const int tr_row = 4 * hh + (jj >> 2), tr_q = jj & 3;
-  const int key_lane[2] = {kw0 + jj, kw0 + 16 + jj};
+  const uint32_t tr_base =
+      (uint32_t)(tr_row * PT::RB + (((tr_q >> 1) ^ PT::f(tr_row)) * 16) + 8 * (tr_q & 1));
+  int key_lane[KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt) key_lane[kt] = kw0 + 16 * kt + jj;
+  const int qoff = (int)(a.n_k - a.n_q);
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) load_tile(t + 1);
-    const uint32_t qb = lds_tiles0 + (uint32_t)(buf * 2 * PT::BYTES);
-    const uint32_t ob = qb + (uint32_t)PT::BYTES;
-    // S = Q K^T and dP = dO V^T: [pair tile pt][key tile kt]
-    f32x4 s[2][2], dp[2][2];
+  auto compute = [&](int t, int slot) {
+    const uint32_t qb = ring0 + (uint32_t)(slot * RG::SLOT);
+    const uint32_t ob = qb + (uint32_t)RG::TB;
+    const float2* meta = reinterpret_cast<const float2*>(&ring[slot * RG::SLOT + 2 * RG::TB +
+                                                               wave * RG::META]);
+    f32x4 s[2][KT], dp[2][KT];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         s[pt][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         dp[pt][kt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       }
@@ -343,55 +362,71 @@ void bwd_dkdv_kernel(BwdArgs a) {
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        const bf16x8 aq = lds_read16(qb + PT::at(16 * pt + jj, 4 * ks + hh));
-        const bf16x8 ao = lds_read16(ob + PT::at(16 * pt + jj, 4 * ks + hh));
+        const uint32_t ra = (rd_base ^ (uint32_t)(64 * ks)) + (uint32_t)(16 * pt * PT::RB);
+        const bf16x8 aq = lds_read16(qb + ra);
+        const bf16x8 ao = lds_read16(ob + ra);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
           s[pt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq, kf[kt][ks], s[pt][kt], 0, 0, 0);
           dp[pt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kt][ks], dp[pt][kt], 0, 0, 0);
         }
       }
     // P and dS; lane (jj, hh) holds pairs 16 pt + 4 hh + r of key 16 kt + jj
-    bf16x8 pb[2], sb[2];
+    bf16x8 pb[KT], sb[KT];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int pr = 16 * pt + 4 * hh + r;
-        const float l2 = m_lse[buf][pr], ds = m_dsum[buf][pr];
-        const int pos = m_pos[buf][pr];
+        const uint32_t p = (uint32_t)(t * 32 + pr);
+        const float2 m = meta[pr];
+        const int pos = p < n_pairs_u ? qoff + rows_lds[p / G] : -1;
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const float p = key_lane[kt] <= pos
-                              ? fast_exp2(__builtin_fmaf(s[pt][kt][r], a.scale_log2, -l2))
-                              : 0.0f;
-          pb[kt][4 * pt + r] = (__bf16)p;
-          sb[kt][4 * pt + r] = (__bf16)(p * (dp[pt][kt][r] - ds));
+        for (int kt = 0; kt < KT; ++kt) {
+          const float pv = key_lane[kt] <= pos
+                               ? fast_exp2(__builtin_fmaf(s[pt][kt][r], a.scale_log2, -m.x))
+                               : 0.0f;
+          pb[kt][4 * pt + r] = (__bf16)pv;
+          sb[kt][4 * pt + r] = (__bf16)(pv * (dp[pt][kt][r] - m.y));
         }
       }
     // dV^T += dO^T P, dK^T += Q^T dS: A rows d of d-tile dt, reduction over
     // pairs in the order 4 hh + e (e < 4), 16 + 4 hh + e - 4 (e >= 4)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const uint32_t lo = PT::at(tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
-      const uint32_t hi = PT::at(16 + tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
+      const uint32_t lo = tr_base ^ (uint32_t)(32 * dt);
+      const uint32_t hi = lo + (uint32_t)(16 * PT::RB);
       const bf16x4 o0 = lds_read_tr8(ob + lo), o1 = lds_read_tr8(ob + hi);
       const bf16x4 q0 = lds_read_tr8(qb + lo), q1 = lds_read_tr8(qb + hi);
       const bf16x8 aot = __builtin_shufflevector(o0, o1, 0, 1, 2, 3, 4, 5, 6, 7);
       const bf16x8 aqt = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < KT; ++kt) {
         dv[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aot, pb[kt], dv[kt][dt], 0, 0, 0);
         dk[kt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aqt, sb[kt], dk[kt][dt], 0, 0, 0);
       }
     }
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Tile t sits in slot t % NS.  Iteration t: wait for tile t (the copies
+  // issued after it, of tiles t+1 .. t+NS-2, may still be in flight), meet
+  // (every wave has finished tile t-1, so its slot is free), copy tile
+  // t+NS-1 into that slot, compute tile t.
+#pragma unroll
+  for (int j = 0; j + 1 < NS; ++j)
+    if (j < n_tiles) issue(j, j);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int after = min(NS - 2, n_tiles - 1 - t);
+    if (after >= 2) wait_vm_barrier<2 * KL>();
+    else if (after == 1) wait_vm_barrier<KL>();
+    else wait_vm_barrier<0>();
+    if (t + NS - 1 < n_tiles) issue(t + NS - 1, (t + NS - 1) % NS);
+    compute(t, t % NS);
   }
 
   // ---- accumulate: lane (jj, hh) holds key 16 kt + jj, d = 16 dt + 4 hh + r
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = key_lane[kt];
     if (key >= a.n_k) continue;
     float* dkr = a.dk + ((int64_t)g * a.cap + key) * D + 4 * hh;
@@ -487,8 +522,8 @@ void bwd_dq_kernel(BwdArgs a) {
     qf[ks] = *reinterpret_cast<const bf16x8*>(&wq);
     of[ks] = *reinterpret_cast<const bf16x8*>(&wo);
   }
-  const float my_l2 = my_ok ? a.lse[ph] * kLog2e : INFINITY;
-  const float my_ds = my_ok ? a.dsum[ph] : 0.0f;
+  const float my_l2 = my_ok ? a.meta[2 * ph] : INFINITY;
+  const float my_ds = my_ok ? a.meta[2 * ph + 1] : 0.0f;
   f32x4 dq[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) dq[dt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -516,6 +551,7 @@ void bwd_dq_kernel(BwdArgs a) {
   auto row_addr = [&](int r, int c) -> uint32_t {
     return (uint32_t)(r * RB + ((c ^ Swz16V<D>::f(r)) * 16));
   };
+
   const int tr_row = 4 * hh + (jj >> 2), tr_q = jj & 3;
 
   Unit cur = unit_of(0);
@@ -620,7 +656,7 @@ BwdPlan bwd_plan(int n_q, int h_q, int h_kv, int64_t n_k, const Resolved& r) {
   }
   p.max_items = items > INT32_MAX ? INT32_MAX : (int)items;
   size_t o = 0;
-  p.off_dsum = o;   o += al256((size_t)n_q * h_q * 4);
+  p.off_dsum = o;   o += al256((size_t)n_q * h_q * 8);
   p.off_bitmap = o; o += p.dense ? 0 : al256((size_t)h_kv * p.n_b * p.nw * 4);
   p.off_nseg = o;   o += p.dense ? 0 : al256((size_t)h_kv * p.n_b * 4);
   p.off_items = o;  o += al256((size_t)p.max_items * 8);
@@ -629,15 +665,20 @@ BwdPlan bwd_plan(int n_q, int h_q, int h_kv, int64_t n_k, const Resolved& r) {
   return p;
 }
 
+#ifndef INFLLMV2_DKDV_KT
+#define INFLLMV2_DKDV_KT 1
+#endif
+constexpr int kDkdvKT = INFLLMV2_DKDV_KT;            // 16-key tiles per wave
 template <int D>
 int launch_dkdv(int G, const BwdArgs& a, dim3 grid, hipStream_t st) {
+  constexpr int NT = 256 / kDkdvKT;
   switch (G) {
-    case 1:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1>), grid, dim3(128), 0, st, a); break;
-    case 2:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2>), grid, dim3(128), 0, st, a); break;
-    case 4:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4>), grid, dim3(128), 0, st, a); break;
-    case 8:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8>), grid, dim3(128), 0, st, a); break;
-    case 16: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 16>), grid, dim3(128), 0, st, a); break;
-    case 32: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 32>), grid, dim3(128), 0, st, a); break;
+    case 1:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 1, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
+    case 2:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 2, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
+    case 4:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 4, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
+    case 8:  hipLaunchKernelGGL((bwd_dkdv_kernel<D, 8, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
+    case 16: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 16, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((bwd_dkdv_kernel<D, 32, kDkdvKT>), grid, dim3(NT), 0, st, a); break;
     default: return INFLLMV2_ERR_UNSUPPORTED;
   }
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
@@ -687,6 +728,8 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   if (dtype != INFLLMV2_BF16) return INFLLMV2_ERR_UNSUPPORTED;
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G) || r.B % kChunk != 0) return INFLLMV2_ERR_UNSUPPORTED;
+  // the dK/dV kernel's direct copies address Q, dO and meta with 32-bit offsets
+  if ((int64_t)n_q * h_q * d * 2 >= (1ll << 32)) return INFLLMV2_ERR_UNSUPPORTED;
   const BwdPlan pl = bwd_plan(n_q, h_q, h_kv, n_k, r);
   if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
   if (n_q == 0) return INFLLMV2_OK;
@@ -697,7 +740,7 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   a.out = (const uint16_t*)out; a.lse = lse; a.d_out = (const uint16_t*)d_out;
   a.dq = (uint16_t*)dq; a.dk = dk; a.dv = dv;
   char* w = (char*)ws;
-  a.dsum = (float*)(w + pl.off_dsum);
+  a.meta = (float*)(w + pl.off_dsum);
   a.bitmap = (uint32_t*)(w + pl.off_bitmap);
   a.nseg = (int32_t*)(w + pl.off_nseg);
   a.items = (int2*)(w + pl.off_items);
