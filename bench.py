@@ -63,14 +63,20 @@ def _kept_keys(pos, p):
 
 
 def _kernel_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of a kernel source and every header of the library (the kernels
+    include them), so a counter figure goes stale when any of them changes."""
+    csrc = os.path.dirname(path)
+    h = hashlib.sha256()
+    for f in [path] + sorted(os.path.join(csrc, n) for n in os.listdir(csrc) if n.endswith(".h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
-def _traffic(kernel_name, src_file):
-    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they
-    were taken on the current kernel source (else None)."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_name}.json")
+def _traffic(kernel_name, src_file, workload):
+    """HBM bytes per call from committed rocprofv3 PMC summaries of this
+    workload, if they were taken on the current kernel source (else None)."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{kernel_name}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -543,7 +549,7 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 # the counter figure is per launch of the final-chunk workload
-                "traffic": _traffic(dom, src) if w.get("launches", 1) == 1 else None,
+                "traffic": _traffic(dom, src, wl.name) if w.get("launches", 1) == 1 else None,
                 "kernel": dom,
                 ("algorithmic_gflop_per_step" if w.get("launches", 1) > 1
                  else "algorithmic_gflop_per_launch"): round(w["flop"] / 1e9, 2),
@@ -559,7 +565,7 @@ def main():
         achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic(dom, src), "kernel": dom,
+                "traffic": _traffic(dom, src, wl.name), "kernel": dom,
                 "algorithmic_mb_per_launch": round(w["bytes"] / 1e6, 3),
                 "kernel_ms": round(dom_ms, 4)}
 
