@@ -50,6 +50,10 @@ Readings where the pages leave a step open (each one listed in the design doc):
   R15 head h belongs to KV group floor(h * h_kv / h_q).
   R16 compressed keys are stored in K's dtype (round-to-nearest-even).
   R18 if a query has no more eligible blocks than k, it keeps all of them.
+  R21 training: gradients of the attention over each query's kept keys with
+      the selection held fixed (top-k passes no gradient; compressed keys and
+      block scores receive none); a key's dk / dv sum the contributions of
+      every row that attends it.
 
 Everything is float64; inputs are upcast exactly.  No blocking, no online
 softmax, no fusion: each function is one step of the definition.
