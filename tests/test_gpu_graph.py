@@ -1,10 +1,12 @@
 """HIP graph capture of whole steps (chunked prefill, ragged decode, tree
-verification).  The library only launches kernels on the caller's stream and
+verification, prefill forward + backward).  The library only launches kernels on the caller's stream and
 allocates nothing, so a step captures whole; bench.py times steps as graph
 replays.  Each test captures a step, then replays it several times with the
 program's own eager work in between (the same plan run eagerly on other
 queries, other torch work, synchronisations) and checks every replay against
-the eager result bit for bit (the kernels are deterministic)."""
+the eager result bit for bit (the kernels are deterministic; the backward's
+dk and dv are sums of float32 atomics, whose order may vary, so they are
+compared to 1e-5 of their largest magnitude)."""
 import sys
 
 import numpy as np
@@ -123,3 +125,47 @@ def test_graph_tree_step(B, PL):
     _replay_check(lambda: plan.run(q, k, v, ck[0], kd, vd, mask),
                   lambda: [plan.out, plan.lse, plan.block_idx],
                   lambda: plan.run(q2, k, v, ck[0], kd, vd, mask))
+
+
+def test_graph_forward_backward_step(B, PL):
+    _say("graph: prefill forward + backward step")
+    from block_sparse_long_infllmv2_amd.workloads import make_upstream_grad
+    p = Params(topk=12, dense_len=0)
+    c = make_prefill(24, n_k=5000, n_q=300, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=4, alpha=1.5, beta=1.5)
+    q, k, v = up(c.q), up(c.k), up(c.v)
+    q2 = up(np.flip(c.q, axis=0).copy())
+    do = up(make_upstream_grad(24, c.n_q, 32, 128, "bf16"))
+    h_kv, n_k, d = c.k.shape
+    plan = PL.PrefillPlan(c.n_q, n_k, c.q.shape[1], h_kv, d, torch.bfloat16, p)
+    ck = torch.zeros((h_kv, _nwin(n_k, p), d), dtype=torch.bfloat16, device="cuda")
+    plan.compress(k, ck, m_begin=0)
+    dq = torch.empty_like(q)
+    dk = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+
+    def step(qq):
+        dk.zero_()
+        dv.zero_()
+        plan.run(qq, k, v, ck)
+        plan.backward(qq, k, v, do, dq, dk, dv)
+
+    step(q)
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (plan.out, plan.block_idx, dq, dk, dv)]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(q)
+    for i in range(4):
+        step(q2)                                          # eager, different queries
+        torch.cuda.synchronize()
+        assert not torch.equal(dq, ref[2]), "the eager work in between should change dq"
+        (torch.randn(1 << 16, device="cuda") * 2.0).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "block_idx", "dq"), (plan.out, plan.block_idx, dq),
+                              ref[:3]):
+            assert torch.equal(a, b), f"replay {i}: {name} differs from the eager step"
+        for name, a, b in zip(("dk", "dv"), (dk, dv), ref[3:]):
+            tol = 1e-5 * float(b.abs().max())
+            assert float((a - b).abs().max()) <= tol, f"replay {i}: {name} differs"
