@@ -80,17 +80,22 @@ class PrefillPlan:
         B.infllmv2_sparse_attn_prefill(q, k_cache, v_cache, self.n_k, self.block_idx, self.out,
                                        self.lse, self.p)
 
-    def backward(self, q, k_cache, v_cache, d_out, dq, dk, dv):
+    def backward_workspace_bytes(self):
+        return B.infllmv2_workspace_size(B.OP_PREFILL_BWD, self.n_q, self.h_q, self.h_kv,
+                                         self.d, self.n_k, self.p)
+
+    def backward(self, q, k_cache, v_cache, d_out, dq, dk, dv, ws=None):
         """Gradients of the last attend() with its selection fixed: dq
         [n_q][h_q][d] written, float32 dk / dv [h_kv][cap][d] added into.
-        The workspace is allocated on the first call."""
-        if getattr(self, "bwd_ws", None) is None:
-            n = B.infllmv2_workspace_size(B.OP_PREFILL_BWD, self.n_q, self.h_q, self.h_kv,
-                                          self.d, self.n_k, self.p)
-            self.bwd_ws = torch.empty(n, dtype=torch.uint8, device=self.out.device)
+        Without `ws` the plan allocates its workspace on the first call."""
+        if ws is None:
+            if getattr(self, "bwd_ws", None) is None:
+                self.bwd_ws = torch.empty(self.backward_workspace_bytes(), dtype=torch.uint8,
+                                          device=self.out.device)
+            ws = self.bwd_ws
         B.infllmv2_sparse_attn_prefill_backward(q, k_cache, v_cache, self.n_k, self.block_idx,
-                                                self.out, self.lse, d_out, dq, dk, dv,
-                                                self.bwd_ws, self.p)
+                                                self.out, self.lse, d_out, dq, dk, dv, ws,
+                                                self.p)
 
     def run(self, q, k_cache, v_cache, ck_cache, m_begin=None):
         if not self.dense:
@@ -119,10 +124,13 @@ class ChunkedPrefill:
     long prompt.  Each chunk: compress the windows it completes, block
     scores, top-k, sparse attention (a chunk whose keys number fewer than
     dense_len: its windows, then dense attention only).  Plans and buffers
-    are made once; all chunks share one score and one selection scratch
-    buffer and write into one output."""
+    are made once; all chunks share one score scratch buffer and write into
+    one output.  The chunks share one selection buffer too, unless
+    keep_selections is set (training): then every chunk keeps its own rows'
+    selections, which backward() needs."""
 
-    def __init__(self, n, chunk, h_q, h_kv, d, dtype, params, device="cuda"):
+    def __init__(self, n, chunk, h_q, h_kv, d, dtype, params, device="cuda",
+                 keep_selections=False):
         self.p = B.to_params(params)
         self.n, self.chunk = n, chunk
         dev = torch.device(device)
@@ -131,11 +139,17 @@ class ChunkedPrefill:
         self.lse = torch.empty((n, h_q), dtype=torch.float32, device=dev)
         nb_max = (n + self.p.block_size - 1) // self.p.block_size
         self.score_buf = torch.empty(chunk * h_kv * nb_max, dtype=torch.float32, device=dev)
-        self.idx_buf = torch.empty(chunk * h_kv * self.p.topk, dtype=torch.int32, device=dev)
+        per_row = h_kv * self.p.topk
+        self.keep_selections = keep_selections
+        self.idx_buf = torch.empty((n if keep_selections else chunk) * per_row,
+                                   dtype=torch.int32, device=dev)
         self.plans = [PrefillPlan(q1 - q0, n_k, h_q, h_kv, d, dtype, params, device=dev,
                                   out=self.out[q0:q1], lse=self.lse[q0:q1],
-                                  score_buf=self.score_buf, idx_buf=self.idx_buf)
+                                  score_buf=self.score_buf,
+                                  idx_buf=self.idx_buf[q0 * per_row:] if keep_selections
+                                  else self.idx_buf)
                       for (q0, q1, n_k, _, _) in self.sched]
+        self.bwd_ws = None
 
     def run(self, q, k_cache, v_cache, ck_cache, skip_attention=False):
         """q [n][h_q][d]; K/V caches [h_kv][cap >= n][d]; ck_cache
@@ -156,6 +170,20 @@ class ChunkedPrefill:
         """The attention calls of every chunk (selections from the last run)."""
         for (q0, q1, _, _, _), pl in zip(self.sched, self.plans):
             pl.attend(q[q0:q1], k_cache, v_cache)
+
+    def backward(self, q, k_cache, v_cache, d_out, dq, dk, dv):
+        """Gradients of the whole prompt's attention (the last run, its
+        selections fixed): dq [n][h_q][d] written, float32 dk / dv
+        [h_kv][cap][d] added into by every chunk (zero them first).  Needs
+        keep_selections."""
+        if not self.keep_selections:
+            raise ValueError("backward() needs ChunkedPrefill(..., keep_selections=True)")
+        if self.bwd_ws is None:
+            n = max(pl.backward_workspace_bytes() for pl in self.plans)
+            self.bwd_ws = torch.empty(n, dtype=torch.uint8, device=self.out.device)
+        for (q0, q1, _, _, _), pl in zip(self.sched, self.plans):
+            pl.backward(q[q0:q1], k_cache, v_cache, d_out[q0:q1], dq[q0:q1], dk, dv,
+                        ws=self.bwd_ws)
 
 
 class DecodePlan:

@@ -199,3 +199,42 @@ def test_backward_rejects_f32_and_small_workspace(B):
     with pytest.raises(B.InfLLMv2Error, match="workspace"):
         B.infllmv2_sparse_attn_prefill_backward(qb, kb, kb, n_k, bi, qb, lse, qb, qb, dk, dk,
                                                 small, p)
+
+
+def test_backward_block192(B):
+    _say("backward block 192 (three 64-key chunks per block), n_k=3000, n_q=120, topk=6")
+    c = case(60, 3000, 120, 16, 2, 64, block_size=192, topk=6, dense_len=0)
+    sel = random_selection(61, c.n_q, c.n_k, 2, c.params)
+    compare(B, c, sel, "block192")
+
+
+def test_backward_whole_prompt_in_chunks(B):
+    """A 2500-token prompt run forward and backward in chunks of 1000 (the
+    first chunk dense, the others sparse): every chunk adds its dk/dv into the
+    same buffers, and the result equals the oracle's backward of the whole
+    prompt with each row's selection as the forward made it."""
+    _say("chunked backward: 2500 tokens in chunks of 1000, dense_len 1500")
+    from block_sparse_long_infllmv2_amd import pipeline as PL
+    p = Params(topk=8, dense_len=1500)
+    n, chunk, h_q, h_kv, d = 2500, 1000, 16, 1, 64
+    c = make_prefill(70, n_k=n, n_q=n, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype="bf16",
+                     n_planted=3, alpha=1.5, beta=1.5)
+    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    nc = O.num_windows(n, p.kernel_size, p.kernel_stride)
+    ck = torch.zeros((h_kv, nc, d), dtype=torch.bfloat16, device="cuda")
+    cp = PL.ChunkedPrefill(n, chunk, h_q, h_kv, d, torch.bfloat16, p, keep_selections=True)
+    cp.run(q, k, v, ck)
+    d_out = make_upstream_grad(71, n, h_q, d, "bf16")
+    dq = torch.empty_like(q)
+    dk = torch.zeros((h_kv, n, d), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    cp.backward(q, k, v, dev(d_out), dq, dk, dv)
+    torch.cuda.synchronize()
+    assert [pl.dense for pl in cp.plans] == [True, False, False]
+    sel = cp.idx_buf.view(n, h_kv, p.topk).cpu().numpy()
+    rows = [None if cp.plans[i // chunk].dense else [s[s >= 0] for s in sel[i]]
+            for i in range(n)]
+    rq, rk, rv = O.prefill_backward(c.q, c.k, c.v, rows, p, d_out)
+    check_grad(host(dq), rq, "chunked dq")
+    check_grad(dk.cpu().numpy(), rk, "chunked dk")
+    check_grad(dv.cpu().numpy(), rv, "chunked dv")
