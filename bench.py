@@ -14,7 +14,9 @@ with 16 drafts, 4 = ragged decode of 8 sequences up to 128K, 5 = 128K decode,
 its new windows -> scores -> top-k -> attention over the keys so far), 8 = the
 final chunk with 128-token blocks and top-6, 9 = the backward of workload 2's
 attention (dQ, dK, dV through the kept blocks, selections and forward
-outputs resident), one training step's attention gradient for the chunk.
+outputs resident), one training step's attention gradient for the chunk,
+10 = the backward of workload 7's whole 131072-token prompt (16 chunk
+backwards adding into one dK/dV).
 
 Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
 HIP graph and replayed once; --eager times individual launches), per-stage
@@ -115,6 +117,9 @@ class Workload:
         elif wid == 9:
             self.case = config(2, seed=seed)
             self.name = "sparse_prefill_backward_bf16_128k_chunk8192"
+        elif wid == 10:
+            self.case = config(2, seed=seed, n_q=131072)
+            self.name = "sparse_prefill_backward_bf16_128k_whole_16x8192"
         elif wid == 5:
             self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
             self.name = "decode_bf16_128k"
@@ -142,6 +147,24 @@ class Workload:
             torch.cuda.synchronize()
             self.tokens = n_k
             self.kind = "prefill_whole"
+        elif wid == 10:
+            from block_sparse_long_infllmv2_amd.workloads import make_upstream_grad
+            self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
+            h_kv, n_k, d = c.k.shape
+            self.cp = PL.ChunkedPrefill(n_k, 8192, c.q.shape[1], h_kv, d, bf, p, device=dev,
+                                        keep_selections=True)
+            self.plan = self.cp.plans[-1]
+            nc = _n_windows(n_k, p.kernel_size, p.kernel_stride)
+            self.ck = torch.zeros((h_kv, nc, d), dtype=bf, device=dev)
+            # the whole prompt's forward (selections, outputs, log-sum-exp)
+            self.cp.run(self.q, self.k, self.v, self.ck)
+            self.d_out = up(make_upstream_grad(seed, n_k, c.q.shape[1], d, "bf16"))
+            self.dq = torch.empty_like(self.q)
+            self.dk = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device=dev)
+            self.dv = torch.zeros_like(self.dk)
+            torch.cuda.synchronize()
+            self.tokens = n_k
+            self.kind = "prefill_bwd_whole"
         elif wid == 9:
             from block_sparse_long_infllmv2_amd.workloads import make_upstream_grad
             self.q, self.k, self.v = up(c.q), up(c.k), up(c.v)
@@ -234,7 +257,7 @@ class Workload:
                 if not skip_dominant:
                     pc.attend(qc, self.k, self.v)
                 mark("sparse_attn_prefill")
-        elif self.kind == "prefill_bwd":
+        elif self.kind in ("prefill_bwd", "prefill_bwd_whole"):
             mark("start")
             if not skip_dominant:
                 self.backward()
@@ -266,14 +289,17 @@ class Workload:
             mark("tree_verify")
 
     def backward(self):
-        self.plan.backward(self.q, self.k, self.v, self.d_out, self.dq, self.dk, self.dv)
+        if self.kind == "prefill_bwd_whole":
+            self.cp.backward(self.q, self.k, self.v, self.d_out, self.dq, self.dk, self.dv)
+        else:
+            self.plan.backward(self.q, self.k, self.v, self.d_out, self.dq, self.dk, self.dv)
 
     # the dominant call alone (the attention call of the step)
     def dominant_call(self):
         pl = self.plan
         if self.kind == "prefill_whole":
             raise NotImplementedError("timed by graph difference only")
-        if self.kind == "prefill_bwd":
+        if self.kind in ("prefill_bwd", "prefill_bwd_whole"):
             self.backward()
             return
         if self.kind == "prefill":
@@ -294,6 +320,14 @@ class Workload:
             return {"dominant": "sparse_attn_prefill", "bound": "mfma",
                     "flop": 4.0 * d * h_q * keys, "score_flop": 2.0 * d * h_kv * float(nvis),
                     "src": "attn_bf16.hip", "launches": len(self.cp.plans)}
+        if self.kind == "prefill_bwd_whole":
+            h_kv, n_k, d = c.k.shape
+            h_q = c.q.shape[1]
+            keys = sum(_kept_keys(x, p) for x in range(n_k))
+            return {"dominant": "sparse_attn_prefill_backward", "bound": "mfma",
+                    "flop": 10.0 * d * h_q * keys, "score_flop": 0.0,
+                    "src": "attn_bwd.hip", "launches": len(self.cp.plans),
+                    "launches_in_call": 7}
         if self.kind == "prefill_bwd":
             # five products over the kept keys (S, dP, dV, dK, dQ), 2 d flop
             # per (row, head, key) each: 2.5 times the forward's two
@@ -367,21 +401,27 @@ def cpu_baseline(wl, budget_s=20.0):
             return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
                     "sample": f"{len(rows)} of {n} prompt positions (every {step}th) incl. "
                               f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
-        if wl.kind == "prefill_bwd":
+        if wl.kind in ("prefill_bwd", "prefill_bwd_whole"):
             # gradients of single rows, selections taken from the GPU forward
-            sel = wl.plan.block_idx.cpu().numpy()
+            sel = (wl.cp.idx_buf.view(c.q.shape[0], c.k.shape[0], p.topk) if
+                   wl.kind == "prefill_bwd_whole" else wl.plan.block_idx).cpu().numpy()
+            dense_row = [False] * c.n_q
+            if wl.kind == "prefill_bwd_whole":
+                for (q0, q1, _, _, _), pc in zip(wl.cp.sched, wl.cp.plans):
+                    for r in range(q0, q1):
+                        dense_row[r] = pc.dense
             d_out = wl.d_out.float().cpu().numpy()
             sel_rows = [None] * c.n_q
             rows, i = [], 0
             step = max(1, c.n_q // 256)
             while time.perf_counter() - t0 < budget_s and i < c.n_q:
-                sel_rows[i] = [s[s >= 0] for s in sel[i]]
+                sel_rows[i] = None if dense_row[i] else [s[s >= 0] for s in sel[i]]
                 O.prefill_backward(c.q, c.k, c.v, sel_rows, p, d_out, rows=[i])
                 rows.append(i)
                 i += step
             dt = time.perf_counter() - t0
             return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{len(rows)} of {c.n_q} chunk queries (every {step}th): dq of "
+                    "sample": f"{len(rows)} of {c.n_q} queries (every {step}th): dq of "
                               f"the row and its dk/dv contributions, float64 numpy, 1 thread"}
         if wl.kind == "prefill":
             ck = O.compress_keys(c.k, p, "bf16")
@@ -560,7 +600,8 @@ def main():
             # a call of several kernels: no single-launch counter figure
             roof["traffic"] = None
             roof["kernels_in_call"] = w["launches_in_call"]
-            roof["algorithmic_gflop_per_call"] = roof.pop("algorithmic_gflop_per_launch")
+            if "algorithmic_gflop_per_launch" in roof:
+                roof["algorithmic_gflop_per_call"] = roof.pop("algorithmic_gflop_per_launch")
     else:
         achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -574,6 +615,9 @@ def main():
     if wl.kind == "prefill_whole":
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": 8192,
                     "chunks": len(wl.cp.plans)})
+    elif wl.kind == "prefill_bwd_whole":
+        cfg.update({"context": int(c.k.shape[1]), "chunk_queries": 8192,
+                    "chunks": len(wl.cp.plans), "pass": "backward (dq, dk, dv)"})
     elif wl.kind in ("prefill", "prefill_bwd"):
         cfg.update({"context": int(c.k.shape[1]), "chunk_queries": int(c.n_q)})
         if wl.kind == "prefill_bwd":
