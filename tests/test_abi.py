@@ -44,6 +44,9 @@ def lib():
                                                 i32, i32, P, P, P, P, sz, PP, P]
     lib.infllmv2_tree_verify.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P, i32,
                                          i32, i32, P, P, P, P, sz, PP, P]
+    lib.infllmv2_sparse_attn_prefill_backward.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64,
+                                                          i32, i32, i32, P, P, P, P, P, P, P,
+                                                          P, sz, PP, P]
     lib.Params = Params
     return lib
 
@@ -159,3 +162,30 @@ def test_attention_validation(lib):
               FAKE, None, FAKE, tneed - 256, params(lib), None) == WORKSPACE
     assert tv(1, FAKE, 16, FAKE, FAKE, 20000, 20000, FAKE, None, FAKE, 32, 2, 128, FAKE,
               FAKE, None, FAKE, tneed, params(lib), None) == INVALID  # no draft V
+
+
+def test_backward_validation(lib):
+    bwd = lib.infllmv2_sparse_attn_prefill_backward
+    ws = lib.infllmv2_workspace_size
+    need = ws(2, 64, 32, 2, 128, 20000, params(lib))
+    assert need > 64 * 32 * 8                                       # (lse, do.o) per pair
+    assert ws(2, 20001, 32, 2, 128, 20000, params(lib)) == 0        # n_q > n_k
+    dense_need = ws(2, 64, 32, 2, 128, 4000, params(lib))           # dense: no bitmap
+    assert 0 < dense_need < need
+
+    def call(dtype=1, n_q=64, n_k=20000, cap=20000, h_q=32, h_kv=2, d=128, idx=FAKE,
+             lse=FAKE, ws_ptr=FAKE, ws_bytes=None, p=None):
+        return bwd(dtype, FAKE, n_q, FAKE, FAKE, cap, n_k, h_q, h_kv, d, idx, FAKE, lse, FAKE,
+                   FAKE, FAKE, FAKE, ws_ptr, need if ws_bytes is None else ws_bytes,
+                   p if p is not None else params(lib), None)
+    assert call(dtype=0) == UNSUPPORTED                              # float32: bf16 only
+    assert call(lse=None) == INVALID                                 # lse is required
+    assert call(idx=None) == INVALID                                 # sparse needs block_idx
+    assert call(n_q=20001) == INVALID                                # more queries than keys
+    assert call(cap=100) == INVALID                                  # cap < n_k
+    assert call(h_q=6) == UNSUPPORTED                                # group size 3
+    assert call(p=params(lib, block_size=96)) == UNSUPPORTED         # block not 64-aligned
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws_ptr=None) == WORKSPACE
+    assert call(ws_ptr=ctypes.c_void_p(0x10010)) == WORKSPACE        # not 256-byte aligned
+    assert call(n_q=0) == OK                                         # nothing to do
