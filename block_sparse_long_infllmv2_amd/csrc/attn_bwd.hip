@@ -732,8 +732,10 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   if (dtype != INFLLMV2_BF16) return INFLLMV2_ERR_UNSUPPORTED;
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G) || r.B % kChunk != 0) return INFLLMV2_ERR_UNSUPPORTED;
-  // the dK/dV kernel's direct copies address Q, dO and meta with 32-bit offsets
-  if ((int64_t)n_q * h_q * d * 2 >= (1ll << 32)) return INFLLMV2_ERR_UNSUPPORTED;
+  // the dK/dV kernel's direct copies address Q, dO and meta with 32-bit
+  // offsets, and multiplies row indices in 24 bits
+  if ((int64_t)n_q * h_q * d * 2 >= (1ll << 32) || n_q >= (1 << 24))
+    return INFLLMV2_ERR_UNSUPPORTED;
   const BwdPlan pl = bwd_plan(n_q, h_q, h_kv, n_k, r);
   if (!ws || ws_bytes < pl.bytes || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
   if (n_q == 0) return INFLLMV2_OK;

@@ -267,7 +267,8 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
  *   ws >= infllmv2_workspace_size(INFLLMV2_OP_PREFILL_BWD, n_q, h_q, h_kv, d,
  *        n_k, p) bytes, 256-byte aligned.
  * bf16 only (INFLLMV2_F32 returns INFLLMV2_ERR_UNSUPPORTED), block_size a
- * multiple of 64, G in {1, 2, 4, 8, 16, 32}.
+ * multiple of 64, G in {1, 2, 4, 8, 16, 32}, n_q < 2^24 and
+ * n_q * h_q * d * 2 < 2^32 bytes (larger calls: split the chunk).
  */
 int infllmv2_sparse_attn_prefill_backward(int dtype, const void* q, int32_t n_q,
                                           const void* k, const void* v, int64_t cap,

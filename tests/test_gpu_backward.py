@@ -238,3 +238,13 @@ def test_backward_whole_prompt_in_chunks(B):
     check_grad(host(dq), rq, "chunked dq")
     check_grad(dk.cpu().numpy(), rk, "chunked dk")
     check_grad(dv.cpu().numpy(), rv, "chunked dv")
+
+
+@pytest.mark.parametrize("n_k,n_q,dense_len", [(1, 1, 8192), (40, 40, 8192), (700, 1, 0),
+                                               (63, 17, 0)])
+def test_backward_tiny_shapes(B, n_k, n_q, dense_len):
+    _say(f"backward tiny shape n_k={n_k} n_q={n_q} dense_len={dense_len}")
+    c = case(80 + n_k, n_k, n_q, 16, 2, 64, topk=4, dense_len=dense_len)
+    dense = n_k < dense_len
+    sel = None if dense else random_selection(81, n_q, n_k, 2, c.params)
+    compare(B, c, sel, f"tiny {n_k}x{n_q}", dense=dense)
