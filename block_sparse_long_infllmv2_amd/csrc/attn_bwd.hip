@@ -1,6 +1,7 @@
 // Gradients of the block-sparse prefill attention with the kept blocks fixed
 // (block selection is a top-k and has no gradient), bf16 inputs, float32
-// accumulation, on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16).
+// accumulation, on gfx950 matrix cores (v_mfma_f32_16x16x32_bf16); float32
+// inputs take a vector-ALU kernel (bwd_f32_kernel, at the end).
 // Sources: "MiniCPM 4.0" blog (shadowrocket9.top), InfLLM v2 section (the
 // sparse attention is trainable: the model is trained with it); "MiniCPM4:
 // running LLMs on phones and PCs" (xugj520.cn), section 1.1 (attention over
@@ -75,20 +76,23 @@ constexpr int kPlanThreads1 = 1024;
 // meta[row][h] = (lse * log2 e, sum_d do[row][h][d] * o[row][h][d]); D/8
 // lanes per pair.
 // ---------------------------------------------------------------------------
-template <int D>
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_dsum_kernel(BwdArgs a) {
-  constexpr int L = D / 8;
+  constexpr int E = Elem<T>::kPer16B;
+  constexpr int L = D / E;
+  const T* dO = reinterpret_cast<const T*>(a.d_out);
+  const T* O = reinterpret_cast<const T*>(a.out);
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t pair = gid / L;
   const int part = (int)(gid % L);
   const int64_t n_pairs = (int64_t)a.n_q * a.h_q;
   float acc = 0.0f;
   if (pair < n_pairs) {
-    float x[8], y[8];
-    Elem<uint16_t>::unpack(ldg16(a.d_out + pair * D + 8 * part), x);
-    Elem<uint16_t>::unpack(ldg16(a.out + pair * D + 8 * part), y);
+    float x[E], y[E];
+    Elem<T>::unpack(ldg16(dO + pair * D + E * part), x);
+    Elem<T>::unpack(ldg16(O + pair * D + E * part), y);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(x[i], y[i], acc);
+    for (int i = 0; i < E; ++i) acc = __builtin_fmaf(x[i], y[i], acc);
   }
 #pragma unroll
   for (int o = L / 2; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -622,6 +626,91 @@ void bwd_dq_kernel(BwdArgs a) {
   (void)KL;
 }
 
+// ---------------------------------------------------------------------------
+// float32 inputs: one wave per (row, head) on the vector ALU, for the
+// exact-precision callers (small shapes).  Per 64-key piece of a kept block:
+// lane j takes key j (s = q.k_j, dp = do.v_j, p, ds), then lane d accumulates
+// dq[d] += ds_j k_j[d] and adds scale ds_j q[d], p_j do[d] into dk, dv with
+// float32 atomics.  A block listed twice counts once.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(64) void bwd_f32_kernel(BwdArgs a) {
+  constexpr int R = D / 64;                        // dims per lane in the d phases
+  __shared__ float qs[D], dos[D], ps[64], dss[64];
+  const int rh = blockIdx.x, lane = threadIdx.x;
+  const int row = rh / a.h_q, head = rh % a.h_q;
+  const int G = a.h_q / a.h_kv, g = head / G;
+  const float* qf = reinterpret_cast<const float*>(a.q);
+  const float* kf = reinterpret_cast<const float*>(a.k);
+  const float* vf = reinterpret_cast<const float*>(a.v);
+  const float* dof = reinterpret_cast<const float*>(a.d_out);
+  for (int d = lane; d < D; d += 64) {
+    qs[d] = qf[(int64_t)rh * D + d];
+    dos[d] = dof[(int64_t)rh * D + d];
+  }
+  __syncthreads();
+  const float l2 = a.meta[2 * (int64_t)rh], dsum = a.meta[2 * (int64_t)rh + 1];
+  const int64_t pos = a.n_k - a.n_q + row;
+  const float* kg = kf + (int64_t)g * a.cap * D;
+  const float* vg = vf + (int64_t)g * a.cap * D;
+  float* dkg = a.dk + (int64_t)g * a.cap * D;
+  float* dvg = a.dv + (int64_t)g * a.cap * D;
+  float dq[R];
+#pragma unroll
+  for (int i = 0; i < R; ++i) dq[i] = 0.0f;
+  const int64_t own = pos / a.B;
+  const int n_list = a.dense ? (int)(own + 1) : a.topk;
+  const int32_t* lst = a.dense ? nullptr : a.block_idx + ((int64_t)row * a.h_kv + g) * a.topk;
+  for (int e = 0; e < n_list; ++e) {
+    int64_t b = e;
+    if (!a.dense) {
+      b = lst[e];
+      if (b < 0 || b >= a.n_b || b > own) continue;
+      bool dup = false;
+      for (int e2 = 0; e2 < e; ++e2) dup = dup || lst[e2] == b;
+      if (dup) continue;
+    }
+    const int64_t k_end = min((b + 1) * (int64_t)a.B, pos + 1);
+    for (int64_t key0 = b * a.B; key0 < k_end; key0 += 64) {
+      const int nv = (int)min((int64_t)64, k_end - key0);
+      float p = 0.0f, ds = 0.0f;
+      if (lane < nv) {
+        const float* kr = kg + (key0 + lane) * D;
+        const float* vr = vg + (key0 + lane) * D;
+        float s = 0.0f, dp = 0.0f;
+        for (int d = 0; d < D; d += 4) {
+          const float4 k4 = *reinterpret_cast<const float4*>(kr + d);
+          const float4 v4 = *reinterpret_cast<const float4*>(vr + d);
+          s = __builtin_fmaf(qs[d], k4.x, s); s = __builtin_fmaf(qs[d + 1], k4.y, s);
+          s = __builtin_fmaf(qs[d + 2], k4.z, s); s = __builtin_fmaf(qs[d + 3], k4.w, s);
+          dp = __builtin_fmaf(dos[d], v4.x, dp); dp = __builtin_fmaf(dos[d + 1], v4.y, dp);
+          dp = __builtin_fmaf(dos[d + 2], v4.z, dp); dp = __builtin_fmaf(dos[d + 3], v4.w, dp);
+        }
+        p = fast_exp2(__builtin_fmaf(s, a.scale_log2, -l2));
+        ds = p * (dp - dsum);
+      }
+      ps[lane] = p;
+      dss[lane] = ds;
+      __syncthreads();
+      for (int j = 0; j < nv; ++j) {
+        const float pj = ps[j], dsj = dss[j];
+        const int64_t kj = (key0 + j) * D;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+          const int d = lane + 64 * i;
+          dq[i] = __builtin_fmaf(dsj, kg[kj + d], dq[i]);
+          unsafeAtomicAdd(dkg + kj + d, a.scale * dsj * qs[d]);
+          unsafeAtomicAdd(dvg + kj + d, pj * dos[d]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+  float* dqo = reinterpret_cast<float*>(a.dq) + (int64_t)rh * D;
+#pragma unroll
+  for (int i = 0; i < R; ++i) dqo[lane + 64 * i] = a.scale * dq[i];
+}
+
 }  // namespace infllmv2
 
 // ---------------------------------------------------------------------------
@@ -729,9 +818,9 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !aligned16(d_out) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return INFLLMV2_ERR_INVALID_ARG;
-  if (dtype != INFLLMV2_BF16) return INFLLMV2_ERR_UNSUPPORTED;
   const int G = h_q / h_kv;
-  if (!group_ok_for_mfma(G) || r.B % kChunk != 0) return INFLLMV2_ERR_UNSUPPORTED;
+  const bool f32 = dtype == INFLLMV2_F32;
+  if (!f32 && (!group_ok_for_mfma(G) || r.B % kChunk != 0)) return INFLLMV2_ERR_UNSUPPORTED;
   // the dK/dV kernel's direct copies address Q, dO and meta with 32-bit
   // offsets, and multiplies row indices in 24 bits
   if ((int64_t)n_q * h_q * d * 2 >= (1ll << 32) || n_q >= (1 << 24))
@@ -755,15 +844,29 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   a.B = r.B; a.n_b = pl.n_b; a.nw = pl.nw; a.n_chunks = pl.n_chunks; a.seg_rows = pl.seg_rows;
   a.max_items = pl.max_items; a.dense = dense ? 1 : 0;
   a.scale = r.scale; a.scale_log2 = r.scale * kLog2e;
+  hipStream_t st = (hipStream_t)stream;
+  if (f32) {
+    if ((int64_t)n_q * h_q >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
+    const unsigned blocks = (unsigned)ceil_div((int64_t)n_q * h_q * (d / 4), 256);
+    if (d == 128) {
+      hipLaunchKernelGGL((bwd_dsum_kernel<float, 128>), dim3(blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_f32_kernel<128>), dim3((unsigned)(n_q * h_q)), dim3(64), 0, st, a);
+    } else {
+      hipLaunchKernelGGL((bwd_dsum_kernel<float, 64>), dim3(blocks), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((bwd_f32_kernel<64>), dim3((unsigned)(n_q * h_q)), dim3(64), 0, st, a);
+    }
+    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  }
   const int TT = dq_tile_tokens(G);
   a.n_tiles = (int)ceil_div(n_q, TT);
   if ((int64_t)a.n_tiles * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
-  hipStream_t st = (hipStream_t)stream;
 
   const int64_t dsum_threads = (int64_t)n_q * h_q * (d / 8);
   const unsigned dsum_blocks = (unsigned)ceil_div(dsum_threads, 256);
-  if (d == 128) hipLaunchKernelGGL((bwd_dsum_kernel<128>), dim3(dsum_blocks), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((bwd_dsum_kernel<64>), dim3(dsum_blocks), dim3(256), 0, st, a);
+  if (d == 128)
+    hipLaunchKernelGGL((bwd_dsum_kernel<uint16_t, 128>), dim3(dsum_blocks), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((bwd_dsum_kernel<uint16_t, 64>), dim3(dsum_blocks), dim3(256), 0, st, a);
   if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
   if (!dense) {
     const int64_t words = (int64_t)h_kv * pl.n_b * pl.nw;

@@ -266,9 +266,10 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
  *        dv may differ between runs.
  *   ws >= infllmv2_workspace_size(INFLLMV2_OP_PREFILL_BWD, n_q, h_q, h_kv, d,
  *        n_k, p) bytes, 256-byte aligned.
- * bf16 only (INFLLMV2_F32 returns INFLLMV2_ERR_UNSUPPORTED), block_size a
- * multiple of 64, G in {1, 2, 4, 8, 16, 32}, n_q < 2^24 and
- * n_q * h_q * d * 2 < 2^32 bytes (larger calls: split the chunk).
+ * bf16: matrix cores; block_size a multiple of 64, G in {1, 2, 4, 8, 16,
+ * 32}, n_q < 2^24 and n_q * h_q * d * 2 < 2^32 bytes (larger calls: split
+ * the chunk).  float32 (dq, like q, float32): a vector-ALU path meant for
+ * small shapes, any block_size and group size the forward accepts.
  */
 int infllmv2_sparse_attn_prefill_backward(int dtype, const void* q, int32_t n_q,
                                           const void* k, const void* v, int64_t cap,

@@ -70,12 +70,12 @@ def check_close(got, ref, dtype, where=""):
     return err.max(), err.mean()
 
 
-def check_grad(got, ref, where=""):
+def check_grad(got, ref, where="", dtype="bf16"):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
     assert np.all(np.isfinite(got)), f"{where}: non-finite gradient"
-    mx, mean = TOL["bf16"]
+    mx, mean = TOL[dtype]
     # floor: a gradient that vanishes in exact arithmetic (one key: dq = 0)
     # is held to 2e-5 absolute instead of a bar relative to its rounding noise
     scale = max(float(np.abs(ref).max()), GRAD_SCALE_FLOOR)

@@ -178,12 +178,12 @@ def test_backward_validation(lib):
         return bwd(dtype, FAKE, n_q, FAKE, FAKE, cap, n_k, h_q, h_kv, d, idx, FAKE, lse, FAKE,
                    FAKE, FAKE, FAKE, ws_ptr, need if ws_bytes is None else ws_bytes,
                    p if p is not None else params(lib), None)
-    assert call(dtype=0) == UNSUPPORTED                              # float32: bf16 only
+    assert call(dtype=7) == INVALID                                  # unknown dtype
     assert call(lse=None) == INVALID                                 # lse is required
     assert call(idx=None) == INVALID                                 # sparse needs block_idx
     assert call(n_q=20001) == INVALID                                # more queries than keys
     assert call(cap=100) == INVALID                                  # cap < n_k
-    assert call(h_q=6) == UNSUPPORTED                                # group size 3
+    assert call(h_q=6) == UNSUPPORTED                                # group size 3 (bf16)
     assert call(p=params(lib, block_size=96)) == UNSUPPORTED         # block not 64-aligned
     assert call(ws_bytes=need - 1) == WORKSPACE
     assert call(ws_ptr=None) == WORKSPACE

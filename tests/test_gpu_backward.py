@@ -34,8 +34,9 @@ def B():
     return binding
 
 
-def dev(x):
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).cuda()
+def dev(x, dtype="bf16"):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return (t.to(torch.bfloat16) if dtype == "bf16" else t).cuda()
 
 
 def host(t):
@@ -67,12 +68,12 @@ def run_backward(B, c, sel, d_out, dk0=None, dv0=None):
     p = c.params
     n_q, h_q, d = c.q.shape
     h_kv, n_k, _ = c.k.shape
-    q, k, v = dev(c.q), dev(c.k), dev(c.v)
+    q, k, v = dev(c.q, c.dtype), dev(c.k, c.dtype), dev(c.v, c.dtype)
     bi = torch.from_numpy(sel).cuda() if sel is not None else None
     out = torch.empty_like(q)
     lse = torch.empty((n_q, h_q), dtype=torch.float32, device="cuda")
     B.infllmv2_sparse_attn_prefill(q, k, v, n_k, bi, out, lse, p)
-    do = dev(d_out)
+    do = dev(d_out, c.dtype)
     dq = torch.empty_like(q)
     dk = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device="cuda")
     dv = torch.zeros_like(dk)
@@ -97,20 +98,20 @@ def sel_len(sel):
     return sel if isinstance(sel, int) else len(sel)
 
 
-def case(seed, n_k, n_q, h_q, h_kv, d, **pover):
+def case(seed, n_k, n_q, h_q, h_kv, d, dtype="bf16", **pover):
     p = Params(**pover)
-    return make_prefill(seed, n_k, n_q, h_q, h_kv, d, p, "bf16", n_planted=4, alpha=1.0,
+    return make_prefill(seed, n_k, n_q, h_q, h_kv, d, p, dtype, n_planted=4, alpha=1.0,
                         beta=1.5, name="bwd")
 
 
 def compare(B, c, sel, where, dense=False):
-    d_out = make_upstream_grad(7, c.n_q, c.q.shape[1], c.q.shape[2], "bf16")
+    d_out = make_upstream_grad(7, c.n_q, c.q.shape[1], c.q.shape[2], c.dtype)
     dq, dk, dv = run_backward(B, c, None if dense else sel, d_out)
     rows = [None] * c.n_q if dense else [[s[s >= 0] for s in row] for row in sel]
     rq, rk, rv = O.prefill_backward(c.q, c.k, c.v, rows, c.params, d_out)
-    check_grad(dq, rq, f"{where} dq")
-    check_grad(dk, rk, f"{where} dk")
-    check_grad(dv, rv, f"{where} dv")
+    check_grad(dq, rq, f"{where} dq", c.dtype)
+    check_grad(dk, rk, f"{where} dk", c.dtype)
+    check_grad(dv, rv, f"{where} dv", c.dtype)
     return dq, dk, dv, d_out
 
 
@@ -180,25 +181,33 @@ def test_backward_accumulates_into_dk_dv(B):
     assert np.array_equal(dv[~attended], dv0[~attended].astype(np.float64))
 
 
-def test_backward_rejects_f32_and_small_workspace(B):
+def test_backward_rejects_small_workspace(B):
     _say("backward argument checks")
     p = Params(dense_len=0, topk=4)
     n_q, n_k, h_q, h_kv, d = 8, 256, 4, 2, 64
-    q = torch.zeros((n_q, h_q, d), dtype=torch.float32, device="cuda")
-    k = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device="cuda")
+    q = torch.zeros((n_q, h_q, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((h_kv, n_k, d), dtype=torch.bfloat16, device="cuda")
     bi = torch.zeros((n_q, h_kv, 4), dtype=torch.int32, device="cuda")
     lse = torch.zeros((n_q, h_q), dtype=torch.float32, device="cuda")
-    dk = torch.zeros_like(k)
+    dk = torch.zeros((h_kv, n_k, d), dtype=torch.float32, device="cuda")
     nbytes = B.infllmv2_workspace_size(B.OP_PREFILL_BWD, n_q, h_q, h_kv, d, n_k, p)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    with pytest.raises(B.InfLLMv2Error, match="unsupported"):
-        B.infllmv2_sparse_attn_prefill_backward(q, k, k, n_k, bi, q, lse, q, q, dk, dk, ws, p)
-    qb = q.to(torch.bfloat16)
-    kb = k.to(torch.bfloat16)
     small = torch.empty(max(256, nbytes - 512), dtype=torch.uint8, device="cuda")
     with pytest.raises(B.InfLLMv2Error, match="workspace"):
-        B.infllmv2_sparse_attn_prefill_backward(qb, kb, kb, n_k, bi, qb, lse, qb, qb, dk, dk,
-                                                small, p)
+        B.infllmv2_sparse_attn_prefill_backward(q, k, k, n_k, bi, q, lse, q, q, dk, dk, small, p)
+
+
+@pytest.mark.parametrize("n_k,n_q,h_q,h_kv,d,bs,dense_len", [
+    (2048, 128, 2, 1, 64, 64, 0),          # the tiny float32 configuration's shape
+    (200, 200, 8, 2, 128, 64, 8192),       # dense
+    (1500, 90, 6, 3, 64, 32, 0),           # 32-token blocks, group of 2, three KV heads
+])
+def test_backward_f32(B, n_k, n_q, h_q, h_kv, d, bs, dense_len):
+    _say(f"backward float32 n_k={n_k} n_q={n_q} h_q={h_q} h_kv={h_kv} d={d} B={bs}")
+    c = case(90 + n_k, n_k, n_q, h_q, h_kv, d, dtype="f32", topk=8, block_size=bs,
+             dense_len=dense_len)
+    dense = n_k < dense_len
+    sel = None if dense else random_selection(91, n_q, n_k, h_kv, c.params)
+    compare(B, c, sel, f"f32 {n_k}x{n_q}", dense=dense)
 
 
 def test_backward_block192(B):
