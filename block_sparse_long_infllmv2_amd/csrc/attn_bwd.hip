@@ -21,8 +21,8 @@
 //   bwd_count   per (g, block): segments of at most kSegPairs (row, head)
 //               pairs, so that block 0, which every row keeps, is spread over
 //               many workgroups
-//   bwd_plan    one workgroup scans the segment counts into a list of work
-//               items (KV head, 64-key chunk, segment)
+//   bwd_plan    scans the segment counts into a list of work items (KV
+//               head, 64-key chunk, segment), 1024 units per workgroup
 //   bwd_dkdv    key-major: a workgroup of four waves owns one item; each wave
 //               holds 16 keys of K and V as MFMA operands and their dK^T, dV^T
 //               accumulators in registers (two waves per SIMD), and walks the
@@ -42,10 +42,13 @@
 //               the union of the tokens' kept blocks (K and V tiles staged in
 //               LDS by direct loads), and per 64-key chunk computes
 //               S^T = K Q^T, dP^T = V dO^T, dS^T, dQ^T += K^T dS^T.
+// float32 inputs: bwd_dsum, then bwd_f32 (one wave per (row, head)).
 #include "lds_tiles.h"
 
 namespace infllmv2 {
 
+// Element pointers hold bfloat16 bits; the float32 kernels reinterpret them
+// as float.
 struct BwdArgs {
   const uint16_t* q;          // [n_q][h_q][D]
   const uint16_t* k;          // [h_kv][cap][D]
@@ -136,42 +139,52 @@ __device__ __forceinline__ int dense_first_row(const BwdArgs& a, int chunk) {
   return r0 < 0 ? 0 : (int)(r0 < a.n_q ? r0 : a.n_q);
 }
 
-// One workgroup: exclusive scan of the per-unit item counts, items written in
-// (KV head, chunk, segment) order.
+// Work items in (KV head, chunk, segment) order.  Workgroup w owns units
+// [w NT, (w+1) NT): it sums the item counts of all earlier units (its base),
+// scans its own, and writes their items; the last workgroup stores the total.
+__device__ __forceinline__ void plan_unit(const BwdArgs& a, int e, int units, int total_e,
+                                          int& nseg, int& nch, int& c0, int& g) {
+  nseg = 0; nch = 0; c0 = 0; g = 0;
+  if (e >= total_e) return;
+  g = e / units;
+  const int u = e % units;
+  if (a.dense) {
+    const int cnt = a.n_q - dense_first_row(a, u);
+    nseg = (cnt + a.seg_rows - 1) / a.seg_rows;
+    nch = 1;
+    c0 = u;
+  } else {
+    nseg = a.nseg[e];
+    c0 = u * (a.B / kChunk);
+    nch = min(a.B / kChunk, a.n_chunks - c0);
+  }
+}
+
 __global__ __launch_bounds__(kPlanThreads1) void bwd_plan_kernel(BwdArgs a) {
-  __shared__ int scan_lds[kPlanThreads1 / 64];
+  constexpr int NT = kPlanThreads1;
+  __shared__ int scan_lds[NT / 64];
   const int tid = threadIdx.x;
-  const int cpb = a.B / kChunk;
   const int units = a.dense ? a.n_chunks : a.n_b;
   const int total_e = a.h_kv * units;
-  int carry = 0;
-  for (int base = 0; base < total_e; base += kPlanThreads1) {
-    const int e = base + tid;
-    int nseg = 0, nch = 0, c0 = 0, g = 0;
-    if (e < total_e) {
-      g = e / units;
-      const int u = e % units;
-      if (a.dense) {
-        const int cnt = a.n_q - dense_first_row(a, u);
-        nseg = (cnt + a.seg_rows - 1) / a.seg_rows;
-        nch = 1;
-        c0 = u;
-      } else {
-        nseg = a.nseg[e];
-        c0 = u * cpb;
-        nch = min(cpb, a.n_chunks - c0);
-      }
-    }
-    const int cnt_items = nseg * nch;
-    int tot;
-    const int off = carry + block_excl_scan<kPlanThreads1>(cnt_items, &tot, scan_lds);
-    for (int i = 0; i < cnt_items; ++i) {
-      if (off + i >= a.max_items) break;
-      a.items[off + i] = make_int2(g * a.n_chunks + c0 + i / nseg, i % nseg);
-    }
-    carry += tot;
+  const int e0 = blockIdx.x * NT;
+  int before = 0;
+  for (int e = tid; e < e0; e += NT) {
+    int nseg, nch, c0, g;
+    plan_unit(a, e, units, total_e, nseg, nch, c0, g);
+    before += nseg * nch;
   }
-  if (tid == 0) a.n_items[0] = min(carry, a.max_items);
+  int base;
+  block_excl_scan<NT>(before, &base, scan_lds);              // base = sum over threads
+  int nseg, nch, c0, g;
+  plan_unit(a, e0 + tid, units, total_e, nseg, nch, c0, g);
+  const int cnt_items = nseg * nch;
+  int tot;
+  const int off = base + block_excl_scan<NT>(cnt_items, &tot, scan_lds);
+  for (int i = 0; i < cnt_items; ++i) {
+    if (off + i >= a.max_items) break;
+    a.items[off + i] = make_int2(g * a.n_chunks + c0 + i / nseg, i % nseg);
+  }
+  if (blockIdx.x == gridDim.x - 1 && tid == 0) a.n_items[0] = min(base + tot, a.max_items);
 }
 
 // ---------------------------------------------------------------------------
@@ -879,7 +892,9 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
                        dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
   }
-  hipLaunchKernelGGL(bwd_plan_kernel, dim3(1), dim3(kPlanThreads1), 0, st, a);
+  const int plan_units = h_kv * (dense ? pl.n_chunks : pl.n_b);
+  hipLaunchKernelGGL(bwd_plan_kernel, dim3((unsigned)ceil_div(plan_units, kPlanThreads1)),
+                     dim3(kPlanThreads1), 0, st, a);
   if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
   INFLLMV2_TRY(d == 128 ? launch_dkdv<128>(G, a, dim3((unsigned)pl.max_items), st)
                         : launch_dkdv<64>(G, a, dim3((unsigned)pl.max_items), st));
