@@ -558,7 +558,6 @@ void bwd_dq_kernel(BwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0f70);
 
   using DT = DmaTile<D, NT, SW>;
-  constexpr int KL = DT::kLoads;
   DT dma;
   dma.init(tid);
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
@@ -644,7 +643,6 @@ void bwd_dq_kernel(BwdArgs a) {
       *reinterpret_cast<u32x2*>(orow + 16 * dt + 4 * hh) = wv;
     }
   }
-  (void)KL;
 }
 
 // ---------------------------------------------------------------------------
