@@ -265,7 +265,8 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
  *        different workgroups are float32 atomics, so the rounding of dk and
  *        dv may differ between runs.
  *   ws >= infllmv2_workspace_size(INFLLMV2_OP_PREFILL_BWD, n_q, h_q, h_kv, d,
- *        n_k, p) bytes, 256-byte aligned.
+ *        n_k, p) bytes, 256-byte aligned; contents on entry do not matter.
+ *        Calls that share a workspace must not overlap.
  * bf16: matrix cores; block_size a multiple of 64, G in {1, 2, 4, 8, 16,
  * 32}, n_q < 2^24 and n_q * h_q * d * 2 < 2^32 bytes (larger calls: split
  * the chunk).  float32 (dq, like q, float32): a vector-ALU path meant for
