@@ -195,3 +195,17 @@ def test_full_prefill_backward_sampled():
     span = slice(b * p.block_size, (b + 1) * p.block_size)
     check_grad(dk[0, span], rk[0, span], f"dk block {b}")
     check_grad(dv[0, span], rv[0, span], f"dv block {b}")
+    # invariants over every key of the context: each row's weights sum to 1,
+    # so summing dV over keys gives the group's summed upstream gradient; each
+    # row's dS sums to 0, so dK summed over keys vanishes
+    G = c.q.shape[1] // c.k.shape[0]
+    for g in range(c.k.shape[0]):
+        want = d_out[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        got = dv[g].sum(axis=0)
+        err = np.abs(got - want).max() / np.abs(want).max()
+        print(f"  sum of dv over keys, group {g}: relative max error {err:.2e}", flush=True)
+        assert err <= 1e-3
+        kmag = np.abs(dk[g]).sum(axis=0).max()
+        resid = np.abs(dk[g].sum(axis=0)).max() / kmag
+        print(f"  sum of dk over keys, group {g}: {resid:.2e} of sum |dk|", flush=True)
+        assert resid <= 1e-3
