@@ -257,3 +257,39 @@ def test_backward_tiny_shapes(B, n_k, n_q, dense_len):
     dense = n_k < dense_len
     sel = None if dense else random_selection(81, n_q, n_k, 2, c.params)
     compare(B, c, sel, f"tiny {n_k}x{n_q}", dense=dense)
+
+
+def test_backward_cache_larger_than_context(B):
+    """K/V caches with cap > n_k (room for later tokens), 4 KV heads: keys
+    past n_k are never read as data nor written in dk/dv."""
+    _say("backward with cap = n_k + 100, h_kv = 4, G = 4, d = 128")
+    p = Params(topk=6, dense_len=0)
+    n_k, n_q, h_q, h_kv, d, cap = 1900, 70, 16, 4, 128, 2000
+    c = make_prefill(95, n_k, n_q, h_q, h_kv, d, p, "bf16", n_planted=2, alpha=1.0, beta=1.5)
+    sel = random_selection(96, n_q, n_k, h_kv, p)
+    d_out = make_upstream_grad(97, n_q, h_q, d, "bf16")
+    kc = torch.full((h_kv, cap, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    kc[:, :n_k] = dev(c.k)
+    vc[:, :n_k] = dev(c.v)
+    q = dev(c.q)
+    bi = torch.from_numpy(sel).cuda()
+    out = torch.empty_like(q)
+    lse = torch.empty((n_q, h_q), dtype=torch.float32, device="cuda")
+    B.infllmv2_sparse_attn_prefill(q, kc, vc, n_k, bi, out, lse, p)
+    dq = torch.empty_like(q)
+    dk = torch.zeros((h_kv, cap, d), dtype=torch.float32, device="cuda")
+    dv = torch.zeros_like(dk)
+    ws = torch.empty(B.infllmv2_workspace_size(B.OP_PREFILL_BWD, n_q, h_q, h_kv, d, n_k, p),
+                     dtype=torch.uint8, device="cuda")
+    B.infllmv2_sparse_attn_prefill_backward(q, kc, vc, n_k, bi, out, lse, dev(d_out), dq, dk, dv,
+                                            ws, p)
+    torch.cuda.synchronize()
+    dkh = dk.cpu().numpy().astype(np.float64)
+    dvh = dv.cpu().numpy().astype(np.float64)
+    assert np.all(dkh[:, n_k:] == 0) and np.all(dvh[:, n_k:] == 0), "keys past n_k written"
+    rows = [[s[s >= 0] for s in row] for row in sel]
+    rq, rk, rv = O.prefill_backward(c.q, c.k, c.v, rows, p, d_out)
+    check_grad(host(dq), rq, "cap dq")
+    check_grad(dkh[:, :n_k], rk, "cap dk")
+    check_grad(dvh[:, :n_k], rv, "cap dv")
