@@ -395,12 +395,27 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
 //   keys at or above it (<= kSurvivors) go to LDS and wave 0 runs the bitwise
 //     threshold search on them; a full block-wide search is the fallback.
 // ---------------------------------------------------------------------------
+// c-th largest (1 <= c <= N) of N values: the one with exactly c - 1 values
+// ahead of it in (value descending, index ascending) order.
+template <int N>
+__device__ __forceinline__ uint32_t kth_largest(const uint32_t (&x)[N], int c) {
+  uint32_t v = 0u;
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    int ahead = 0;
+#pragma unroll
+    for (int i = 0; i < N; ++i) ahead += (x[i] > x[j]) || (i < j && x[i] == x[j]);
+    v = ahead == c - 1 ? x[j] : v;
+  }
+  return v;
+}
+
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArgs a) {
   __shared__ uint32_t surv[kSurvivors];
   __shared__ int scan4[kTopkThreads / 64];
   __shared__ uint32_t wave_lo[kTopkThreads / 64], wave_hi[kTopkThreads / 64];
-  __shared__ uint32_t sh_T;
+  __shared__ uint32_t sh_T, sh_hi;
   __shared__ int sh_exact;
   const int r = blockIdx.x / a.h_kv, g = blockIdx.x % a.h_kv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -443,22 +458,38 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArg
   uint32_t T = 0u;
   bool exact = need <= 0;
   if (need > 0) {
-    // Lower bound: the need-th largest of the 256 thread maxima (at least
-    // `need` threads hold a key >= it).  Wave 0 finds it with the bitwise
-    // search over those 256 values (4 per lane), starting below the bits
-    // they all share.
+    // Lower bound.  Only the first n_act threads hold eligible blocks; with
+    // c = ceil(need / n_act) keys per thread, let v be each thread's c-th
+    // largest key: any x with ceil(need / c) threads at v >= x has at least
+    // need keys >= x, so the ceil(need / c)-th largest v bounds the threshold
+    // from below (c = 1: the thread maxima).  Wave 0 finds it with the
+    // bitwise search over the 256 values (4 per lane), starting below the
+    // bits they all share.  A row of at most kSurvivors eligible blocks
+    // needs no bound: all its keys (>= 1) survive.  hi is the row's largest
+    // key.
     uint32_t lo = 0u, hi = 0xffffffffu;
     if (need <= kTopkThreads) {
-      surv[tid] = mx;                              // surv is free until the survivors
+      const int n_act = (n_elig + KPT - 1) / KPT;
+      const int c = min(KPT, (need + n_act - 1) / n_act);
+      const int need_t = (need + c - 1) / c;
+      surv[tid] = c > 1 ? kth_largest<KPT>(key, c) : mx;   // surv is free until the survivors
+      uint32_t wm = mx;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)wm, o, 64);
+        wm = y > wm ? y : wm;
+      }
+      if (lane == 0) wave_hi[wv] = wm;
       __syncthreads();
       if (wv == 0) {
         uint32_t m4[kTopkThreads / 64];
-        uint32_t mn = 0xffffffffu, mxx = 0u;
+        uint32_t mn = 0xffffffffu, mxx = 0u, top = 0u;
 #pragma unroll
         for (int j = 0; j < kTopkThreads / 64; ++j) {
           m4[j] = surv[lane + 64 * j];
           mn = m4[j] < mn ? m4[j] : mn;
           mxx = m4[j] > mxx ? m4[j] : mxx;
+          top = wave_hi[j] > top ? wave_hi[j] : top;
         }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
@@ -468,12 +499,14 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArg
           mxx = a2 > mxx ? a2 : mxx;
         }
         bool ex = false;
-        const uint32_t wl = threshold_search<kTopkThreads / 64>(m4, need, mn, mxx, &ex);
-        if (lane == 0) { wave_lo[0] = wl; wave_hi[0] = mxx; }
+        const uint32_t wl = n_elig <= kSurvivors
+                                ? 1u
+                                : threshold_search<kTopkThreads / 64>(m4, need_t, mn, mxx, &ex);
+        if (lane == 0) { wave_lo[0] = wl; sh_hi = top; }
       }
       __syncthreads();
       lo = wave_lo[0];
-      hi = wave_hi[0];
+      hi = sh_hi;
     }
     int mine = 0;
 #pragma unroll
