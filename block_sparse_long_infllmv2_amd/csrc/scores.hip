@@ -21,6 +21,8 @@ namespace infllmv2 {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreMaxWindows = 1024;   // window scores held in LDS per chunk
 constexpr int kMfmaMinRows = 64;         // fewer rows: the streaming kernel
+constexpr int kScoreMinWgs = 512;        // streaming kernel: workgroups aimed for
+constexpr int kScoreMinBlocks = 4;       // ... but at least this many blocks each
 
 struct ScoreArgs {
   const void* q;
@@ -642,11 +644,18 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.vec_store = (nb_cap % 4 == 0) && aligned16(scores);
   // blocks per workgroup: as many as keep the chunk's windows within the LDS
   // buffer (a chunk of n blocks spans at most (n*B + ks - 2)/s + 2 windows)
+  // and, for few rows, as few as still give about kScoreMinWgs workgroups
+  // (a decode row alone would otherwise leave most CUs without loads to issue)
   int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * r.s - r.ks + 2) / r.B);
   if (bpw > 32) bpw = 32;
   if (bpw < 1) return INFLLMV2_ERR_UNSUPPORTED;
-  a.blocks_per_wg = bpw;
   const int64_t nb_launch = (int64_t)max_pos / r.B + 1;
+  {
+    const int64_t spread = ceil_div(nb_launch * rows * h_kv, (int64_t)kScoreMinWgs);
+    const int64_t want = spread < kScoreMinBlocks ? kScoreMinBlocks : spread;
+    if (want < bpw) bpw = (int)want;
+  }
+  a.blocks_per_wg = bpw;
   a.chunks_per_row = (int)ceil_div(nb_launch, bpw);
   if ((int64_t)a.chunks_per_row * rows >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
