@@ -1428,25 +1428,42 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t stage[NS * TILE];   // K0 K1 V0 V1
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;    // seq: the row
-  int L = (int)a.n_k;
-  if constexpr (!TREE) {
-    // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
-    const int Lr = a.seqlens[seq];
-    L = Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr);
+  // The sequence length, the whole kept-block list (topk <= 128: two entries
+  // per lane) and the query are loaded together: the copies then wait for
+  // one memory round trip instead of a chain of dependent ones.
+  int Lr = (int)a.n_k;
+  if constexpr (!TREE) Lr = a.seqlens[seq];
+  const int32_t* lst =
+      a.block_idx ? a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk : nullptr;
+  int32_t lst0 = -1, lst1 = -1;                 // entries lane and 64 + lane
+  if (lst) {
+    if (lane < a.topk) lst0 = lst[lane];
+    if (64 + lane < a.topk) lst1 = lst[64 + lane];
   }
+  const int head = g * 16 + (lane & 15);
+  Row16<D> st;
+  st.init(lane);
+  {
+    const uint16_t* qrow = a.q + ((int64_t)seq * a.h_q + head) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int ks = 0; ks < Row16<D>::NKS; ++ks) {
+      const u32x4 wv = ldg16(qrow + 32 * ks);
+      st.q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
+    }
+  }
+  // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
+  const int L = TREE ? Lr : (Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr));
   const bool dense = L < a.dense_len || a.block_idx == nullptr;
   const int n_b = (L + a.B - 1) / a.B;
   const int cpb = (a.B + kChunk - 1) / kChunk;
-  const int32_t* lst = a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk;
   int n_entries = n_b;
   if (!dense) {
-    // kept blocks = the leading valid entries of the list (topk <= 128):
-    // one load per lane and a ballot instead of a chain of dependent loads
+    // kept blocks = the leading valid entries of the list
     n_entries = a.topk;
 #pragma unroll
     for (int half = 1; half >= 0; --half) {
       const int i = 64 * half + lane;
-      const int32_t b = i < a.topk ? lst[i] : -1;
+      const int32_t b = half ? lst1 : lst0;
       const uint64_t bad = __ballot(i < a.topk && !(b >= 0 && b < n_b));
       if (bad) n_entries = 64 * half + (int)__builtin_ctzll(bad);
     }
@@ -1457,11 +1474,14 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   const int u_begin = min(units, split * per);
   const int n = min(units, u_begin + per) - u_begin;
   // this split's block ids, one per lane (a split spans at most 64 entries),
-  // loaded before any direct copy is issued so that no global load of the
-  // loop makes the compiler wait on the copies
+  // taken from the loaded list with cross-lane reads
   const int e_base = u_begin / cpb;
   int blk_lane = e_base + lane;
-  if (!dense) blk_lane = e_base + lane < n_entries ? lst[e_base + lane] : 0;
+  if (!dense) {
+    const int e = e_base + lane;                // < n_entries <= 128 where used
+    const int32_t v0 = __shfl(lst0, e & 63, 64), v1 = __shfl(lst1, e & 63, 64);
+    blk_lane = e < n_entries ? (e < 64 ? v0 : v1) : 0;
+  }
   struct Unit { int key0, nv; };
   auto unit = [&](int u) -> Unit {
     if (TREE && u == ctx_units) return Unit{0, (int)a.n_rows};   // the draft chunk
@@ -1493,17 +1513,6 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
     return isd ? vdr : vseq + (un.nv > 0 ? (int64_t)un.key0 * D : 0);
   };
 
-  const int head = g * 16 + (lane & 15);
-  Row16<D> st;
-  st.init(lane);
-  {
-    const uint16_t* qrow = a.q + ((int64_t)seq * a.h_q + head) * D + 8 * (lane >> 4);
-#pragma unroll
-    for (int ks = 0; ks < Row16<D>::NKS; ++ks) {
-      const u32x4 wv = ldg16(qrow + 32 * ks);
-      st.q[ks] = *reinterpret_cast<const bf16x8*>(&wv);
-    }
-  }
   __builtin_amdgcn_s_waitcnt(0x0f70);   // Q has arrived before the direct loads start
 
   using DTK = DmaTile<D, 64, Swz16K<D>>;

@@ -201,8 +201,9 @@ int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_q,
  *   q    [batch][h_q][d]        k, v [batch][h_kv][cap][d]
  *   seqlens int32 [batch], 1 <= seqlens[b] <= cap
  *   max_seqlen host: upper bound of seqlens (sizes launch and workspace)
- *   block_idx int32 [batch][h_kv][topk] (ignored for dense sequences; may be
- *            NULL when max_seqlen < dense_len)
+ *   block_idx int32 [batch][h_kv][topk] (may be NULL when max_seqlen <
+ *            dense_len; when not NULL every row must be readable: the rows
+ *            of dense sequences are read and their values ignored)
  *   out  [batch][h_q][d]        lse float32 [batch][h_q] or NULL
  *   ws   >= infllmv2_workspace_size(INFLLMV2_OP_DECODE, batch, h_q, h_kv, d,
  *            max_seqlen, p) bytes, 256-byte aligned; contents on entry do
