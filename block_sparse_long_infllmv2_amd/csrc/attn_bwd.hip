@@ -128,6 +128,27 @@ __global__ __launch_bounds__(256) void bwd_mark_kernel(BwdArgs a) {
   atomicOr(a.bitmap + ((int64_t)g * a.n_b + b) * a.nw + (row >> 5), 1u << (row & 31));
 }
 
+// Bitmap column of one 32-row word w for KV head g (workgroup (w, g)): the
+// rows' kept blocks are ORed into an LDS copy of the n_b words, which is then
+// written whole, so the bitmap needs no clearing and no global atomics.
+constexpr int kMarkLdsBlocks = 16384;          // n_b up to this: the LDS column
+__global__ __launch_bounds__(256) void bwd_mark_lds_kernel(BwdArgs a) {
+  extern __shared__ uint32_t col[];
+  const int w = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  for (int b = tid; b < a.n_b; b += 256) col[b] = 0u;
+  __syncthreads();
+  const int r0 = 32 * w;
+  const int n_e = min(32, a.n_q - r0) * a.topk;
+  for (int e = tid; e < n_e; e += 256) {
+    const int rr = e / a.topk, i = e - rr * a.topk;
+    const int32_t b = a.block_idx[((int64_t)(r0 + rr) * a.h_kv + g) * a.topk + i];
+    if (b >= 0 && b < a.n_b) atomicOr(&col[b], 1u << rr);
+  }
+  __syncthreads();
+  uint32_t* out = a.bitmap + (int64_t)g * a.n_b * a.nw + w;
+  for (int b = tid; b < a.n_b; b += 256) out[(int64_t)b * a.nw] = col[b];
+}
+
 // one wave per (g, block): rows that kept it -> segments of seg_rows rows
 __global__ __launch_bounds__(256) void bwd_count_kernel(BwdArgs a) {
   const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -896,12 +917,18 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
     hipLaunchKernelGGL((bwd_dsum_kernel<uint16_t, 64>), dim3(dsum_blocks), dim3(256), 0, st, a);
   if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
   if (!dense) {
-    const int64_t words = (int64_t)h_kv * pl.n_b * pl.nw;
-    const int64_t fb = ceil_div(words, 256);
-    hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)(fb < 4096 ? fb : 4096)), dim3(256), 0, st,
-                       a.bitmap, words);
-    const int64_t marks = (int64_t)n_q * h_kv * r.topk;
-    hipLaunchKernelGGL(bwd_mark_kernel, dim3((unsigned)ceil_div(marks, 256)), dim3(256), 0, st, a);
+    if (pl.n_b <= kMarkLdsBlocks) {
+      hipLaunchKernelGGL(bwd_mark_lds_kernel, dim3((unsigned)pl.nw, (unsigned)h_kv), dim3(256),
+                         (size_t)pl.n_b * 4, st, a);
+    } else {
+      const int64_t words = (int64_t)h_kv * pl.n_b * pl.nw;
+      const int64_t fb = ceil_div(words, 256);
+      hipLaunchKernelGGL(bwd_fill_kernel, dim3((unsigned)(fb < 4096 ? fb : 4096)), dim3(256), 0,
+                         st, a.bitmap, words);
+      const int64_t marks = (int64_t)n_q * h_kv * r.topk;
+      hipLaunchKernelGGL(bwd_mark_kernel, dim3((unsigned)ceil_div(marks, 256)), dim3(256), 0, st,
+                         a);
+    }
     hipLaunchKernelGGL(bwd_count_kernel, dim3((unsigned)ceil_div((int64_t)h_kv * pl.n_b, 4)),
                        dim3(256), 0, st, a);
     if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
