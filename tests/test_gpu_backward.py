@@ -293,3 +293,13 @@ def test_backward_cache_larger_than_context(B):
     check_grad(host(dq), rq, "cap dq")
     check_grad(dkh[:, :n_k], rk, "cap dk")
     check_grad(dvh[:, :n_k], rv, "cap dv")
+
+
+def test_backward_more_blocks_than_the_lds_bitmap_column(B):
+    """n_b = 16401 blocks, more than the 16384-word LDS column of the row
+    bitmap: the bitmap is cleared and marked with global atomics instead."""
+    n_k = 64 * 16400 + 37
+    _say(f"backward n_k={n_k} (16401 blocks) n_q=40 G=2 d=64 topk=4")
+    c = case(70, n_k, 40, 2, 1, 64, topk=4, dense_len=0)
+    sel = random_selection(71, c.n_q, n_k, 1, c.params)
+    compare(B, c, sel, "16401 blocks")
