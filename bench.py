@@ -487,8 +487,9 @@ def main():
                          "for scaling FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}); the path is "
-              "single-GPU and sharding is described in DESIGN.md, not run.", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the path is "
+              "built and measured on one GPU; a multi-GPU run is not implemented.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -25,7 +25,7 @@ It computes, slowly and literally, in float64, what the method defines:
     (xugj520.cn, section 1.1 technical notes; the pomoai.com CPM.cu article,
     section 2 on the tree verification structure).
 
-Readings where the pages leave a step open (each one listed in the design doc):
+Readings where the pages leave a step open:
   R3  dense iff the sequence's total KV length n_k < dense_len.
   R5  only full kernel windows exist (no padded tail window).
   R6  a window is visible to a query at position p iff it ends at or before p.
