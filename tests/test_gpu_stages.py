@@ -257,6 +257,24 @@ def test_prefill_bf16_block128(B, PL):
     _check_prefill(plan, ck, c, rows=list(range(0, 120, 4)) + [119])
 
 
+@pytest.mark.parametrize("bs,n_k,n_q,h_q,h_kv,d,topk,dtype", [
+    (96, 5000, 150, 32, 2, 128, 8, "bf16"),   # 16-head groups; last block 8 keys
+    (96, 3030, 100, 8, 2, 64, 8, "bf16"),     # G = 4 (32-row tiles); last block 54 keys
+    (32, 2500, 120, 32, 2, 128, 24, "bf16"),  # one 32-key chunk per block
+    (32, 2000, 80, 16, 2, 64, 16, "bf16"),    # G = 8
+    (96, 2000, 100, 2, 1, 64, 8, "f32"),
+])
+def test_prefill_blocks_not_multiple_of_64(B, PL, bs, n_k, n_q, h_q, h_kv, d, topk, dtype):
+    # a 96-token block is a full and a half 64-key chunk, a 32-token block a
+    # half chunk; chunks past the context hold no keys
+    _say(f"prefill {dtype} block_size={bs} n_k={n_k} n_q={n_q} h_q={h_q} h_kv={h_kv} d={d}")
+    p = Params(block_size=bs, topk=topk, dense_len=0)
+    c = make_prefill(17, n_k=n_k, n_q=n_q, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
+                     n_planted=3, alpha=1.5, beta=1.5)
+    plan, ck = _run_prefill(B, PL, c)
+    _check_prefill(plan, ck, c, rows=sorted(set(list(range(0, n_q, 4)) + [n_q - 1, n_q - 2])))
+
+
 def test_prefill_bf16_dense_below_dense_len(B, PL):
     _say("prefill bf16 dense")
     p = Params(dense_len=4096)
@@ -352,6 +370,16 @@ def test_decode_block128(B, PL):
     _check_decode(plan, c)
 
 
+@pytest.mark.parametrize("bs,topk", [(96, 8), (32, 24)])
+def test_decode_blocks_not_multiple_of_64(B, PL, bs, topk):
+    _say(f"decode bf16 block_size={bs} topk={topk}")
+    p = Params(block_size=bs, topk=topk, dense_len=2048)
+    c = make_decode(16, [100, 2047, 2048, 5000, 9001, 200, 4130], h_q=32, h_kv=2, d=128,
+                    params=p, dtype="bf16", planted_per_token=1 / 512)
+    plan = _run_decode(B, PL, c)
+    _check_decode(plan, c)
+
+
 def test_decode_large_batch_fewer_splits(B, PL):
     # 40 sequences x 2 KV heads: the split count falls to ceil(512 / 80) = 7
     _say("decode bf16 batch 40")
@@ -384,6 +412,7 @@ def test_decode_repeated_calls_reuse_workspace(B, PL):
                                                         ("bf16", 5000, 16, 8192, 64),
                                                         ("bf16", 9000, 40, 0, 64),
                                                         ("bf16", 9000, 16, 0, 128),
+                                                        ("bf16", 9000, 16, 0, 96),
                                                         ("f32", 3000, 7, 0, 64)])
 def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len, bs):
     _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len} block={bs}")
