@@ -408,16 +408,22 @@ def test_decode_repeated_calls_reuse_workspace(B, PL):
 
 
 # ----------------------------------------------------------------- tree ----
-@pytest.mark.parametrize("dtype,n_ctx,T,dense_len,bs", [("bf16", 12000, 16, 8192, 64),
-                                                        ("bf16", 5000, 16, 8192, 64),
-                                                        ("bf16", 9000, 40, 0, 64),
-                                                        ("bf16", 9000, 16, 0, 128),
-                                                        ("bf16", 9000, 16, 0, 96),
-                                                        ("f32", 3000, 7, 0, 64)])
-def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len, bs):
-    _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len} block={bs}")
+@pytest.mark.parametrize("dtype,n_ctx,T,dense_len,bs,heads", [
+    ("bf16", 12000, 16, 8192, 64, (32, 2, 128)),
+    ("bf16", 5000, 16, 8192, 64, (32, 2, 128)),
+    ("bf16", 9000, 40, 0, 64, (32, 2, 128)),
+    ("bf16", 9000, 16, 0, 128, (32, 2, 128)),
+    ("bf16", 9000, 16, 0, 96, (32, 2, 128)),
+    # other group sizes: union planner and the 32-row tile kernel
+    ("bf16", 9000, 16, 0, 64, (8, 2, 64)),       # G = 4
+    ("bf16", 6000, 20, 0, 64, (16, 2, 128)),     # G = 8
+    ("bf16", 7000, 16, 8192, 64, (8, 2, 128)),   # G = 4, dense
+    ("f32", 3000, 7, 0, 64, (4, 2, 64))])
+def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len, bs, heads):
+    h_q, h_kv, d = heads
+    _say(f"tree {dtype} n_ctx={n_ctx} T={T} dense_len={dense_len} block={bs} "
+         f"h_q={h_q} h_kv={h_kv} d={d}")
     p = Params(dense_len=dense_len, topk=16 if bs == 64 else 8, block_size=bs)
-    h_q, h_kv, d = (32, 2, 128) if dtype == "bf16" else (4, 2, 64)
     c = make_tree(8, n_ctx=n_ctx, n_draft=T, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
                   n_planted=max(1, n_ctx // 2048))
     q = dev(c.q, dtype)
