@@ -60,10 +60,12 @@ def _check_ck(got, ref, dtype, where):
         np.testing.assert_allclose(got, ref, rtol=1e-6, atol=1e-7)
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 64)])
-def test_compress_keys(B, dtype, d):
-    _say(f"compress {dtype} d={d}")
-    p = Params()
+@pytest.mark.parametrize("dtype,d,ks,s", [("bf16", 128, 32, 16), ("f32", 64, 32, 16),
+                                         ("bf16", 64, 32, 16), ("bf16", 128, 64, 32),
+                                         ("f32", 64, 48, 16), ("bf16", 128, 32, 32)])
+def test_compress_keys(B, dtype, d, ks, s):
+    _say(f"compress {dtype} d={d} kernel {ks}/{s}")
+    p = Params(kernel_size=ks, kernel_stride=s)
     rng = np.random.default_rng(1)
     lens = [1000, 333, 31]
     cap = 1024
@@ -73,7 +75,7 @@ def test_compress_keys(B, dtype, d):
         k[i, :, :L] = rng.standard_normal((h_kv, L, d))
     kk = dev(k, dtype)
     host_k = host(kk)
-    nc_cap = O.num_windows(cap, 32, 16)
+    nc_cap = O.num_windows(cap, ks, s)
     ck = torch.full((3, h_kv, nc_cap, d), 7.0, dtype=tdt(dtype), device="cuda")
     B.infllmv2_compress_keys(kk, torch.tensor(lens, dtype=torch.int32, device="cuda"), 0,
                              nc_cap, ck, p)
@@ -103,7 +105,25 @@ def test_compress_keys(B, dtype, d):
     ("f32", 128, 12, 2, 12, 64, 1)])
 def test_block_scores_on_oracle_ck(B, dtype, d, h_q, h_kv, rows, bs, mode):
     _say(f"scores {dtype} d={d} h_q={h_q} h_kv={h_kv} rows={rows} block={bs} mode={mode}")
-    p = Params(dense_len=0, block_size=bs, score_mode=mode)
+    _scores_case(B, dtype, d, h_q, h_kv, rows, Params(dense_len=0, block_size=bs,
+                                                      score_mode=mode))
+
+
+@pytest.mark.parametrize("ks,s,bs,rows", [
+    (64, 32, 128, 300),   # ks = 2s, B = 4s: matrix-core kernel at stride 32
+    (64, 32, 256, 300),   # B = 8s
+    (64, 32, 128, 12),    # streaming kernel
+    (32, 32, 64, 12),     # windows that do not overlap (ks = s)
+    (48, 16, 64, 300),    # ks = 3s: the streaming kernel also for many rows
+])
+def test_block_scores_window_geometries(B, ks, s, bs, rows):
+    _say(f"scores bf16 kernel {ks}/{s} block={bs} rows={rows}")
+    _scores_case(B, "bf16", 128, 32, 2, rows,
+                 Params(dense_len=0, block_size=bs, kernel_size=ks, kernel_stride=s))
+
+
+def _scores_case(B, dtype, d, h_q, h_kv, rows, p):
+    mode, bs = p.score_mode, p.block_size
     n_k = 5000
     c = make_prefill(3, n_k=n_k, n_q=1, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
                      n_planted=5, alpha=1.5, beta=1.5)
