@@ -128,12 +128,26 @@ def _i32(t, name):
     return _ptr(t)
 
 
+def _need(t, name, shape, dtype=None, optional=False):
+    """The library sees raw pointers only: a buffer of another shape or dtype
+    than the call's sizes imply would be read or written out of bounds, so
+    it is rejected here, before any launch."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
 # ---------------------------------------------------------------- C calls --
 def infllmv2_compress_keys(k_cache, seqlens, m_begin, m_end, ck_cache, params):
     """k_cache [batch][h_kv][cap][d] -> ck_cache [batch][h_kv][nc_cap][d]."""
     batch, h_kv, cap, d = k_cache.shape
-    assert ck_cache.shape[:2] == (batch, h_kv) and ck_cache.shape[3] == d
-    assert ck_cache.dtype == k_cache.dtype
+    _need(ck_cache, "ck_cache", (batch, h_kv, ck_cache.shape[2], d), k_cache.dtype)
+    _need(seqlens, "seqlens", (batch,), torch.int32)
     p = to_params(params)
     _check(LIB.infllmv2_compress_keys(_dt(k_cache), _ptr(k_cache), batch, h_kv, cap, d,
                                       _i32(seqlens, "seqlens"), int(m_begin), int(m_end),
@@ -146,7 +160,11 @@ def infllmv2_block_scores(q, row_seq, row_pos, ck_cache, seqlens, scores, max_po
     """q [rows][h_q][d], ck [batch][h_kv][nc_cap][d] -> scores [rows][h_kv][nb_cap]."""
     rows, h_q, d = q.shape
     batch, hk, nc_cap, _ = ck_cache.shape
-    assert scores.dtype == torch.float32 and scores.shape[:2] == (rows, hk)
+    _need(ck_cache, "ck_cache", (batch, hk, nc_cap, d), q.dtype)
+    _need(scores, "scores", (rows, hk, scores.shape[2]), torch.float32)
+    _need(row_seq, "row_seq", (rows,), torch.int32, optional=True)
+    _need(row_pos, "row_pos", (rows,), torch.int32, optional=True)
+    _need(seqlens, "seqlens", (batch,), torch.int32)
     p = to_params(params)
     _check(LIB.infllmv2_block_scores(_dt(q), _ptr(q), rows, _i32(row_seq, "row_seq"),
                                      _i32(row_pos, "row_pos"), h_q, hk, d, _ptr(ck_cache),
@@ -159,7 +177,12 @@ def infllmv2_select_topk(scores, row_seq, row_pos, seqlens, block_idx, params):
     """scores [rows][h_kv][nb_cap] -> block_idx [rows][h_kv][topk] int32."""
     rows, h_kv, nb_cap = scores.shape
     p = to_params(params)
-    assert block_idx.dtype == torch.int32 and block_idx.shape == (rows, h_kv, p.topk)
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
+    _need(block_idx, "block_idx", (rows, h_kv, p.topk), torch.int32)
+    _need(row_seq, "row_seq", (rows,), torch.int32, optional=True)
+    _need(row_pos, "row_pos", (rows,), torch.int32, optional=True)
+    _need(seqlens, "seqlens", (seqlens.shape[0],), torch.int32)
     _check(LIB.infllmv2_select_topk(_ptr(scores), rows, _i32(row_seq, "row_seq"),
                                     _i32(row_pos, "row_pos"), h_kv, nb_cap,
                                     _i32(seqlens, "seqlens"), seqlens.shape[0],
@@ -172,6 +195,11 @@ def infllmv2_sparse_attn_prefill(q, k_cache, v_cache, n_k, block_idx, out, lse, 
     n_q, h_q, d = q.shape
     h_kv, cap, _ = k_cache.shape
     p = to_params(params)
+    _need(k_cache, "k_cache", (h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (h_kv, cap, d), q.dtype)
+    _need(out, "out", (n_q, h_q, d), q.dtype)
+    _need(lse, "lse", (n_q, h_q), torch.float32, optional=True)
+    _need(block_idx, "block_idx", (n_q, h_kv, p.topk), torch.int32, optional=True)
     _check(LIB.infllmv2_sparse_attn_prefill(_dt(q), _ptr(q), n_q, _ptr(k_cache),
                                             _ptr(v_cache), cap, int(n_k), h_q, h_kv, d,
                                             _i32(block_idx, "block_idx"), _ptr(out), _ptr(lse),
@@ -190,6 +218,13 @@ def infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, max_seqlen, block_
     batch, h_q, d = q.shape
     _, h_kv, cap, _ = k_cache.shape
     p = to_params(params)
+    _need(k_cache, "k_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(seqlens, "seqlens", (batch,), torch.int32)
+    _need(out, "out", (batch, h_q, d), q.dtype)
+    _need(lse, "lse", (batch, h_q), torch.float32, optional=True)
+    _need(block_idx, "block_idx", (batch, h_kv, p.topk), torch.int32, optional=True)
+    _need(ws, "ws", (ws.numel(),), torch.uint8)
     _check(LIB.infllmv2_sparse_attn_decode(_dt(q), _ptr(q), batch, _ptr(k_cache),
                                            _ptr(v_cache), cap, _i32(seqlens, "seqlens"),
                                            int(max_seqlen), h_q, h_kv, d,
@@ -207,6 +242,15 @@ def infllmv2_tree_verify(q, k_cache, v_cache, n_ctx, k_draft, v_draft, tree_mask
     p = to_params(params)
     if tree_mask.dtype not in (torch.int64, torch.uint64):
         raise TypeError("tree_mask must be a 64-bit integer tensor")
+    _need(tree_mask, "tree_mask", (T,))
+    _need(k_cache, "k_cache", (h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (h_kv, cap, d), q.dtype)
+    _need(k_draft, "k_draft", (h_kv, T, d), q.dtype)
+    _need(v_draft, "v_draft", (h_kv, T, d), q.dtype)
+    _need(out, "out", (T, h_q, d), q.dtype)
+    _need(lse, "lse", (T, h_q), torch.float32, optional=True)
+    _need(block_idx, "block_idx", (T, h_kv, p.topk), torch.int32, optional=True)
+    _need(ws, "ws", (ws.numel(),), torch.uint8)
     _check(LIB.infllmv2_tree_verify(_dt(q), _ptr(q), T, _ptr(k_cache), _ptr(v_cache), cap,
                                     int(n_ctx), _ptr(k_draft), _ptr(v_draft), _ptr(tree_mask),
                                     h_q, h_kv, d, _i32(block_idx, "block_idx"), _ptr(out),
@@ -223,8 +267,15 @@ def infllmv2_sparse_attn_prefill_backward(q, k_cache, v_cache, n_k, block_idx, o
     n_q, h_q, d = q.shape
     h_kv, cap, _ = k_cache.shape
     p = to_params(params)
-    if dk.dtype != torch.float32 or dv.dtype != torch.float32:
-        raise TypeError("dk and dv must be float32")
+    _need(k_cache, "k_cache", (h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (h_kv, cap, d), q.dtype)
+    for name, t in (("out", out), ("d_out", d_out), ("dq", dq)):
+        _need(t, name, (n_q, h_q, d), q.dtype)
+    _need(lse, "lse", (n_q, h_q), torch.float32)
+    _need(dk, "dk", (h_kv, cap, d), torch.float32)
+    _need(dv, "dv", (h_kv, cap, d), torch.float32)
+    _need(block_idx, "block_idx", (n_q, h_kv, p.topk), torch.int32, optional=True)
+    _need(ws, "ws", (ws.numel(),), torch.uint8)
     _check(LIB.infllmv2_sparse_attn_prefill_backward(
         _dt(q), _ptr(q), n_q, _ptr(k_cache), _ptr(v_cache), cap, int(n_k), h_q, h_kv, d,
         _i32(block_idx, "block_idx"), _ptr(out), _ptr(lse), _ptr(d_out), _ptr(dq), _ptr(dk),
