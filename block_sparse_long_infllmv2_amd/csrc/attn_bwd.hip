@@ -16,8 +16,10 @@
 //
 // Kernels (in launch order):
 //   bwd_dsum    per (row, head): lse * log2(e) and dsum = do . o (float32)
-//   fill        clears the row bitmap (sparse chunks only)
 //   bwd_mark    bitmap[g][b] bit i set when row i kept block b for KV head g
+//               (sparse chunks only): one workgroup per 32-row word column,
+//               built in LDS and written whole; above 16384 blocks a fill
+//               kernel clears the bitmap and global atomics set the bits
 //   bwd_count   per (g, block): segments of at most kSegPairs (row, head)
 //               pairs, so that block 0, which every row keeps, is spread over
 //               many workgroups
