@@ -45,8 +45,10 @@ Readings where the pages leave a step open:
   R13 prefill queries are the last n_q positions of the KV; decode's query
       sits at seqlen-1 with its own K/V already stored.
   R14 mask bit j of mask[i] (LSB first) means draft i may attend draft j;
-      drafts are not part of block selection, which runs over the context
-      as seen from its last position.
+      a draft always attends itself, whether or not its own bit is set, and
+      bits at or above the draft count are ignored; drafts are not part of
+      block selection, which runs over the context as seen from its last
+      position.
   R15 head h belongs to KV group floor(h * h_kv / h_q).
   R16 compressed keys are stored in K's dtype (round-to-nearest-even).
   R18 if a query has no more eligible blocks than k, it keeps all of them.
@@ -435,20 +437,18 @@ def tree_verify(q, k, v, k_draft, v_draft, mask, params, dtype: str,
     if not dense and ck is None:
         ck = compress_keys(k, params, dtype)
     res = {"o": {}, "lse": {}, "S": {}, "sel": {}, "ck": ck, "dense": dense}
+    n_b = -(-n_ctx // params.block_size)
     for i in drafts:
         bits = int(mask[i])
-        anc = [j for j in range(T) if (bits >> j) & 1]
+        # bit j (LSB first) of mask[i]: draft i attends draft j; the draft
+        # always attends itself, and bits at or above T name no draft (R14)
+        anc = sorted({i} | {j for j in range(T) if (bits >> j) & 1})
         extra = (kd[:, anc], vd[:, anc])
         if dense:
-            h_q, d = q[i].shape
-            h_kv = k.shape[0]
-            scale = _scale(params, d)
-            o = np.zeros((h_q, d)); lse = np.zeros(h_q)
-            for h in range(h_q):
-                g = _group_of_head(h, h_q, h_kv)
-                keys = np.concatenate([k[g], extra[0][g]], axis=0)
-                vals = np.concatenate([v[g], extra[1][g]], axis=0)
-                o[h], lse[h] = attend(q[i, h], keys, vals, scale)
+            # dense context (R3): every context block, i.e. every key
+            # 0 .. n_ctx-1, in the same softmax as the drafts
+            every = [np.arange(n_b)] * k.shape[0]
+            o, lse = attend_selected(q[i], k, v, every, pos, params, extra=extra)
             res["o"][i], res["lse"][i] = o, lse
             continue
         o, lse, S, sel = _sparse_row(q[i], k, v, ck, pos, params, extra=extra)

@@ -437,6 +437,82 @@ def test_tree_non_ancestor_drafts_do_not_matter_and_self_only():
     assert np.abs(r3["o"][3] - r["o"][3]).max() > 1e-6
 
 
+def test_tree_dense_chain_equals_causal_prefill_of_context_plus_drafts():
+    # context shorter than dense_len: with chain parents (draft i's ancestors
+    # are drafts 0..i) the drafts are just the next T tokens of one sequence,
+    # so draft i's output is row n_ctx+i of dense causal attention over the
+    # n_ctx+T tokens (torch SDPA with is_causal, float64)
+    p = Params(topk=4, dense_len=4096)
+    T, n_ctx, h_q, h_kv, d = 5, 700, 4, 2, 16
+    c = make_tree(18, n_ctx=n_ctx, n_draft=T, h_q=h_q, h_kv=h_kv, d=d, params=p,
+                  dtype="f32", n_planted=2, parents=[-1, 0, 1, 2, 3])
+    r = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, "f32")
+    assert r["dense"] and not r["sel"]
+    keys = torch.from_numpy(np.concatenate([c.k, c.k_draft], axis=1).astype(np.float64))
+    vals = torch.from_numpy(np.concatenate([c.v, c.v_draft], axis=1).astype(np.float64))
+    n = n_ctx + T
+    for h in range(h_q):
+        g = h * h_kv // h_q
+        # queries of the whole sequence: the drafts' own at the last T rows
+        qq = torch.zeros((n, d), dtype=torch.float64)
+        qq[n_ctx:] = torch.from_numpy(c.q[:, h].astype(np.float64))
+        o = torch.nn.functional.scaled_dot_product_attention(
+            qq[None, None], keys[g][None, None], vals[g][None, None],
+            is_causal=True, scale=0.25)[0, 0].numpy()
+        logits = 0.25 * (qq[n_ctx:] @ keys[g].T)
+        causal = torch.arange(n)[None, :] <= (n_ctx + torch.arange(T))[:, None]
+        lse = torch.logsumexp(logits.masked_fill(~causal, -math.inf), dim=1).numpy()
+        for i in range(T):
+            np.testing.assert_allclose(r["o"][i][h], o[n_ctx + i], atol=1e-12)
+            np.testing.assert_allclose(r["lse"][i][h], lse[i], atol=1e-12)
+
+
+def test_tree_dense_self_only_equals_sdpa_over_context_and_self():
+    p = Params(topk=4, dense_len=4096)
+    T, n_ctx = 4, 300
+    c = make_tree(19, n_ctx=n_ctx, n_draft=T, h_q=2, h_kv=1, d=8, params=p,
+                  dtype="f32", n_planted=1)
+    selfmask = np.array([1 << i for i in range(T)], dtype=np.uint64)
+    r = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, selfmask, p, "f32")
+    keys = np.concatenate([c.k, c.k_draft], axis=1)
+    vals = np.concatenate([c.v, c.v_draft], axis=1)
+    for i in range(T):
+        mask = np.zeros((1, n_ctx + T), bool)
+        mask[0, :n_ctx] = True
+        mask[0, n_ctx + i] = True
+        for h in range(2):
+            ref = _sdpa(c.q[i, h][None], keys[0], vals[0], mask, 1 / math.sqrt(8))[0]
+            np.testing.assert_allclose(r["o"][i][h], ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("dense_len", [0, 4096])
+def test_tree_self_bit_always_honoured_and_high_bits_ignored(dense_len):
+    # a draft attends itself whether or not its own bit is set, and mask bits
+    # at or above the draft count name no draft
+    p = Params(topk=4, dense_len=dense_len)
+    T = 6
+    c = make_tree(20, n_ctx=800, n_draft=T, h_q=4, h_kv=2, d=16, params=p,
+                  dtype="f32", n_planted=2, parents=[-1, 0, 0, 1, 3, 2])
+    r = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, "f32")
+    odd = c.mask.copy()
+    for i in range(T):
+        odd[i] = np.uint64(int(odd[i]) & ~(1 << i)) | (np.uint64(1) << np.uint64(63 - i))
+    assert all(not (int(odd[i]) >> i) & 1 for i in range(T))
+    r2 = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, odd, p, "f32")
+    for i in range(T):
+        np.testing.assert_array_equal(r2["o"][i], r["o"][i])
+        np.testing.assert_array_equal(r2["lse"][i], r["lse"][i])
+    # an all-zero mask is the self-only mask
+    zero = np.zeros(T, dtype=np.uint64)
+    selfmask = np.array([1 << i for i in range(T)], dtype=np.uint64)
+    r3 = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, zero, p, "f32")
+    r4 = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, selfmask, p, "f32")
+    for i in range(T):
+        np.testing.assert_array_equal(r3["o"][i], r4["o"][i])
+    # dropping a real ancestor changes the output (the pin can see a draft)
+    assert np.abs(r4["o"][4] - r["o"][4]).max() > 1e-6
+
+
 # ----------------------------------------------------- backward (training) ----
 def _torch_selected_grads(q, k, v, sel_rows, p, d_out):
     """torch autograd (float64) of the same attention, row by row."""
