@@ -17,8 +17,11 @@ constexpr int kCompressSplit = 4;       // thread groups sharing one window's ro
 // A window is summed by kCompressSplit groups of d/E threads; group q adds
 // rows t = q, q + 4, ... of the window, each thread one 16-byte column chunk
 // (a window row is read as one coalesced 256-byte segment for bf16, d=128).
-// The partial sums meet in LDS.  For bf16 keys every partial and total sum
-// of <= 2^16 values is exact in float32, so the order does not matter.
+// The partial sums meet in LDS.  The sum is rounded in float32: once the
+// window's values spread over more than ~16 binary orders of magnitude a
+// partial sum drops low bits, so another summation order can move the
+// stored bf16 mean by one unit in the last place in rare cases.  Tests allow
+// for that (at most 1 in 10^4 elements differ from a float64 mean).
 template <typename T, int D>
 __global__ __launch_bounds__(kCompressThreads) void compress_keys_kernel(
     const T* __restrict__ k, int h_kv, int64_t cap, const int32_t* __restrict__ seqlens,

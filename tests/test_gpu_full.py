@@ -34,26 +34,41 @@ def _host(t):
 
 @pytest.mark.parametrize("wid", [2, 8])      # 8: 128-token blocks, top-6
 def test_full_prefill_128k_chunk_sampled_rows(wid):
+    """Outputs, log-sum-exp and selections of 590 rows of the final chunk
+    against the oracle: one contiguous band of 512 rows (every edge of the
+    8-token tiles inside it, and a 64-row band edge), the chunk's first and
+    last rows and tile edges at its ends, and 64 seeded random rows."""
+    from oracle_pool import prefill_rows
     _say(f"full prefill 128K, final 8192-query chunk (workload {wid})")
     wl = _workload(wid)
     c, p = wl.case, wl.p
     rng = np.random.default_rng(123)
-    rows = sorted(set([0, 1, 7, 8, 9, 63, 64, 4095, 4096, 8183, 8184, 8190, 8191] +
-                      list(rng.integers(0, c.n_q, 11))))
+    band = list(range(4064, 4576))
+    rows = sorted(set([0, 1, 7, 8, 9, 15, 16, 63, 64, 8183, 8184, 8190, 8191] + band +
+                      list(rng.integers(0, c.n_q, 64))))
+    assert len(rows) >= 256
     ck = O.compress_keys(c.k, p, "bf16")
     gck = _host(wl.ck)
     assert np.count_nonzero(gck != ck) <= max(1, ck.size // 10000)
-    res = O.prefill(c.q, c.k, c.v, p, "bf16", rows=rows, ck=ck)
+    res = prefill_rows(c.q, c.k, c.v, p, "bf16", ck, rows)
+    _say(f"oracle done for {len(rows)} rows")
     out = _host(wl.plan.out)
     lse = wl.plan.lse.cpu().numpy()
     sel = wl.plan.block_idx.cpu().numpy()
+    swaps = 0
+    worst = 0.0
     for i in rows:
         pos = c.n_k - c.n_q + i
-        P = [check_selection(sel[i, g], res["S"][i][g], res["sel"][i][g], pos, p,
-                             f"row {i} g {g}") for g in range(2)]
-        o, l = O.attend_selected(c.q[i], c.k, c.v, P, pos, p)
-        check_close(out[i], o, "bf16", f"row {i}")
-        np.testing.assert_allclose(lse[i], l, atol=2e-3)
+        o_ref, l_ref, S, osel = res[i]
+        P = [check_selection(sel[i, g], S[g], osel[g], pos, p, f"row {i} g {g}")
+             for g in range(2)]
+        if any(set(P[g].tolist()) != set(int(b) for b in osel[g]) for g in range(2)):
+            swaps += 1                      # a tie-band swap: the oracle on the GPU's set
+            o_ref, l_ref = O.attend_selected(c.q[i], c.k, c.v, P, pos, p)
+        mx, _ = check_close(out[i], o_ref, "bf16", f"row {i}")
+        worst = max(worst, mx)
+        np.testing.assert_allclose(lse[i], l_ref, atol=2e-3)
+    _say(f"{len(rows)} rows: max-abs {worst:.3g}, {swaps} tie-band swaps")
     # every row of the chunk: a valid selection (forced blocks, ascending, full)
     for g in range(2):
         s = sel[:, g]
