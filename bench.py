@@ -18,12 +18,17 @@ outputs resident), one training step's attention gradient for the chunk,
 10 = the backward of workload 7's whole 131072-token prompt (16 chunk
 backwards adding into one dK/dV).
 
-Prints one JSON line: tokens/s over K timed steps (the K steps captured as one
-HIP graph and replayed once; --eager times individual launches), per-stage
-times from HIP events recorded between the library calls of eager steps, the
-dominant call's roofline fraction (its time = HIP-event time of the K-step
-graph minus that of the same K steps without the call, median of 5 such pairs,
-events on the graph's stream), and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line.  Timing: each of the K timed iterations flushes the
+caches (a read-modify-write of 1 GiB, 4x the Infinity Cache) and then replays
+the whole step, captured once as a HIP graph, between two HIP events;
+ms_per_step is the median, with p10 / p90 / mean beside it.  The dominant
+call (the attention call) is timed the same way on its own after the step's
+earlier stages, and its mean duration gives the roofline fraction
+(algorithmic FLOP or bytes per launch over that time).  Other workloads of
+the metric (--also: ragged decode, 128K decode at batch 1, tree
+verification) are timed the same way and reported in the same line.  The
+CPU oracle is timed on a bounded sample of the headline workload, its rows
+spread over the host cores (worker processes forked before the GPU is used).
 """
 from __future__ import annotations
 
@@ -88,51 +93,56 @@ def _traffic(kernel_name, src_file, workload):
     return t.get("hbm_bytes_per_launch")
 
 
+def build_case(wid, seed=0, score_mode=None):
+    """The seeded inputs of a workload, on the host: (case, name, rep).
+
+    rep > 1 (workload 6): decode at 128K for `rep` copies of one
+    131072-token sequence, each in its own HBM (same values, separate
+    addresses, so every sequence's K/V is really read)."""
+    from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, Params, config
+    rep = 1
+    if wid == 7:
+        # the whole 128K prompt: queries at every position, 16 chunks of 8192
+        case, name = config(2, seed=seed, n_q=131072), "sparse_prefill_bf16_128k_whole_16x8192"
+    elif wid == 8:
+        # the final chunk with the other variant the pages describe:
+        # 128-token blocks, top-6
+        case = config(2, seed=seed, params=Params(block_size=128, topk=6))
+        name = "sparse_prefill_bf16_128k_chunk8192_block128_top6"
+    elif wid == 9:
+        case, name = config(2, seed=seed), "sparse_prefill_backward_bf16_128k_chunk8192"
+    elif wid == 10:
+        case = config(2, seed=seed, n_q=131072)
+        name = "sparse_prefill_backward_bf16_128k_whole_16x8192"
+    elif wid == 5:
+        case, name = config(1, seed=seed, seqlen=131072, n_planted=64), "decode_bf16_128k"
+    elif wid == 6:
+        case = config(1, seed=seed, seqlen=131072, n_planted=64)
+        name, rep = "decode_bf16_128k_batch32", 32
+    elif wid in CONFIG_NAMES and wid != 0:
+        case, name = config(wid, seed=seed), CONFIG_NAMES[wid]
+    else:
+        raise SystemExit(f"workload {wid} is a parity case, not a bench workload")
+    if score_mode is not None:
+        case.params = case.params.replace(score_mode=score_mode)
+    return case, name, rep
+
+
 # ----------------------------------------------------------------------------
 class Workload:
     """Builds inputs on the GPU and exposes step() plus algorithmic work."""
 
-    def __init__(self, wid, torch, seed=0, score_mode=None):
+    def __init__(self, wid, torch, seed=0, score_mode=None, case=None):
         from block_sparse_long_infllmv2_amd import binding as B
         from block_sparse_long_infllmv2_amd import pipeline as PL
-        from block_sparse_long_infllmv2_amd.workloads import CONFIG_NAMES, Params, config
         self.torch, self.B, self.PL = torch, B, PL
         self.wid = wid
         dev = torch.device("cuda:0")
         self.dev = dev
-        # batched decode at 128K: `rep` copies of one 131072-token sequence, each
-        # in its own HBM (same values, separate addresses, so every sequence's
-        # K/V is really read); shows the decode kernel where HBM bandwidth,
-        # not launch latency, is the limit
-        self.rep = 1
-        if wid == 7:
-            # the whole 128K prompt: queries at every position, 16 chunks of 8192
-            self.case = config(2, seed=seed, n_q=131072)
-            self.name = "sparse_prefill_bf16_128k_whole_16x8192"
-        elif wid == 8:
-            # the final chunk again with the other variant the pages describe:
-            # 128-token blocks, top-6
-            self.case = config(2, seed=seed, params=Params(block_size=128, topk=6))
-            self.name = "sparse_prefill_bf16_128k_chunk8192_block128_top6"
-        elif wid == 9:
-            self.case = config(2, seed=seed)
-            self.name = "sparse_prefill_backward_bf16_128k_chunk8192"
-        elif wid == 10:
-            self.case = config(2, seed=seed, n_q=131072)
-            self.name = "sparse_prefill_backward_bf16_128k_whole_16x8192"
-        elif wid == 5:
-            self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
-            self.name = "decode_bf16_128k"
-        elif wid == 6:
-            self.case = config(1, seed=seed, seqlen=131072, n_planted=64)
-            self.rep = 32
-            self.name = "decode_bf16_128k_batch32"
-        else:
-            self.case = config(wid, seed=seed)
-            self.name = CONFIG_NAMES[wid]
+        if case is None:
+            case = build_case(wid, seed, score_mode)
+        self.case, self.name, self.rep = case
         c = self.case
-        if score_mode is not None:
-            c.params = c.params.replace(score_mode=score_mode)
         p = c.params
         self.p = p
         bf = torch.bfloat16
@@ -229,8 +239,6 @@ class Workload:
             torch.cuda.synchronize()
             self.tokens = c.q.shape[0]
             self.kind = "tree"
-        else:
-            raise SystemExit(f"workload {wid} is a parity case, not a bench workload")
 
     # one step, with optional per-stage event recording; skip_dominant leaves
     # out the attention call (to time that call inside real steps by difference)
@@ -377,82 +385,140 @@ class Workload:
                 "union_blocks": int(union), "src": "attn_bf16.hip"}
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """The CPU oracle as it stands, single-threaded, on a bounded sample."""
-    import oracle as O
+# ---- CPU baseline: the oracle as it stands, over the host's cores ----------
+# Worker processes are forked before the GPU is touched; they inherit the
+# host inputs through this module-level dict and compute oracle rows only.
+_CPU = {}
+
+
+def _cpu_worker_init():
     from threadpoolctl import threadpool_limits
-    c, p = wl.case, wl.p
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        if wl.kind == "prefill_whole":
-            # query i sees keys [0, i]: the oracle's prefill of that prefix with
-            # one query, its compressed keys cut from the whole prompt's
-            ck = O.compress_keys(c.k, p, "bf16")
-            n = c.k.shape[1]
-            rows, i = [], 0
-            step = max(1, n // 256)
-            while time.perf_counter() - t0 < budget_s and i < n:
-                nw = O.num_windows(i + 1, p.kernel_size, p.kernel_stride)
-                O.prefill(c.q[i:i + 1], c.k[:, :i + 1], c.v[:, :i + 1], p, "bf16", rows=[0],
-                          ck=ck[:, :nw])
-                rows.append(i)
-                i += step
-            dt = time.perf_counter() - t0
-            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{len(rows)} of {n} prompt positions (every {step}th) incl. "
-                              f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
-        if wl.kind in ("prefill_bwd", "prefill_bwd_whole"):
-            # gradients of single rows, selections taken from the GPU forward
-            sel = (wl.cp.idx_buf.view(c.q.shape[0], c.k.shape[0], p.topk) if
-                   wl.kind == "prefill_bwd_whole" else wl.plan.block_idx).cpu().numpy()
-            dense_row = [False] * c.n_q
-            if wl.kind == "prefill_bwd_whole":
+    threadpool_limits(limits=1)            # one BLAS thread per worker process
+
+
+def _cpu_row(i):
+    import oracle as O
+    c, p, kind = _CPU["case"], _CPU["case"].params, _CPU["kind"]
+    if kind == "prefill":
+        O.prefill(c.q, c.k, c.v, p, "bf16", rows=[i], ck=_CPU["ck"])
+    elif kind == "prefill_whole":
+        nw = O.num_windows(i + 1, p.kernel_size, p.kernel_stride)
+        O.prefill(c.q[i:i + 1], c.k[:, :i + 1], c.v[:, :i + 1], p, "bf16", rows=[0],
+                  ck=_CPU["ck"][:, :nw])
+    elif kind == "decode":
+        O.decode(c.q[i:i + 1], [c.k[i]], [c.v[i]], [c.seqlens[i]], p, "bf16")
+    elif kind == "tree":
+        O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, "bf16",
+                      ck=_CPU["ck"], drafts=[i])
+    return i
+
+
+def _cpu_bwd_row(arg):
+    import oracle as O
+    i, sel_row = arg
+    c = _CPU["case"]
+    sel_rows = [None] * c.q.shape[0]
+    sel_rows[i] = sel_row
+    O.prefill_backward(c.q, c.k, c.v, sel_rows, c.params, _CPU["d_out"], rows=[i])
+    return i
+
+
+def _one_thread():
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
+def cpu_workers():
+    """Worker count: the host cores this process may run on, at most 16 (a
+    one-GPU share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class CpuBaseline:
+    """Times the CPU oracle on a bounded sample of a workload, rows spread
+    over a pool of forked worker processes (one BLAS thread each)."""
+
+    def __init__(self, case, kind, workers):
+        import multiprocessing
+
+        import copy
+
+        import oracle as O
+        # the oracle works in float64: upcast the inputs once here (exact),
+        # not in every row's call
+        case = copy.copy(case)
+        for name in ("q", "k", "v", "k_draft", "v_draft"):
+            x = getattr(case, name, None)
+            if isinstance(x, list):
+                setattr(case, name, [np.asarray(a, np.float64) for a in x])
+            elif isinstance(x, np.ndarray):
+                setattr(case, name, np.asarray(x, np.float64))
+        _CPU.clear()
+        _CPU.update(case=case, kind=kind)
+        self.case, self.kind, self.workers = case, kind, workers
+        # compressed keys of the whole context, once, in this process (timed
+        # and counted with the rows); the workers inherit them
+        self.ck_s = 0.0
+        if kind in ("prefill", "prefill_whole", "tree"):
+            t0 = time.perf_counter()
+            with_one_thread = _one_thread()
+            with with_one_thread:
+                _CPU["ck"] = O.compress_keys(case.k, case.params, "bf16")
+            self.ck_s = time.perf_counter() - t0
+        self.pool = multiprocessing.get_context("fork").Pool(workers, _cpu_worker_init)
+
+    def close(self):
+        self.pool.terminate()
+        self.pool.join()
+
+    def _run(self, fn, items, budget_s, t0):
+        done = 0
+        while time.perf_counter() - t0 < budget_s and done < len(items):
+            batch = items[done:done + self.workers]
+            self.pool.map(fn, batch, chunksize=1)
+            done += len(batch)
+        return done, time.perf_counter() - t0
+
+    def measure(self, budget_s, wl=None):
+        import oracle as O
+        c, p, kind, W = self.case, self.case.params, self.kind, self.workers
+        tail = f"float64 numpy oracle, {W} worker processes x 1 thread"
+        t0 = time.perf_counter() - self.ck_s
+        if kind in ("prefill", "prefill_whole"):
+            n = c.q.shape[0]
+            step = max(1, n // 4096)
+            rows = list(range(0, n, step))
+            done, dt = self._run(_cpu_row, rows, budget_s, t0)
+            what = "prompt positions" if kind == "prefill_whole" else "chunk queries"
+            return {"value": done / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
+                    "sample": f"{done} of {n} {what} (every {step}th) incl. compressing "
+                              f"all {_CPU['ck'].shape[1]} windows once; {tail}"}
+        if kind in ("prefill_bwd", "prefill_bwd_whole"):
+            sel = (wl.cp.idx_buf.view(c.q.shape[0], c.k.shape[0], p.topk)
+                   if kind == "prefill_bwd_whole" else wl.plan.block_idx).cpu().numpy()
+            dense_row = [False] * c.q.shape[0]
+            if kind == "prefill_bwd_whole":
                 for (q0, q1, _, _, _), pc in zip(wl.cp.sched, wl.cp.plans):
                     for r in range(q0, q1):
                         dense_row[r] = pc.dense
-            d_out = wl.d_out.float().cpu().numpy()
-            sel_rows = [None] * c.n_q
-            rows, i = [], 0
-            step = max(1, c.n_q // 256)
-            while time.perf_counter() - t0 < budget_s and i < c.n_q:
-                sel_rows[i] = None if dense_row[i] else [s[s >= 0] for s in sel[i]]
-                O.prefill_backward(c.q, c.k, c.v, sel_rows, p, d_out, rows=[i])
-                rows.append(i)
-                i += step
-            dt = time.perf_counter() - t0
-            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{len(rows)} of {c.n_q} queries (every {step}th): dq of "
-                              f"the row and its dk/dv contributions, float64 numpy, 1 thread"}
-        if wl.kind == "prefill":
-            ck = O.compress_keys(c.k, p, "bf16")
-            rows, i = [], 0
-            step = max(1, c.n_q // 256)
-            while time.perf_counter() - t0 < budget_s and i < c.n_q:
-                O.prefill(c.q, c.k, c.v, p, "bf16", rows=[i], ck=ck)
-                rows.append(i)
-                i += step
-            dt = time.perf_counter() - t0
-            return {"value": len(rows) / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{len(rows)} of {c.n_q} chunk queries (every {step}th) incl. "
-                              f"compressing all {ck.shape[1]} windows, float64 numpy, 1 thread"}
-        if wl.kind == "decode":
-            n = 0
-            while time.perf_counter() - t0 < budget_s and n < len(c.seqlens):
-                O.decode(c.q[n:n + 1], [c.k[n]], [c.v[n]], [c.seqlens[n]], p, "bf16")
-                n += 1
-            dt = time.perf_counter() - t0
-            return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                    "sample": f"{n} of {len(c.seqlens)} sequences, float64 numpy, 1 thread"}
-        T = c.q.shape[0]
-        n = 0
-        ck = O.compress_keys(c.k, p, "bf16")
-        while time.perf_counter() - t0 < budget_s and n < T:
-            O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, c.mask, p, "bf16", ck=ck,
-                          drafts=[n])
-            n += 1
-        dt = time.perf_counter() - t0
-        return {"value": n / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                "sample": f"{n} of {T} drafts, float64 numpy, 1 thread"}
+            n = c.q.shape[0]
+            step = max(1, n // 1024)
+            items = [(i, None if dense_row[i] else [s_[s_ >= 0] for s_ in sel[i]])
+                     for i in range(0, n, step)]
+            t0 = time.perf_counter()
+            done, dt = self._run(_cpu_bwd_row, items, budget_s, t0)
+            return {"value": done / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
+                    "sample": f"{done} of {n} queries (every {step}th): dq of the row and "
+                              f"its dk/dv contributions; {tail}"}
+        if kind == "tree":
+            T = c.q.shape[0]
+            done, dt = self._run(_cpu_row, list(range(T)), budget_s, t0)
+            return {"value": done / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
+                    "sample": f"{done} of {T} drafts incl. compressing the context; {tail}"}
+        n = len(c.seqlens)
+        done, dt = self._run(_cpu_row, list(range(n)), budget_s, t0)
+        return {"value": done / dt, "unit": "tokens/s", "cores": W, "kind": "oracle",
+                "sample": f"{done} of {n} sequences, each from its compressed keys; {tail}"}
 
 
 def _keep_busy(fn, seconds, torch):
@@ -466,135 +532,134 @@ def _keep_busy(fn, seconds, torch):
             break
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
-    ap.add_argument("--eager", action="store_true",
-                    help="time steps as individual launches instead of HIP graph replays")
-    ap.add_argument("--score-mode", type=int, default=None, choices=[0, 1],
-                    help="group score reading: 0 summed query (default), 1 sum of "
-                         "per-head softmaxes over the visible windows")
-    ap.add_argument("--warm-seconds", type=float, default=0.3,
-                    help="untimed work after the warm-up steps and after graph capture, "
-                         "so that timing starts at steady clocks")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device copy (3 times): the reference "
-                         "for scaling FETCH_SIZE / WRITE_SIZE counters")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the path is "
-              "built and measured on one GPU; a multi-GPU run is not implemented.",
-              file=sys.stderr)
-        sys.exit(2)
+def _capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
 
-    import torch
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.calibrate_copy:
-        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibration": "device copy", "bytes_read": a.numel() * 4,
-                          "bytes_written": b.numel() * 4, "launches": 3}))
-        return
-    wl = Workload(args.workload, torch, score_mode=args.score_mode)
-    print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
-    # The clocks ramp up under sustained load and fall back while the GPU idles
-    # (a kernel's duration drifts down by ~20% over the first ~100 ms of work):
-    # keep stepping, untimed, for at least --warm-seconds before any timing.
-    _keep_busy(wl.step, args.warm_seconds, torch)
+def _stats(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
-    # per-stage times: eager steps with HIP events between the library calls
-    evs = []
+
+class Flush:
+    """Evicts the caches between timed iterations: a read-modify-write of a
+    1 GiB buffer (4x the 256 MB Infinity Cache, far beyond the L2s), on the
+    current stream, outside the timed brackets."""
+    BYTES = 1 << 30
+
+    def __init__(self, torch):
+        self.buf = torch.zeros(self.BYTES // 4, dtype=torch.float32, device="cuda:0")
+
+    def __call__(self):
+        self.buf.add_(1.0)
+
+
+def _timed_loop(torch, iters, flush, before, timed):
+    """iters x (flush; before(); event; timed(); event): per-iteration
+    milliseconds of timed() on the current stream, caches cold each time.
+    Returns (list of ms, wall seconds of the whole loop incl. flushes)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for e0, e1 in evs:
+        flush()
+        if before is not None:
+            before()
+        e0.record()
+        timed()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [e0.elapsed_time(e1) for e0, e1 in evs], wall
+
+
+def time_workload(wl, torch, steps, warmup, warm_seconds, flush):
+    """Cold-cache timing of one workload.
+
+    * step: the whole step (every stage) captured as one HIP graph; each of
+      `steps` iterations flushes the caches, then replays the graph between
+      two HIP events.  ms_per_step = median; p10 / p90 / mean reported.
+    * dominant call: the step's stages before it replayed untimed after the
+      flush (so its inputs are as cold as in a real step: the selections
+      were just written, K/V were not touched), then the call's own graph
+      between two events.  For the whole-prompt workload, whose attention
+      calls interleave with the other stages, it is the median step minus
+      the median step without those calls.
+    * warm: the step graph replayed `steps` times back to back, no flush.
+    * stages: eager steps with events between the library calls, flushed."""
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    _keep_busy(wl.step, warm_seconds, torch)
+
+    # per-stage times of eager steps (flush before each step)
+    stage_ev = []
+    for _ in range(steps):
+        flush()
         ev = []
         wl.step(ev)
-        evs.append(ev)
+        stage_ev.append(ev)
     torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t0
     stages = {}
-    for ev in evs:
-        per_step = {}
+    for ev in stage_ev:
+        per = {}
         for (n0, e0), (n1, e1) in zip(ev[:-1], ev[1:]):
-            per_step[n1] = per_step.get(n1, 0.0) + e0.elapsed_time(e1)
-        for k, v in per_step.items():
+            per[n1] = per.get(n1, 0.0) + e0.elapsed_time(e1)
+        for k, v in per.items():
             stages.setdefault(k, []).append(v)
-    stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    stage_ms = {k: float(np.median(v)) for k, v in stages.items()}
 
-    w = wl.work()
-    dom = w["dominant"]
-    if args.eager:
-        wall = wall_eager
-        dom_ms = stage_ms[dom]
-        mode = "eager"
+    g_step = _capture(torch, wl.step)
+    separable = wl.kind != "prefill_whole"
+    has_pre = wl.kind not in ("prefill_bwd", "prefill_bwd_whole")
+    g_pre = _capture(torch, lambda: wl.step(skip_dominant=True)) if has_pre else None
+    g_dom = _capture(torch, wl.dominant_call) if separable else None
+    torch.cuda.synchronize()
+    # capturing left the GPU idle: untimed flushed replays until it is warm again
+    _keep_busy(lambda: (flush(), g_step.replay()), warm_seconds, torch)
+
+    step_ms, wall = _timed_loop(torch, steps, flush, None, g_step.replay)
+    if separable:
+        dom_ms, _ = _timed_loop(torch, steps, flush,
+                                g_pre.replay if g_pre is not None else None, g_dom.replay)
+        dom = _stats(dom_ms)
     else:
-        # The K timed steps as one HIP graph (the library only launches kernels
-        # on the caller's stream and allocates nothing, so steps capture whole):
-        # the GPU runs them back to back with no host launch gaps, which
-        # otherwise dominate the small decode steps.  One untimed replay first.
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for _ in range(args.steps):
-                wl.step()
-        # the same K steps without the dominant call: the difference is that
-        # call's cost inside real steps (same neighbours, same cache state)
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for _ in range(args.steps):
-                wl.step(skip_dominant=True)
-        # capturing left the GPU idle: untimed replays until it is warm again
-        _keep_busy(g.replay, args.warm_seconds, torch)
-        gr.replay()
-        torch.cuda.synchronize()
-        # the timed K steps: one replay, wall clock and events
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        t0 = time.perf_counter()
-        ev[0].record()
-        g.replay()
-        ev[1].record()
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        # dominant call: median over 5 (full, without-the-call) replay pairs
-        diffs = []
-        for i in range(5):
-            if i:
-                ev[0].record()
-                g.replay()
-                ev[1].record()
-            ev[2].record()
-            gr.replay()
-            ev[3].record()
-            torch.cuda.synchronize()
-            diffs.append(ev[0].elapsed_time(ev[1]) - ev[2].elapsed_time(ev[3]))
-        dom_ms = float(np.median(diffs)) / args.steps
-        mode = "hip_graph"
-    print(f"[bench] {args.steps} steps in {wall:.4f} s ({mode}); eager {wall_eager:.4f} s",
-          file=sys.stderr, flush=True)
-    ms_per_step = wall * 1e3 / args.steps
-    value = wl.tokens / (ms_per_step / 1e3)
+        pre_ms, _ = _timed_loop(torch, steps, flush, None, g_pre.replay)
+        d = float(np.median(step_ms) - np.median(pre_ms))
+        dom = {"median": d, "p10": None, "p90": None, "mean": d, "n": steps,
+               "method": "median step - median step without the attention calls"}
+    # warm: back-to-back replays of the step graph, no flush
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        g_step.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_ms = e0.elapsed_time(e1) / steps
+    return {"step": _stats(step_ms), "dominant": dom, "warm_ms_per_step": warm_ms,
+            "stages_ms": stage_ms, "timed_loop_wall_s": wall}
+
+
+def _roofline(wl, w, dom):
+    """Roofline object for the dominant call: algorithmic work per launch
+    over its mean cold-cache duration."""
     src = os.path.join(ROOT, "block_sparse_long_infllmv2_amd", "csrc", w["src"])
+    t_ms = dom["mean"]
     if w["bound"] == "mfma":
-        achieved = w["flop"] / (dom_ms * 1e-3) / 1e12
+        achieved = w["flop"] / (t_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                # the counter figure is per launch of the final-chunk workload
-                "traffic": _traffic(dom, src, wl.name) if w.get("launches", 1) == 1 else None,
-                "kernel": dom,
+                "traffic": _traffic(w["dominant"], src, wl.name)
+                if w.get("launches", 1) == 1 else None,
+                "kernel": w["dominant"],
                 ("algorithmic_gflop_per_step" if w.get("launches", 1) > 1
-                 else "algorithmic_gflop_per_launch"): round(w["flop"] / 1e9, 2),
-                "kernel_ms": round(dom_ms, 4)}
+                 else "algorithmic_gflop_per_launch"): round(w["flop"] / 1e9, 2)}
         if w.get("launches", 1) > 1:
             roof["launches_per_step"] = w["launches"]
         if "launches_in_call" in w:
@@ -604,13 +669,23 @@ def main():
             if "algorithmic_gflop_per_launch" in roof:
                 roof["algorithmic_gflop_per_call"] = roof.pop("algorithmic_gflop_per_launch")
     else:
-        achieved = w["bytes"] / (dom_ms * 1e-3) / 1e9
+        achieved = w["bytes"] / (t_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                "traffic": _traffic(dom, src, wl.name), "kernel": dom,
-                "algorithmic_mb_per_launch": round(w["bytes"] / 1e6, 3),
-                "kernel_ms": round(dom_ms, 4)}
+                "traffic": _traffic(w["dominant"], src, wl.name), "kernel": w["dominant"],
+                "algorithmic_mb_per_launch": round(w["bytes"] / 1e6, 3)}
+        if "union_blocks" in w:
+            roof["union_blocks"] = w["union_blocks"]
+    roof["kernel_ms"] = round(t_ms, 4)
+    roof["kernel_ms_median"] = round(dom["median"], 4)
+    if dom.get("p10") is not None:
+        roof["kernel_ms_p10"] = round(dom["p10"], 4)
+        roof["kernel_ms_p90"] = round(dom["p90"], 4)
+    roof["timing"] = "HIP events on the launch stream, caches flushed before each launch"
+    return roof
 
+
+def _config(wl):
     cfg = {"workload": wl.name}
     c = wl.case
     if wl.kind == "prefill_whole":
@@ -633,19 +708,123 @@ def main():
                 "kernel_stride": wl.p.kernel_stride, "topk": wl.p.topk,
                 "init_blocks": wl.p.init_blocks, "local_blocks": wl.p.local_blocks,
                 "dense_len": wl.p.dense_len})
+    return cfg
 
-    out = {"metric": METRIC, "value": round(value, 2), "unit": "tokens/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-           "data": "synthetic", "config": cfg, "roofline": roof, "launch": mode,
-           "score_mode": wl.p.score_mode,
-           "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-           "eager_ms_per_step": round(wall_eager * 1e3 / args.steps, 4)}
+
+def _record(wl, t):
+    """Throughput and roofline of one timed workload."""
+    w = wl.work()
+    st = t["step"]
+    ms = st["median"]
+    rec = {"value": round(wl.tokens / (ms * 1e-3), 2), "unit": "tokens/s",
+           "ms_per_step": round(ms, 4), "ms_per_step_p10": round(st["p10"], 4),
+           "ms_per_step_p90": round(st["p90"], 4), "ms_per_step_mean": round(st["mean"], 4),
+           "warm_ms_per_step": round(t["warm_ms_per_step"], 4),
+           "config": _config(wl), "roofline": _roofline(wl, w, t["dominant"]),
+           "stages_ms": {k: round(v, 4) for k, v in t["stages_ms"].items()}}
     if w["bound"] == "mfma":
-        out["scoring_gflop"] = round(w["score_flop"] / 1e9, 2)
+        rec["scoring_gflop"] = round(w["score_flop"] / 1e9, 2)
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed iterations (each: cache flush, then one step)")
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--also", default="4,5,3",
+                    help="comma-separated workloads timed in the same run and reported "
+                         "in the same line (4 = ragged decode, 5 = 128K decode at batch 1, "
+                         "3 = tree verification); empty for none")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--score-mode", type=int, default=None, choices=[0, 1],
+                    help="group score reading: 0 summed query (default), 1 sum of "
+                         "per-head softmaxes over the visible windows")
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="untimed work after the warm-up steps and after graph capture, "
+                         "so that timing starts at steady clocks")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (3 times): the reference "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for {args.gpus}): the path is "
+              "built and measured on one GPU; a multi-GPU run is not implemented.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        assert torch.cuda.is_available(), "bench.py needs a GPU"
+        a = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": a.numel() * 4,
+                          "bytes_written": b.numel() * 4, "launches": 3}))
+        return
+
+    # host inputs first; the CPU oracle's worker processes are forked now,
+    # before this process touches the GPU
+    case = build_case(args.workload, score_mode=args.score_mode)
+    kind_of = {7: "prefill_whole", 9: "prefill_bwd", 10: "prefill_bwd_whole", 3: "tree",
+               1: "decode", 4: "decode", 5: "decode", 6: "decode"}
+    kind = kind_of.get(args.workload, "prefill")
+    cpu = None
     if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+        cpu = CpuBaseline(case[0], kind, cpu_workers())
+    print(f"[bench] workload {case[1]}: host inputs ready", file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    flush = Flush(torch)
+    wl = Workload(args.workload, torch, case=case)
+    print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
+    t = time_workload(wl, torch, args.steps, args.warmup, args.warm_seconds, flush)
+    rec = _record(wl, t)
+    print(f"[bench] {wl.name}: median step {rec['ms_per_step']} ms "
+          f"(p10 {rec['ms_per_step_p10']}, p90 {rec['ms_per_step_p90']}), "
+          f"roofline {rec['roofline']['frac']}", file=sys.stderr, flush=True)
+
+    out = {"metric": METRIC, "value": rec["value"], "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+           "ms_per_step_p10": rec["ms_per_step_p10"], "ms_per_step_p90": rec["ms_per_step_p90"],
+           "ms_per_step_mean": rec["ms_per_step_mean"],
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic", "config": rec["config"], "roofline": rec["roofline"],
+           "timing": "per step: 1 GiB cache flush, then the step's HIP graph between HIP "
+                     "events; median over the timed steps",
+           "timed_loop_wall_s": round(t["timed_loop_wall_s"], 4),
+           "warm_ms_per_step": rec["warm_ms_per_step"], "launch": "hip_graph",
+           "score_mode": wl.p.score_mode, "stages_ms": rec["stages_ms"]}
+    if "scoring_gflop" in rec:
+        out["scoring_gflop"] = rec["scoring_gflop"]
+
+    # the other workloads of the metric, timed the same way in this run
+    names = {4: "decode", 5: "decode_batch1_128k", 3: "tree", 1: "decode_batch1_32k",
+             6: "decode_batch32_128k", 8: "prefill_block128_top6", 2: "prefill"}
+    also = [int(x) for x in args.also.split(",") if x.strip()]
+    keep = wl
+    for wid in also:
+        if wid == args.workload:
+            continue
+        w2 = Workload(wid, torch)
+        t2 = time_workload(w2, torch, args.steps, args.warmup, args.warm_seconds, flush)
+        r2 = _record(w2, t2)
+        out[names.get(wid, f"workload_{wid}")] = r2
+        print(f"[bench] {w2.name}: median step {r2['ms_per_step']} ms, roofline "
+              f"{r2['roofline']['frac']}", file=sys.stderr, flush=True)
+        del w2
+        torch.cuda.empty_cache()
+
+    if cpu is not None:
+        print(f"[bench] timing the CPU oracle on a sample ({cpu.workers} workers)",
+              file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu.measure(args.cpu_budget, keep)
+        cpu.close()
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
