@@ -19,6 +19,7 @@ LIB_PATH = os.environ.get("INFLLMV2_LIB") or os.path.join(_HERE, "libinfllmv2.so
 
 F32, BF16 = 0, 1
 OP_DECODE, OP_TREE, OP_PREFILL_BWD = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 8 << 20          # INFLLMV2_NOALLOC_SCRATCH_BYTES
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported configuration",
           3: "workspace missing, misaligned or too small", 4: "HIP launch failed"}
 
@@ -58,6 +59,9 @@ def _load():
                                                         i32, i32, i32, P, P, P, PP, P]),
         "infllmv2_sparse_attn_decode": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, P, i32,
                                                        i32, i32, i32, P, P, P, P, sz, PP, P]),
+        "infllmv2_sparse_attn_decode_noalloc": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64,
+                                                               P, i32, i32, i32, i32, P, P, P,
+                                                               PP, P]),
         "infllmv2_tree_verify": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P,
                                                 i32, i32, i32, P, P, P, P, sz, PP, P]),
         "infllmv2_sparse_attn_prefill_backward": (ctypes.c_int, [ctypes.c_int, P, i32, P, P,
@@ -232,6 +236,28 @@ def infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, max_seqlen, block_
                                            _ptr(ws), ws.numel() * ws.element_size(),
                                            ctypes.byref(p), _stream()),
            "infllmv2_sparse_attn_decode")
+
+
+def infllmv2_sparse_attn_decode_noalloc(q, k_cache, v_cache, seqlens, max_seqlen, block_idx,
+                                        out, lse, params):
+    """infllmv2_sparse_attn_decode with the library's fixed scratch array in
+    place of a workspace (NOALLOC_SCRATCH_BYTES per GPU): nothing is
+    allocated; calls on one GPU must not overlap."""
+    batch, h_q, d = q.shape
+    _, h_kv, cap, _ = k_cache.shape
+    p = to_params(params)
+    _need(k_cache, "k_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(seqlens, "seqlens", (batch,), torch.int32)
+    _need(out, "out", (batch, h_q, d), q.dtype)
+    _need(lse, "lse", (batch, h_q), torch.float32, optional=True)
+    _need(block_idx, "block_idx", (batch, h_kv, p.topk), torch.int32, optional=True)
+    _check(LIB.infllmv2_sparse_attn_decode_noalloc(_dt(q), _ptr(q), batch, _ptr(k_cache),
+                                                   _ptr(v_cache), cap, _i32(seqlens, "seqlens"),
+                                                   int(max_seqlen), h_q, h_kv, d,
+                                                   _i32(block_idx, "block_idx"), _ptr(out),
+                                                   _ptr(lse), ctypes.byref(p), _stream()),
+           "infllmv2_sparse_attn_decode_noalloc")
 
 
 def infllmv2_tree_verify(q, k_cache, v_cache, n_ctx, k_draft, v_draft, tree_mask, block_idx,

@@ -31,6 +31,8 @@
 //            drafts' kept blocks plus one chunk holding the draft tokens
 //            (masked by the uint64 ancestor mask); partials as in decode.
 //   combine: merges the split partials with their log-sum-exp weights.
+#include <mutex>
+
 #include "lds_tiles.h"
 
 namespace infllmv2 {
@@ -1988,6 +1990,59 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
     hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(batch * h_q), dim3(64), 0, st,
                        a.ws, a.n_split, (uint16_t*)out, lse);
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+// ---------------------------------------------------------------------------
+// Decode without a caller workspace, for callers that cannot allocate: the
+// split partials live in a fixed device array of this library, one copy per
+// GPU, held until the process ends.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[INFLLMV2_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];       // device address of `scratch`, per device
+
+// The array's device address on the current device, looked up once per
+// device.  In host code `scratch` names a host-side stand-in, so only this
+// address may be handed to kernels.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return INFLLMV2_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr)
+      return INFLLMV2_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFLLMV2_OK;
+}
+}  // namespace
+
+extern "C" int infllmv2_sparse_attn_decode_noalloc(int dtype, const void* q, int32_t batch,
+                                                   const void* k, const void* v, int64_t cap,
+                                                   const int32_t* seqlens, int32_t max_seqlen,
+                                                   int32_t h_q, int32_t h_kv, int32_t d,
+                                                   const int32_t* block_idx, void* out,
+                                                   float* lse, const infllmv2_params* p,
+                                                   void* stream) {
+  // the size check needs valid sizes: the decode call's own checks run first
+  // on everything but the workspace
+  INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
+  Resolved r;
+  INFLLMV2_TRY(check_params(p, d, &r));
+  if (batch < 0 || max_seqlen <= 0) return INFLLMV2_ERR_INVALID_ARG;
+  const size_t need = decode_workspace_bytes(batch, h_q, h_kv, d, max_seqlen, r);
+  if (need > (size_t)INFLLMV2_NOALLOC_SCRATCH_BYTES) return INFLLMV2_ERR_WORKSPACE;
+  void* ws = nullptr;
+  INFLLMV2_TRY(scratch_address(&ws));
+  return infllmv2_sparse_attn_decode(dtype, q, batch, k, v, cap, seqlens, max_seqlen, h_q,
+                                     h_kv, d, block_idx, out, lse, ws,
+                                     (size_t)INFLLMV2_NOALLOC_SCRATCH_BYTES, p, stream);
 }
 
 namespace infllmv2 {

@@ -35,7 +35,8 @@
  *     and queues nothing.  A failed launch returns INFLLMV2_ERR_HIP.  Faults
  *     inside queued work surface at the caller's next synchronisation.
  *   - Nothing aborts, throws or prints.  The library is stateless and
- *     reentrant.
+ *     reentrant, except infllmv2_sparse_attn_decode_noalloc, whose calls on
+ *     one GPU share that GPU's fixed scratch array.
  *   - dtype selects the element type of q, k, v, compressed keys and outputs:
  *     INFLLMV2_F32 (float) or INFLLMV2_BF16 (bfloat16, stored as uint16).
  *     Accumulation is float32 in both cases.
@@ -240,6 +241,33 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
                          int32_t d, const int32_t* block_idx, void* out, float* lse,
                          void* ws, size_t ws_bytes, const infllmv2_params* p,
                          void* stream);
+
+/*
+ * infllmv2_sparse_attn_decode without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, results and errors are
+ * those of infllmv2_sparse_attn_decode, which it calls with the library's own
+ * fixed scratch array in place of `ws`: INFLLMV2_NOALLOC_SCRATCH_BYTES per
+ * GPU, a static device array that each GPU the library runs on holds until
+ * the process ends.  It allocates nothing (no hipMalloc, no hipFree); its
+ * first call on a device looks up that device's copy of the array (the
+ * current device, which the stream must belong to).
+ *   - A call whose workspace would exceed the array
+ *     (infllmv2_workspace_size(INFLLMV2_OP_DECODE, ...) >
+ *     INFLLMV2_NOALLOC_SCRATCH_BYTES) returns INFLLMV2_ERR_WORKSPACE and
+ *     queues nothing.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (other streams, other threads) race and may return wrong
+ *     results.  Serialise them, or use infllmv2_sparse_attn_decode with
+ *     workspaces of your own.
+ */
+#define INFLLMV2_NOALLOC_SCRATCH_BYTES (8u << 20)
+int infllmv2_sparse_attn_decode_noalloc(int dtype, const void* q, int32_t batch,
+                                        const void* k, const void* v, int64_t cap,
+                                        const int32_t* seqlens, int32_t max_seqlen,
+                                        int32_t h_q, int32_t h_kv, int32_t d,
+                                        const int32_t* block_idx, void* out, float* lse,
+                                        const infllmv2_params* p, void* stream);
 
 /*
  * Gradients of infllmv2_sparse_attn_prefill with each query's kept blocks

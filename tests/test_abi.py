@@ -42,6 +42,8 @@ def lib():
                                                  i32, i32, P, P, P, PP, P]
     lib.infllmv2_sparse_attn_decode.argtypes = [ctypes.c_int, P, i32, P, P, i64, P, i32, i32,
                                                 i32, i32, P, P, P, P, sz, PP, P]
+    lib.infllmv2_sparse_attn_decode_noalloc.argtypes = [ctypes.c_int, P, i32, P, P, i64, P,
+                                                        i32, i32, i32, i32, P, P, P, PP, P]
     lib.infllmv2_tree_verify.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P, i32,
                                          i32, i32, P, P, P, P, sz, PP, P]
     lib.infllmv2_sparse_attn_prefill_backward.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64,
@@ -189,3 +191,19 @@ def test_backward_validation(lib):
     assert call(ws_ptr=None) == WORKSPACE
     assert call(ws_ptr=ctypes.c_void_p(0x10010)) == WORKSPACE        # not 256-byte aligned
     assert call(n_q=0) == OK                                         # nothing to do
+
+
+def test_decode_noalloc_host_checks(lib):
+    """The no-allocation decode rejects on the host what the decode call
+    rejects, and any request whose workspace exceeds the fixed scratch
+    array (8 MiB), before touching the GPU."""
+    big = 1 << 14
+    assert lib.infllmv2_workspace_size(0, big, 32, 2, 128, 4096, params(lib)) > 8 << 20
+    args = lambda batch, hq=32, hkv=2, d=128, ml=4096: (
+        1, FAKE, batch, FAKE, FAKE, 4096, FAKE, ml, hq, hkv, d, None, FAKE, None)
+    assert lib.infllmv2_sparse_attn_decode_noalloc(*args(big), params(lib), None) == WORKSPACE
+    assert lib.infllmv2_sparse_attn_decode_noalloc(*args(4, hq=30, hkv=4), params(lib),
+                                                   None) == INVALID
+    assert lib.infllmv2_sparse_attn_decode_noalloc(*args(4, d=96), params(lib),
+                                                   None) == UNSUPPORTED
+    assert lib.infllmv2_sparse_attn_decode_noalloc(*args(4, ml=0), params(lib), None) == INVALID
