@@ -546,16 +546,31 @@ def _stats(xs):
 
 
 class Flush:
-    """Evicts the caches between timed iterations: a read-modify-write of a
-    1 GiB buffer (4x the 256 MB Infinity Cache, far beyond the L2s), on the
-    current stream, outside the timed brackets."""
+    """Evicts the caches between timed iterations, on the current stream,
+    outside the timed brackets, with a 1 GiB buffer (4x the 256 MB Infinity
+    Cache, far beyond the L2s).
+      write_read (default): write the buffer, then read it back (a sum), so
+        the caches hold clean lines of unrelated data, as after the weight
+        reads of a model's other layers;
+      rmw: one read-modify-write pass, which leaves the caches full of dirty
+        lines that the timed step must write back as it evicts them;
+      none: no flush (warm caches)."""
     BYTES = 1 << 30
 
-    def __init__(self, torch):
+    def __init__(self, torch, mode="write_read"):
+        self.mode = mode
         self.buf = torch.zeros(self.BYTES // 4, dtype=torch.float32, device="cuda:0")
+        self.acc = torch.zeros((), dtype=torch.float32, device="cuda:0")
+        self.torch = torch
 
     def __call__(self):
-        self.buf.add_(1.0)
+        if self.mode == "none":
+            return
+        if self.mode == "rmw":
+            self.buf.add_(1.0)
+            return
+        self.buf.fill_(1.0)
+        self.torch.sum(self.buf, dim=0, out=self.acc)
 
 
 def _timed_loop(torch, iters, flush, before, timed):
@@ -746,6 +761,8 @@ def main():
     ap.add_argument("--warm-seconds", type=float, default=0.3,
                     help="untimed work after the warm-up steps and after graph capture, "
                          "so that timing starts at steady clocks")
+    ap.add_argument("--flush", default="write_read", choices=["write_read", "rmw", "none"],
+                    help="cache flush before each timed iteration (see Flush)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (3 times): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters")
@@ -780,7 +797,7 @@ def main():
     print(f"[bench] workload {case[1]}: host inputs ready", file=sys.stderr, flush=True)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    flush = Flush(torch)
+    flush = Flush(torch, args.flush)
     wl = Workload(args.workload, torch, case=case)
     print(f"[bench] workload {wl.name}: setup done", file=sys.stderr, flush=True)
     t = time_workload(wl, torch, args.steps, args.warmup, args.warm_seconds, flush)
@@ -795,8 +812,8 @@ def main():
            "ms_per_step_mean": rec["ms_per_step_mean"],
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic", "config": rec["config"], "roofline": rec["roofline"],
-           "timing": "per step: 1 GiB cache flush, then the step's HIP graph between HIP "
-                     "events; median over the timed steps",
+           "timing": f"per step: 1 GiB cache flush ({args.flush}), then the step's HIP graph "
+                     "between HIP events; median over the timed steps",
            "timed_loop_wall_s": round(t["timed_loop_wall_s"], 4),
            "warm_ms_per_step": rec["warm_ms_per_step"], "launch": "hip_graph",
            "score_mode": wl.p.score_mode, "stages_ms": rec["stages_ms"]}

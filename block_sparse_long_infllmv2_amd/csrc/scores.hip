@@ -13,39 +13,10 @@
 // group-summed query sits in LDS, d/E threads dot one compressed-key row,
 // the window scores of the chunk go to LDS and one thread per block pools
 // them.  It is HBM-bound for decode-sized row counts.
-#include "device_common.h"
 #include "host_common.h"
+#include "score_common.h"
 
 namespace infllmv2 {
-
-constexpr int kScoreThreads = 256;
-constexpr int kScoreMaxWindows = 1024;   // window scores held in LDS per chunk
-constexpr int kMfmaMinRows = 64;         // fewer rows: the streaming kernel
-constexpr int kScoreMinWgs = 512;        // streaming kernel: workgroups aimed for
-constexpr int kScoreMinBlocks = 4;       // ... but at least this many blocks each
-
-struct ScoreArgs {
-  const void* q;
-  const int32_t* row_seq;
-  const int32_t* row_pos;
-  const void* ck;
-  const int32_t* seqlens;
-  float* scores;
-  int64_t nc_cap, nb_cap;
-  int h_q, h_kv, B, ks, s, dense_len, blocks_per_wg, chunks_per_row, batch, max_pos, rows;
-  bool vec_store;             // rows of `scores` are 16-byte aligned
-  float scale;
-};
-
-// First window whose span [m*s, m*s+ks) reaches block b (i.e. m*s+ks-1 >= b*B).
-__device__ __forceinline__ int64_t first_window_of_block(int64_t b, int B, int ks, int s) {
-  const int64_t t = b * B - ks + 1;
-  return t <= 0 ? 0 : (t + s - 1) / s;
-}
-// Last window starting inside block b (m*s <= (b+1)*B - 1).
-__device__ __forceinline__ int64_t last_window_of_block(int64_t b, int B, int s) {
-  return ((b + 1) * B - 1) / s;
-}
 
 template <typename T, int D>
 __global__ __launch_bounds__(kScoreThreads) void block_scores_stream_kernel(ScoreArgs a) {
@@ -642,19 +613,9 @@ extern "C" int infllmv2_block_scores(int dtype, const void* q, int32_t rows,
   a.B = r.B; a.ks = r.ks; a.s = r.s; a.dense_len = r.dense_len; a.scale = r.scale;
   a.batch = batch; a.max_pos = max_pos; a.rows = rows;
   a.vec_store = (nb_cap % 4 == 0) && aligned16(scores);
-  // blocks per workgroup: as many as keep the chunk's windows within the LDS
-  // buffer (a chunk of n blocks spans at most (n*B + ks - 2)/s + 2 windows)
-  // and, for few rows, as few as still give about kScoreMinWgs workgroups
-  // (a decode row alone would otherwise leave most CUs without loads to issue)
-  int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * r.s - r.ks + 2) / r.B);
-  if (bpw > 32) bpw = 32;
-  if (bpw < 1) return INFLLMV2_ERR_UNSUPPORTED;
   const int64_t nb_launch = (int64_t)max_pos / r.B + 1;
-  {
-    const int64_t spread = ceil_div(nb_launch * rows * h_kv, (int64_t)kScoreMinWgs);
-    const int64_t want = spread < kScoreMinBlocks ? kScoreMinBlocks : spread;
-    if (want < bpw) bpw = (int)want;
-  }
+  const int bpw = stream_blocks_per_wg(r.B, r.ks, r.s, nb_launch, rows, h_kv);
+  if (bpw < 1) return INFLLMV2_ERR_UNSUPPORTED;
   a.blocks_per_wg = bpw;
   a.chunks_per_row = (int)ceil_div(nb_launch, bpw);
   if ((int64_t)a.chunks_per_row * rows >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
