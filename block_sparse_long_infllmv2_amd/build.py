@@ -55,8 +55,27 @@ def _compile(src: str, hipcc: str) -> str:
     return obj
 
 
+PROBES = os.path.join(HERE, "probes")
+
+
+def build_probes(hipcc: str) -> list:
+    """Stand-alone measurement programs (probes/*.hip -> probes/<name>): not
+    part of the library, built so that their results can be reproduced."""
+    out = []
+    for src in sorted(glob.glob(os.path.join(PROBES, "*.hip"))):
+        exe = src[:-len(".hip")]
+        cmd = [hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-o", exe, src]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+        out.append(exe)
+    return out
+
+
 def build(jobs: int = 8, verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link libinfllmv2.so; returns its path."""
+    """Compile every csrc/*.hip and link libinfllmv2.so (and the probes);
+    returns the library's path."""
     hipcc = _hipcc()
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sources()
@@ -68,8 +87,9 @@ def build(jobs: int = 8, verbose: bool = True) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    probes = build_probes(hipcc)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
+        print(f"built {LIB} from {len(srcs)} sources, {len(probes)} probe(s)")
     return LIB
 
 
