@@ -601,8 +601,8 @@ def time_workload(wl, torch, steps, warmup, warm_seconds, flush):
       two HIP events.  ms_per_step = median; p10 / p90 / mean reported.
     * dominant call: the step's stages before it replayed untimed after the
       flush (so its inputs are as cold as in a real step: the selections
-      were just written, K/V were not touched), then the call's own graph
-      between two events.  For the whole-prompt workload, whose attention
+      were just written, K/V were not touched), then the call itself,
+      launched eagerly between two events.  For the whole-prompt workload, whose attention
       calls interleave with the other stages, it is the median step minus
       the median step without those calls.
     * warm: the step graph replayed `steps` times back to back, no flush.
@@ -633,15 +633,16 @@ def time_workload(wl, torch, steps, warmup, warm_seconds, flush):
     separable = wl.kind != "prefill_whole"
     has_pre = wl.kind not in ("prefill_bwd", "prefill_bwd_whole")
     g_pre = _capture(torch, lambda: wl.step(skip_dominant=True)) if has_pre else None
-    g_dom = _capture(torch, wl.dominant_call) if separable else None
     torch.cuda.synchronize()
     # capturing left the GPU idle: untimed flushed replays until it is warm again
     _keep_busy(lambda: (flush(), g_step.replay()), warm_seconds, torch)
 
     step_ms, wall = _timed_loop(torch, steps, flush, None, g_step.replay)
     if separable:
+        # the call itself is launched eagerly (queued behind the flush, so no
+        # host gap): events then bracket its kernels without a graph launch
         dom_ms, _ = _timed_loop(torch, steps, flush,
-                                g_pre.replay if g_pre is not None else None, g_dom.replay)
+                                g_pre.replay if g_pre is not None else None, wl.dominant_call)
         dom = _stats(dom_ms)
     else:
         pre_ms, _ = _timed_loop(torch, steps, flush, None, g_pre.replay)
