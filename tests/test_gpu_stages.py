@@ -480,6 +480,59 @@ def test_tree_verify(B, PL, dtype, n_ctx, T, dense_len, bs, heads):
         np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if dtype == "bf16" else 1e-4)
 
 
+@pytest.mark.parametrize("dtype,n_ctx,dense_len,heads", [
+    ("bf16", 9000, 0, (32, 2, 128)),      # 16-head groups: drafts as decode rows
+    ("bf16", 5000, 8192, (32, 2, 128)),   # dense context
+    ("bf16", 9000, 0, (8, 2, 64)),        # G = 4: union planner + 32-row tiles
+    ("f32", 3000, 0, (4, 2, 64)),         # float32 path
+])
+def test_tree_verify_mask_self_bit_and_high_bits(B, PL, dtype, n_ctx, dense_len, heads):
+    """A draft always attends itself and mask bits at or above the draft count
+    name no draft: masks with every self bit cleared and high bits set give
+    the oracle's result (which follows the same reading) and exactly the
+    result of the plain ancestor masks."""
+    h_q, h_kv, d = heads
+    T = 12
+    _say(f"tree odd masks {dtype} n_ctx={n_ctx} dense_len={dense_len} h_q={h_q} h_kv={h_kv}")
+    p = Params(dense_len=dense_len, topk=16)
+    c = make_tree(9, n_ctx=n_ctx, n_draft=T, h_q=h_q, h_kv=h_kv, d=d, params=p, dtype=dtype,
+                  n_planted=max(1, n_ctx // 2048))
+    odd = c.mask.copy()
+    for i in range(T):
+        odd[i] = np.uint64((int(odd[i]) & ~(1 << i)) | (0xF << (60 - i % 8)) | (1 << (T + i)))
+    assert all(not (int(odd[i]) >> i) & 1 for i in range(T))
+    q, k, v = dev(c.q, dtype), dev(c.k, dtype), dev(c.v, dtype)
+    kd, vd = dev(c.k_draft, dtype), dev(c.v_draft, dtype)
+    nc = O.num_windows(n_ctx, 32, 16)
+    ck = torch.zeros((h_kv, nc, d), dtype=tdt(dtype), device="cuda")
+    B.infllmv2_compress_keys(k.unsqueeze(0), torch.tensor([n_ctx], dtype=torch.int32,
+                                                          device="cuda"), 0, nc,
+                             ck.unsqueeze(0), p)
+    plan = PL.TreePlan(T, n_ctx, h_q, h_kv, d, tdt(dtype), p)
+    plan.run(q, k, v, ck, kd, vd, torch.from_numpy(c.mask.astype(np.int64)).cuda())
+    torch.cuda.synchronize()
+    plain_out, plain_lse = plan.out.clone(), plan.lse.clone()
+    plan.run(q, k, v, ck, kd, vd, torch.from_numpy(odd.view(np.int64)).cuda())
+    torch.cuda.synchronize()
+    assert torch.equal(plan.out, plain_out) and torch.equal(plan.lse, plain_lse)
+    res = O.tree_verify(c.q, c.k, c.v, c.k_draft, c.v_draft, odd, p, dtype)
+    out = host(plan.out)
+    lse = plan.lse.cpu().numpy()
+    pos = n_ctx - 1
+    for i in range(T):
+        anc = sorted({i} | {j for j in range(T) if (int(odd[i]) >> j) & 1})
+        extra = (c.k_draft[:, anc], c.v_draft[:, anc])
+        if res["dense"]:
+            ref_o, ref_l = res["o"][i], res["lse"][i]
+        else:
+            sel = plan.block_idx.cpu().numpy()
+            P = [check_selection(sel[i, g], res["S"][i][g], res["sel"][i][g], pos, p,
+                                 f"draft {i} g {g}") for g in range(h_kv)]
+            ref_o, ref_l = O.attend_selected(c.q[i], c.k, c.v, P, pos, p, extra)
+        check_close(out[i], ref_o, dtype, f"draft {i}")
+        np.testing.assert_allclose(lse[i], ref_l, atol=2e-3 if dtype == "bf16" else 1e-4)
+
+
 # ------------------------------------------------------ whole-prompt prefill ----
 def test_chunked_prefill_whole_prompt(B, PL):
     """A 2560-token prompt prefilled in 5 chunks of 512 (the first, with fewer
