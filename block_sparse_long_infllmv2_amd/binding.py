@@ -37,12 +37,18 @@ class Params(ctypes.Structure):
                 ("score_mode", ctypes.c_int32)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
+DEBUG_LIB_PATH = os.path.join(_HERE, "libinfllmv2_debug.so")
+
+
+def _load(path=None):
+    """The library at `path` (default: the one this module binds) with its
+    functions' argument and result types set."""
+    path = path or LIB_PATH
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m block_sparse_long_infllmv2_amd.build` (hipcc, gfx950)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     PP = ctypes.POINTER(Params)
@@ -69,6 +75,8 @@ def _load():
                                                                  P, P, P, P, P, P, P, sz, PP,
                                                                  P]),
         "infllmv2_workspace_size": (sz, [ctypes.c_int, i32, i32, i32, i32, i64, PP]),
+        "infllmv2_debug_check": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int),
+                                                ctypes.POINTER(ctypes.c_int), P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)

@@ -21,6 +21,10 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libinfllmv2.so")
 OBJDIR = os.path.join(ROOT, "_build", "obj")
+# the same sources with -DINFLLMV2_DEBUG: every attention call first checks
+# the kept-block rows and tree masks it consumes (infllmv2_debug_check)
+DEBUG_LIB = os.path.join(HERE, "libinfllmv2_debug.so")
+DEBUG_OBJDIR = os.path.join(ROOT, "_build", "obj_debug")
 
 ARCH = "gfx950"
 CXXFLAGS = [
@@ -42,9 +46,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, hipcc: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *CXXFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, hipcc: str, debug: bool = False) -> str:
+    obj = os.path.join(DEBUG_OBJDIR if debug else OBJDIR, os.path.basename(src) + ".o")
+    cmd = [hipcc, *CXXFLAGS, *(["-DINFLLMV2_DEBUG"] if debug else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(ln for ln in (r.stderr or "").splitlines()
                      if "packed-fp32-ops" not in ln)
@@ -73,27 +77,39 @@ def build_probes(hipcc: str) -> list:
     return out
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    """Compile every csrc/*.hip and link libinfllmv2.so (and the probes);
-    returns the library's path."""
-    hipcc = _hipcc()
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, hipcc), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs: list, lib: str, hipcc: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 8, verbose: bool = True, debug: bool = True) -> str:
+    """Compile every csrc/*.hip and link libinfllmv2.so, the debug build
+    libinfllmv2_debug.so (unless debug=False) and the probes; returns the
+    library's path."""
+    hipcc = _hipcc()
+    os.makedirs(OBJDIR, exist_ok=True)
+    os.makedirs(DEBUG_OBJDIR, exist_ok=True)
+    srcs = sources()
+    jobs_list = [(s, False) for s in srcs] + ([(s, True) for s in srcs] if debug else [])
+    with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
+        objs = list(ex.map(lambda sd: _compile(sd[0], hipcc, sd[1]), jobs_list))
+    _link(objs[:len(srcs)], LIB, hipcc)
+    if debug:
+        _link(objs[len(srcs):], DEBUG_LIB, hipcc)
     probes = build_probes(hipcc)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources, {len(probes)} probe(s)")
+        print(f"built {LIB}{' and ' + DEBUG_LIB if debug else ''} from {len(srcs)} sources, "
+              f"{len(probes)} probe(s)")
     return LIB
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
-    build(ap.parse_args().jobs)
+    ap.add_argument("--no-debug", action="store_true", help="skip the debug build")
+    args = ap.parse_args()
+    build(args.jobs, debug=not args.no_debug)

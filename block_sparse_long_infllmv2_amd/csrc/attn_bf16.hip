@@ -1937,6 +1937,9 @@ extern "C" int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_
   a.cap = cap; a.n_k = n_k; a.n_rows = n_q; a.h_q = h_q; a.h_kv = h_kv; a.topk = r.topk;
   a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
+#ifdef INFLLMV2_DEBUG
+  if (!dense) INFLLMV2_TRY(debug_check_rows(block_idx, n_q, h_kv, r, n_k, n_q, nullptr, 0, st));
+#endif
   if (dtype == INFLLMV2_F32) return prefill_f32(a, d, st);
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
@@ -1977,6 +1980,10 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
   a.n_split = (int)n_split;
   hipStream_t st = (hipStream_t)stream;
+#ifdef INFLLMV2_DEBUG
+  if (max_seqlen >= r.dense_len)
+    INFLLMV2_TRY(debug_check_rows(block_idx, batch, h_kv, r, max_seqlen, 0, seqlens, 1, st));
+#endif
   if (dtype == INFLLMV2_F32) return decode_f32(a, d, st);
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
@@ -2100,6 +2107,11 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
   a.n_split = (int)n_split;
   hipStream_t st = (hipStream_t)stream;
+#ifdef INFLLMV2_DEBUG
+  INFLLMV2_TRY(debug_check_masks(tree_mask, n_draft, st));
+  if (!dense)
+    INFLLMV2_TRY(debug_check_rows(block_idx, n_draft, h_kv, r, n_ctx, 0, nullptr, 2, st));
+#endif
   if (dtype == INFLLMV2_F32) return tree_f32(a, d, st);
   const int G = h_q / h_kv;
   if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;

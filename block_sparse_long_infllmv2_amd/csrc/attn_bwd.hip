@@ -895,6 +895,9 @@ extern "C" int infllmv2_sparse_attn_prefill_backward(
   a.max_items = pl.max_items; a.dense = dense ? 1 : 0;
   a.scale = r.scale; a.scale_log2 = r.scale * kLog2e;
   hipStream_t st = (hipStream_t)stream;
+#ifdef INFLLMV2_DEBUG
+  if (!dense) INFLLMV2_TRY(debug_check_rows(block_idx, n_q, h_kv, r, n_k, n_q, nullptr, 0, st));
+#endif
   if (f32) {
     if ((int64_t)n_q * h_q >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
     const unsigned blocks = (unsigned)ceil_div((int64_t)n_q * h_q * (d / 4), 256);

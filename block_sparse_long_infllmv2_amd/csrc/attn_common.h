@@ -36,6 +36,13 @@ struct AttnArgs {
 };
 
 
+// Debug builds (-DINFLLMV2_DEBUG): checks of the kept-block rows / tree masks
+// a call consumes (mode 0 prefill, 1 decode, 2 tree), queued before its
+// attention kernels.
+int debug_check_rows(const int32_t* block_idx, int rows, int h_kv, const Resolved& r,
+                     int64_t n_k, int n_q, const int32_t* seqlens, int mode, hipStream_t st);
+int debug_check_masks(const uint64_t* mask, int n_draft, hipStream_t st);
+
 // float32 (vector ALU) attention: exact-precision path for float32 inputs.
 int prefill_f32(const AttnArgs& a, int d, hipStream_t st);
 int decode_f32(const AttnArgs& a, int d, hipStream_t st);

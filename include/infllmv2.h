@@ -310,6 +310,25 @@ int infllmv2_sparse_attn_prefill_backward(int dtype, const void* q, int32_t n_q,
                                           float* dv, void* ws, size_t ws_bytes,
                                           const infllmv2_params* p, void* stream);
 
+/*
+ * host: input checks of the debug build.  A library built with
+ * -DINFLLMV2_DEBUG (libinfllmv2_debug.so) checks, before the attention
+ * kernels of every infllmv2_sparse_attn_prefill / _decode / _tree_verify /
+ * _prefill_backward call, the kept-block rows it will read (min(topk,
+ * eligible) strictly ascending ids in range, the forced initial and local
+ * blocks among them, then -1 padding; rows of dense sequences are skipped)
+ * and the tree masks (no bit at or above n_draft, none naming a later draft).
+ * The kernels never read out of bounds on such input, but their results are
+ * then not those of a valid selection.  This call waits for `stream`,
+ * returns in *code the first violation since the previous call (0 none;
+ * 1 id out of range, 2 not ascending or duplicated, 3 padding before an id,
+ * 4 forced block missing, 5 wrong count, 6 mask bit at or above n_draft,
+ * 7 mask bit naming a later draft) and in *where its row * h_kv + KV head
+ * (or the draft index for 6 and 7), and clears them.  Without
+ * INFLLMV2_DEBUG it returns INFLLMV2_ERR_UNSUPPORTED and touches nothing.
+ */
+int infllmv2_debug_check(int* code, int* where, void* stream);
+
 enum { INFLLMV2_OP_DECODE = 0, INFLLMV2_OP_TREE = 1, INFLLMV2_OP_PREFILL_BWD = 2 };
 
 /* host: workspace bytes needed by infllmv2_sparse_attn_decode (op DECODE,

@@ -44,6 +44,8 @@ def lib():
                                                 i32, i32, P, P, P, P, sz, PP, P]
     lib.infllmv2_sparse_attn_decode_noalloc.argtypes = [ctypes.c_int, P, i32, P, P, i64, P,
                                                         i32, i32, i32, i32, P, P, P, PP, P]
+    lib.infllmv2_debug_check.argtypes = [ctypes.POINTER(ctypes.c_int),
+                                         ctypes.POINTER(ctypes.c_int), P]
     lib.infllmv2_tree_verify.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P, i32,
                                          i32, i32, P, P, P, P, sz, PP, P]
     lib.infllmv2_sparse_attn_prefill_backward.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64,
@@ -207,3 +209,11 @@ def test_decode_noalloc_host_checks(lib):
     assert lib.infllmv2_sparse_attn_decode_noalloc(*args(4, d=96), params(lib),
                                                    None) == UNSUPPORTED
     assert lib.infllmv2_sparse_attn_decode_noalloc(*args(4, ml=0), params(lib), None) == INVALID
+
+
+def test_debug_check_unsupported_without_debug_build(lib):
+    """The normal library has no input checks compiled in: the call says so
+    and touches nothing (no GPU needed)."""
+    code, where = ctypes.c_int(7), ctypes.c_int(7)
+    assert lib.infllmv2_debug_check(ctypes.byref(code), ctypes.byref(where), None) == UNSUPPORTED
+    assert (code.value, where.value) == (7, 7)
