@@ -220,15 +220,16 @@ __global__ __launch_bounds__(kPlanThreads1) void bwd_plan_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dK / dV, key-major.  Tiles of 32 (row, head) pairs of the item's segment
-// are staged as [pair][d] rows with the chunk swizzle of Swz16V (16-byte row
-// reads and transposing reads both free of bank conflicts).
+// are staged as [pair][d] rows, logical 16-byte chunk c of row r at chunk
+// c ^ f(r), and read twice: as rows (16-byte reads) and transposed (8-byte
+// transposing reads), with the swizzle made for that pair of patterns.
 // ---------------------------------------------------------------------------
 template <int D>
 struct PairTile {
   static constexpr int RB = 2 * D;                  // bytes per pair row
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int BYTES = 32 * RB;             // one tensor (Q or dO)
-  __device__ static __forceinline__ int f(int r) { return Swz16V<D>::f(r); }
+  __device__ static __forceinline__ int f(int r) { return Swz16RT<D, Swz16V<D>>::f(r); }
   // byte offset of logical chunk c of pair row r
   __device__ static __forceinline__ uint32_t at(int r, int c) {
     return (uint32_t)(r * RB + ((c ^ f(r)) * 16));
@@ -491,9 +492,9 @@ void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // dQ, query-major.  W waves of 16 (row, head) pairs: pair p of the workgroup
-// is token p / G, head p % G of KV group g.  K and V tiles (Swz16K chunk
-// swizzle) serve 16-byte row reads (S^T and dP^T) and, for K, transposing
-// reads (dQ^T = K^T dS^T).
+// is token p / G, head p % G of KV group g.  K and V tiles serve 16-byte row
+// reads (S^T and dP^T) and, for K, transposing reads (dQ^T = K^T dS^T): the
+// swizzle made for that pair of patterns.
 // ---------------------------------------------------------------------------
 // Four waves per SIMD (128 VGPRs, no spills): two 8-wave workgroups share a
 // CU, and each hides the other's staging and LDS waits (1.83 -> 1.26 ms on
@@ -505,10 +506,7 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int TT = (16 * W) / G;                 // tokens per workgroup
   static_assert(TT >= 1 && TT <= 32, "token bitmask is 32 bits");
   constexpr int NKS = D / 32, NDT = D / 16;
-  // the forward's K layout for both tiles: its 16-byte reads are free of bank
-  // conflicts, the transposing reads of K less so (measured: fewer conflict
-  // cycles and a shorter kernel than with the transposing-read layout)
-  using SW = Swz16K<D>;
+  using SW = Swz16RT<D, Swz16K<D>>;
   constexpr int TILE = SW::TILE;
   constexpr int RB = SW::RB;
   constexpr int SORT_N = TT * kSortCap;

@@ -234,4 +234,24 @@ struct Swz16V {
 };
 template <int D> using Swz16 = Swz16V<D>;   // tile geometry (same for K and V)
 
+// A tile read both ways: as rows (lane (jj, hh) reads row jj, logical chunk
+// 4 ks + hh, with 16-byte reads) and transposed (row 4 hh + jj / 4, chunk
+// 2 dt + (jj % 4) / 2, half jj % 2, with 8-byte transposing reads), as the
+// backward kernels read theirs.  For D = 128, f is the XOR-linear map of the
+// row's low four bits with f(1) = 12, f(2) = 15, f(4) = 4, f(8) = 5: of all
+// 20160 such maps, timed on gfx950 for exactly these two patterns
+// (probes/lds_swizzle_search.hip), one within 5 % of the fastest for both.
+// Swz16V runs the row reads 1.7x slower (bank conflicts), Swz16K the
+// transposed reads 1.8x.  Other D keep Base's map.
+template <int D, class Base>
+struct Swz16RT : Base {
+  __device__ static __forceinline__ int f(int r) {
+    if constexpr (D == 128)
+      return (-(r & 1) & 12) ^ (-((r >> 1) & 1) & 15) ^ (-((r >> 2) & 1) & 4) ^
+             (-((r >> 3) & 1) & 5);
+    else
+      return Base::f(r);
+  }
+};
+
 }  // namespace infllmv2
