@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   constexpr int kStageTiles = kStageBlocks / BPT;  // tiles per staged group
   __shared__ __attribute__((aligned(16))) uint16_t qlds[2][kMfmaRows][D + 8];
   __shared__ int pos_lds[kMfmaRows];
+  __shared__ int own_lds[kMfmaRows];               // the row's own block, -1: no row
   __shared__ __attribute__((aligned(16))) float stage[kMfmaWaves][kMfmaRows * kStageStride];
 
   const int w = xcd_contiguous_index(blockIdx.x, gridDim.x);
@@ -205,6 +206,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       pos = (p >= L || p > a.max_pos || p < 0) ? -1 : (int)p;
     }
     pos_lds[tid] = pos;
+    own_lds[tid] = pos < 0 ? -1 : pos / a.B;
   }
   __syncthreads();
 
@@ -297,9 +299,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
 #pragma unroll 1
     for (int i = 0; i < kMfmaRows / 8; ++i) {
       const int rr = 8 * i + sub;
-      const int p = pos_lds[rr];
-      if (!in || p < 0) continue;
-      const int bo = p / a.B;
+      const int bo = own_lds[rr];
+      if (!in || bo < 0) continue;
       const f32x4 v = *reinterpret_cast<const f32x4*>(&sw[rr * kStageStride + 4 * piece]);
       float* o = a.scores + ((int64_t)(r0 + rr) * a.h_kv + g) * a.nb_cap + blk;
       if (blk + 3 <= bo && a.vec_store) {

@@ -124,21 +124,114 @@ __global__ __launch_bounds__(kTopkThreads) void select_topk_kernel(TopkArgs a) {
 
 // ---------------------------------------------------------------------------
 // One wave per (row, KV head) when the eligible blocks fit in registers
-// (64 * KPL of them).  Keys live in registers (KPL per lane, block
-// b = lane + 64 j); a bitwise search builds the threshold T from the most
-// significant bit down, counting keys >= candidate with ballots and scalar
-// popcounts -- no LDS atomics, no barriers.  The search stops early as soon
-// as some candidate admits exactly `need` keys.  The ascending output order
-// comes from ballot prefix counts (block b = lane + 64 j precedes b' when
-// j < j', or j == j' and lane < lane').
+// (64 * KPL of them): lane l holds the scores of blocks b = l + 64 j
+// (coalesced loads; ascending block order is (j, lane) order).
+//   1. Non-candidates (forced blocks, blocks past the row) become NaN, which
+//      no comparison admits; only the 64-block pieces that reach them are
+//      touched.
+//   2. Lower bound lo: at least `need` lanes hold a score >= the need-th
+//      largest lane maximum, so the threshold is >= it.  A bitwise search
+//      over the 64 lane-maximum keys finds it.
+//   3. Survivors (score >= lo, typically 100-260 of 2048) are compacted
+//      into LDS as (score, block) in ascending block order, from ballots.
+//   4. The threshold T (the need-th largest survivor key), the ranks of the
+//      ties at T (lowest index first) and the output slots all come from
+//      ballots over the survivors, at most kWaveSurvivors / 64 per lane.
+// Rows where the bound is not finite (fewer than `need` finite lane maxima,
+// or need > 64) or whose survivors overflow take a search over every key.
+// Scores compare as floats in steps 1-3 (-0 == +0); keys are the
+// order-preserving uint32 images, NaN candidates ranking below -inf.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float vmax3(float x, float y, float z) {
+  // plain v_max3_f32: NaN operands are ignored, and no canonicalising
+  // instructions are inserted for loaded values
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "v"(y), "v"(z));
+  return r;
+}
+
+constexpr int kWaveSurvivors = 512;   // per wave; a 2048-block row keeps ~100-260
+
+// The k-th largest of one key per lane (1 <= k <= 64; hi = the largest).
+// Close to either end (top-64 rows need the 61st largest = 4th smallest,
+// top-6 rows the 3rd largest), a few wave extrema, each removing all lanes
+// equal to it, find it; otherwise the bitwise search, whose early stop may
+// land between two lane values, then the smallest lane value at or above.
+__device__ __forceinline__ uint32_t kth_largest_of_lanes(uint32_t v, int k, uint32_t hi) {
+  const bool from_top = k <= 32;
+  int r = from_top ? k : 65 - k;         // rank from the nearer end
+  if (r <= 8) {
+    for (;;) {
+      const uint32_t e = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)(from_top ? wave_max_u32(v) : wave_min_u32(v)));
+      const int c = __popcll(__ballot(v == e));
+      if (c >= r) return e;
+      r -= c;
+      v = v == e ? (from_top ? 0u : 0xffffffffu) : v;
+    }
+  }
+  const uint32_t key[1] = {v};
+  bool ex = false;
+  const uint32_t t = threshold_search<1>(key, k, 0u, hi, &ex);
+  return t == 0u ? 0u
+                 : (uint32_t)__builtin_amdgcn_readfirstlane(
+                       (int)wave_min_u32(v >= t ? v : 0xffffffffu));
+}
+
+// Step 4 over n_s survivors held as (score bits, block) in ascending block
+// order, SPL per lane (n_s <= 64 SPL): the need-th largest key T, the ties
+// at T taken lowest index first, the chosen blocks written to out[f_init ..
+// f_init + need) in ascending order.
+template <int SPL>
+__device__ __forceinline__ void select_survivors(const int2* svw, int n_s, int need,
+                                                 uint32_t lo_key, uint32_t hi_key, int f_init,
+                                                 int32_t* out, int lane) {
+  uint32_t sk[SPL];
+  int32_t sbk[SPL];
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    const int q = lane + 64 * i;
+    const int2 e = svw[q];
+    sk[i] = q < n_s ? orderable_key(__int_as_float(e.x)) : 0u;   // survivors: keys > 0
+    sbk[i] = e.y;
+  }
+  bool exact = false;
+  const uint32_t T = threshold_search<SPL>(sk, need, lo_key, hi_key, &exact);
+  int take = 0;
+  if (!exact) {
+    int gt = 0;
+#pragma unroll
+    for (int i = 0; i < SPL; ++i) gt += __popcll(__ballot(sk[i] > T));
+    take = need - gt;
+  }
+  // (i, lane) order is block order
+  int slot = f_init, eq_seen = 0;
+#pragma unroll
+  for (int i = 0; i < SPL; ++i) {
+    bool sel;
+    if (exact) {
+      sel = sk[i] >= T;
+    } else {
+      const uint64_t eqm = __ballot(sk[i] == T);
+      const int rank = eq_seen + lanes_below(eqm);
+      eq_seen += __popcll(eqm);
+      sel = sk[i] > T || (sk[i] == T && rank < take);
+    }
+    const uint64_t selm = __ballot(sel);
+    if (sel) out[slot + lanes_below(selm)] = sbk[i];
+    slot += __popcll(selm);
+  }
+}
+
 template <int KPL>
-__global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n_units) {
-  // per wave: survivors (+ one dummy slot per lane) and the ordered selection
-  // (+ one dummy slot per lane), so that no lane needs a branch to write
-  __shared__ uint32_t surv[4][kSurvivors + 64];
-  __shared__ int32_t sel_lds[4][kMaxTopk + 64];
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KPL <= 32 ? 6 : 1)))
+void select_topk_wave_kernel(TopkArgs a, int n_units) {
+  // per wave: survivors (+ one dummy slot per lane, so that no lane needs a
+  // branch to write); the full-search path reuses sv_b for its selection
+  __shared__ int2 sv[4][kWaveSurvivors + 64];   // (score bits, block)
+  static_assert(kWaveSurvivors >= kMaxTopk, "selection staging fits the survivor slots");
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int unit = blockIdx.x * 4 + wv;
   if (unit >= n_units) return;                   // whole wave leaves
   const int lane = threadIdx.x & 63;
   const int r = unit / a.h_kv, g = unit % a.h_kv;
@@ -169,111 +262,126 @@ __global__ __launch_bounds__(256) void select_topk_wave_kernel(TopkArgs a, int n
   // disjoint runs [0, f_init) and [f_lo, n_elig), and the candidates are
   // exactly the blocks in between: [f_init, f_lo).  The output is the first
   // run, the chosen candidates in ascending order, then the second run.
-  // key 0 = not a candidate; candidates >= 1.  Every lane loads (an in-range
-  // index), then selects: no divergent branch.
   // Entries past n_elig but inside the row (< nb_cap) are read as they are
   // and never become candidates, so a row of at least 64 * KPL entries needs
   // no index clamp.
-  uint32_t key[KPL];
   const uint32_t span = (uint32_t)(f_lo - f_init);
-  auto prep = [&](int j, float x) {
-    const uint32_t k = orderable_key(x);
-    key[j] = (uint32_t)(lane + 64 * j - f_init) < span ? (k > 1u ? k : 1u) : 0u;
-  };
+  auto is_cand = [&](int j) { return (uint32_t)(lane + 64 * j - f_init) < span; };
+  float x[KPL];
   if (a.nb_cap >= 64 * KPL) {
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) prep(j, S[lane + 64 * j]);
+    for (int j = 0; j < KPL; ++j) x[j] = S[lane + 64 * j];
   } else {
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int b = lane + 64 * j;
-      prep(j, S[b < n_elig ? b : n_elig - 1]);
+      x[j] = S[b < n_elig ? b : n_elig - 1];
     }
   }
-  // T = largest value with #(key >= T) >= need (the need-th largest key)
-  uint32_t T = 0;
-  bool exact = need <= 0;       // nothing to choose, or #(key >= T) == need
-  if (need > 0) {
-    // Lower bound: at least `need` lanes hold a key >= the need-th largest
-    // lane maximum, so T >= it and smaller keys cannot matter.  The keys at
-    // or above it usually number a few hundred: the search then runs on them
-    // (kSurvivors per wave in LDS) instead of on all 64 * KPL keys.
-    uint32_t lo = 0, hi = 0xffffffffu;
-    if (need <= 64) {
-      uint32_t mx = 0;
+  // the out slots: [0, f_init) init run, [f_init, lim) chosen, then the local run
+  const int lim = f_init + (need > 0 ? need : 0);
+  const int n_local = n_elig - f_lo;
+  int2* svw = sv[wv];
+
+  // fast path: steps 1-4 above
+  bool done = need <= 0;
+  if (need > 0 && need <= 64) {
+    // in place: a candidate keeps its score (the full search below tests
+    // is_cand itself and reads candidates only)
+    // (on the vector ALU: the scalar unit carries this kernel's searches)
+    const float qnan = __builtin_nanf("");
+    const uint32_t c0 = (uint32_t)(lane - f_init);
 #pragma unroll
-      for (int j = 0; j < KPL; ++j) mx = key[j] > mx ? key[j] : mx;
-      lo = wave_kth_largest(mx, need, lane, &hi);
-    }
-    int mine = 0;
+    for (int j = 0; j < KPL; ++j) x[j] = c0 + 64u * j < span ? x[j] : qnan;
+    float mx = x[0];
+    int j0 = 1;
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) mine += key[j] >= lo && key[j] != 0u;
-    int total;
-    const int off = wave_excl_scan(mine, &total, lane);
-    uint32_t* sv = surv[threadIdx.x >> 6];
-    if (lo != 0u && total <= kSurvivors) {
-      for (int i = lane; i < kSurvivors; i += 64) sv[i] = 0u;
-      __builtin_amdgcn_wave_barrier();
-      int o = off;
+    for (; j0 + 1 < KPL; j0 += 2) mx = vmax3(mx, x[j0], x[j0 + 1]);
+    if (j0 < KPL) mx = vmax3(mx, x[j0], x[j0]);
+    // lane maximum key (NaN: no candidate -> 0) and the wave's largest
+    const uint32_t mk[1] = {orderable_key(mx)};
+    const uint32_t hk = (uint32_t)__builtin_amdgcn_readfirstlane((int)wave_max_u32(mk[0]));
+    // the need-th largest lane maximum (0 if fewer than `need` lanes hold
+    // one; empty lanes hold 0)
+    const uint32_t lo_key = kth_largest_of_lanes(mk[0], need, hk);
+    if (lo_key > orderable_key(-INFINITY)) {
+      // lo as a float, by the inverse of the key map: y >= lo  <=>
+      // key(y) >= lo_key for every non-NaN y (lo_key is a lane maximum's key,
+      // at most key(+inf))
+      const float lo = __uint_as_float((lo_key & 0x80000000u) ? (lo_key & 0x7fffffffu) : ~lo_key);
+      // n_s only grows: once a piece does not fit, no later one does, and
+      // n_s > kWaveSurvivors afterwards sends the row to the full search.
+      // Lanes that keep nothing write a dummy slot (no branch per piece).
+      int n_s = 0;                 // wave-uniform
 #pragma unroll
       for (int j = 0; j < KPL; ++j) {
-        const bool keep = key[j] >= lo && key[j] != 0u;
-        sv[keep ? o : kSurvivors + lane] = key[j];
-        o += keep ? 1 : 0;
+        const bool keep = x[j] >= lo;
+        const uint64_t m = __ballot(keep);
+        const int c = __popcll(m);
+        const bool ok = keep && n_s + c <= kWaveSurvivors;
+        svw[ok ? n_s + lanes_below(m) : kWaveSurvivors + lane] =
+            make_int2(__float_as_int(x[j]), lane + 64 * j);
+        n_s += c;
       }
-      __builtin_amdgcn_wave_barrier();
-      uint32_t sk[kSurvivors / 64];
-#pragma unroll
-      for (int j = 0; j < kSurvivors / 64; ++j) sk[j] = sv[lane + 64 * j];
-      T = threshold_search<kSurvivors / 64>(sk, need, lo, hi, &exact);
-    } else {
-      T = threshold_search<KPL>(key, need, 0u, hi, &exact);
+      if (n_s <= kWaveSurvivors) {
+        __builtin_amdgcn_wave_barrier();
+        if (n_s <= 256)
+          select_survivors<4>(svw, n_s, need, lo_key, hk, f_init, out, lane);
+        else
+          select_survivors<kWaveSurvivors / 64>(svw, n_s, need, lo_key, hk, f_init, out, lane);
+        done = true;
+      }
     }
   }
-  // keys > T are kept; of the keys == T the lowest-indexed ones fill the rest
-  int take = 0;
-  if (!exact) {
-    int gt = 0;
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
-    take = need - gt;
-  }
-  // chosen candidates go to slots f_init, f_init + 1, ... in ascending order;
-  // the two forced runs fill the slots around them.  Separate loops on
-  // wave-uniform conditions keep the unrolled bodies free of branches.
-  const int wv = threadIdx.x >> 6;
-  int base = f_init;
-  const int lim = f_init + (need > 0 ? need : 0);
-  auto emit = [&](int j, bool sel) {
-    const uint64_t selm = __ballot(sel);
-    const int slot = base + lanes_below(selm);
-    const int ok = (int)sel & (int)(slot < lim);            // no short-circuit branch
-    sel_lds[wv][ok ? slot : kMaxTopk + lane] = lane + 64 * j;
-    base += __popcll(selm);
-  };
-  const int mode = __builtin_amdgcn_readfirstlane(need <= 0 ? 0 : (exact ? 1 : 2));
-  if (mode == 1) {
-#pragma unroll
-    for (int j = 0; j < KPL; ++j) emit(j, key[j] >= T);
-  } else if (mode == 2) {
-    int eq_seen = 0;
+  if (!done) {
+    // every key: the bitwise search over all of them
+    uint32_t key[KPL];
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
-      const uint64_t eqm = __ballot(key[j] == T);
-      const int rank = eq_seen + lanes_below(eqm);
-      eq_seen += __popcll(eqm);
-      emit(j, (int)(key[j] > T) | ((int)(key[j] == T) & (int)(rank < take)));
+      const uint32_t k = orderable_key(x[j]);
+      key[j] = is_cand(j) ? (k > 1u ? k : 1u) : 0u;
     }
+    uint32_t hi = 0u;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) hi = key[j] > hi ? key[j] : hi;
+    hi = wave_max_u32(hi);
+    bool exact = false;
+    const uint32_t T = threshold_search<KPL>(key, need, 0u, hi, &exact);
+    int take = 0;
+    if (!exact) {
+      int gt = 0;
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) gt += __popcll(__ballot(key[j] > T));
+      take = need - gt;
+    }
+    // chosen candidates go to slots f_init, f_init + 1, ... in ascending
+    // order, staged in LDS
+    int base = f_init, eq_seen = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      bool sel;
+      if (exact) {
+        sel = key[j] >= T;
+      } else {
+        const uint64_t eqm = __ballot(key[j] == T);
+        const int rank = eq_seen + lanes_below(eqm);
+        eq_seen += __popcll(eqm);
+        sel = key[j] > T || (key[j] == T && rank < take);
+      }
+      const uint64_t selm = __ballot(sel);
+      const int slot = base + lanes_below(selm);
+      const int ok = (int)sel & (int)(slot < lim);           // no short-circuit branch
+      svw[ok ? slot : kWaveSurvivors + lane].y = lane + 64 * j;
+      base += __popcll(selm);
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int i = lane; i < a.topk; i += 64)
+      if (i >= f_init && i < lim) out[i] = svw[i].y;
   }
-  __builtin_amdgcn_wave_barrier();
-  // slots: [0, f_init) init run, [f_init, lim) chosen, then the local run
-  const int n_local = n_elig - f_lo;
+  // the forced runs and the padding
   for (int i = lane; i < a.topk; i += 64) {
-    int v = -1;
-    if (i < f_init) v = i;
-    else if (i < lim) v = sel_lds[wv][i];
-    else if (i < lim + n_local) v = f_lo + (i - lim);
-    out[i] = v;
+    if (i < f_init) out[i] = i;
+    else if (i >= lim) out[i] = i < lim + n_local ? f_lo + (i - lim) : -1;
   }
 }
 
@@ -328,7 +436,10 @@ extern "C" int infllmv2_select_topk(const float* scores, int32_t rows,
     return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
   }
   // eligible blocks per row <= nb_cap: registers hold 64 * KPL keys per wave
-  if (nb_cap <= 64 * 32)
+  if (nb_cap <= 64 * 16)
+    hipLaunchKernelGGL(select_topk_wave_kernel<16>, dim3((unsigned)((n_units + 3) / 4)),
+                       dim3(256), 0, st, a, n_units);
+  else if (nb_cap <= 64 * 32)
     hipLaunchKernelGGL(select_topk_wave_kernel<32>, dim3((unsigned)((n_units + 3) / 4)),
                        dim3(256), 0, st, a, n_units);
   else if (nb_cap <= 64 * 64)

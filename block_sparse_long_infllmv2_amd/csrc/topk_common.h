@@ -78,6 +78,23 @@ __device__ __forceinline__ uint32_t wave_kth_largest(uint32_t v, int k, int lane
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 64 - k);
 }
 
+// Largest (MAX) or smallest value over the wave, in every lane: row
+// reductions by DPP, then the cross-row swaps.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_extreme_u32(uint32_t v) {
+  auto pick = [](uint32_t x, uint32_t y) { return (MAX ? x > y : x < y) ? x : y; };
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));  // quad [1,0,3,2]
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));  // quad [2,3,0,1]
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false)); // row half mirror
+  v = pick(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false)); // row mirror
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = pick(s16[0], s16[1]);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return pick(s32[0], s32[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return wave_extreme_u32<true>(v); }
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return wave_extreme_u32<false>(v); }
+
 // Exclusive prefix sum over the lanes of a wave; *total = sum over all lanes.
 __device__ __forceinline__ int wave_excl_scan(int v, int* total, int lane) {
   int x = v;
@@ -102,6 +119,10 @@ __device__ __forceinline__ int wave_excl_scan(int v, int* total, int lane) {
 template <int N>
 __device__ __forceinline__ uint32_t threshold_search(const uint32_t (&key)[N], int need,
                                                      uint32_t lo, uint32_t hi, bool* exact) {
+  // lo and hi are the same in every lane: scalar registers keep the loop's
+  // candidate and counts off the vector ALU
+  lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)lo);
+  hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)hi);
   const uint32_t diff = lo ^ hi;
   const int top = diff ? 31 - __builtin_clz(diff) : -1;
   uint32_t T = top >= 0 ? lo & ~((2u << top) - 1u) : lo;
