@@ -4,7 +4,9 @@
 // LLMs on phones and PCs" (xugj520.cn), section 1.1 (initial tokens and a
 // sliding window are always kept).
 //
-// One workgroup per (row, KV head).  Scores become order-preserving uint32
+// Rows of up to 4096 eligible blocks take one wave per (row, KV head)
+// (select_topk_wave_kernel, below).  Longer rows: one workgroup per (row,
+// KV head).  Scores become order-preserving uint32
 // keys (staged in LDS when they fit); an MSB-first radix select (four 8-bit
 // digits, LDS histogram, suffix scan to pick the digit) finds the threshold
 // key T of the need-th best non-forced block.  Blocks with key > T are kept,
@@ -385,25 +387,6 @@ void select_topk_wave_kernel(TopkArgs a, int n_units) {
   }
 }
 
-// ---------------------------------------------------------------------------
-// Few rows (decode, tree verification): one 256-thread workgroup per (row,
-// KV head), so a row's work is spread over four waves instead of one.
-// Thread t owns the KPT consecutive blocks [KPT t, KPT t + KPT) (coalesced
-// loads; ascending block order = thread order, so ties and the output order
-// come from block prefix scans).
-//   lower bound: each wave's need-th largest lane maximum is a lower bound of
-//     the threshold (that wave alone holds `need` keys at or above it), so is
-//     their maximum;
-//   keys at or above it (<= kSurvivors) go to LDS and wave 0 runs the bitwise
-//     threshold search on them; a full block-wide search is the fallback.
-// ---------------------------------------------------------------------------
-// c-th largest (1 <= c <= N) of N values: the one with exactly c - 1 values
-// ahead of it in (value descending, index ascending) order.
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void select_topk_block_kernel(TopkArgs a) {
-  topk_block_row<KPT>(a, blockIdx.x / a.h_kv, blockIdx.x % a.h_kv);
-}
-
 }  // namespace infllmv2
 
 using namespace infllmv2;
@@ -425,17 +408,9 @@ extern "C" int infllmv2_select_topk(const float* scores, int32_t rows,
   a.init = r.init; a.local = r.local; a.dense_len = r.dense_len; a.batch = batch;
   const int n_units = rows * h_kv;
   hipStream_t st = (hipStream_t)stream;
-  // few rows: a workgroup per row (KPT consecutive blocks per thread)
-  if (n_units <= kFewRows && nb_cap <= (int64_t)kTopkThreads * 16) {
-    if (nb_cap <= kTopkThreads * 8)
-      hipLaunchKernelGGL(select_topk_block_kernel<8>, dim3((unsigned)n_units),
-                         dim3(kTopkThreads), 0, st, a);
-    else
-      hipLaunchKernelGGL(select_topk_block_kernel<16>, dim3((unsigned)n_units),
-                         dim3(kTopkThreads), 0, st, a);
-    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
-  }
-  // eligible blocks per row <= nb_cap: registers hold 64 * KPL keys per wave
+  // rows of up to 64 * KPL eligible blocks: a wave per row, the keys in
+  // registers (for a handful of decode rows too: one wave per row finishes
+  // sooner than a workgroup per row with barriers)
   if (nb_cap <= 64 * 16)
     hipLaunchKernelGGL(select_topk_wave_kernel<16>, dim3((unsigned)((n_units + 3) / 4)),
                        dim3(256), 0, st, a, n_units);

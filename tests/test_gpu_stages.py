@@ -157,7 +157,7 @@ def _scores_case(B, dtype, d, h_q, h_kv, rows, p):
 
 
 # ----------------------------------------------------------------- topk ----
-@pytest.mark.parametrize("rows", [24, 300])   # few rows: workgroup per row; many: wave per row
+@pytest.mark.parametrize("rows", [24, 300])   # a few decode-sized rows, and many
 def test_select_topk_matches_oracle_exactly(B, rows):
     _say(f"topk exact rows={rows}")
     rng = np.random.default_rng(4)
