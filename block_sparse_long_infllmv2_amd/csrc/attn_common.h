@@ -32,6 +32,9 @@ struct AttnArgs {
   int64_t n_k;                // prefill: keys; tree: context length
   int n_rows;                 // prefill: n_q; decode: batch; tree: n_draft
   int h_q, h_kv, topk, B, dense_len, n_split, n_tiles, union_cap;
+  int ring_min;               // prefill, 16-head groups: blocks kept by at least this
+                              // many of a tile's tokens go through the shared ring,
+                              // the others through each token's own pass (0: all ring)
   float scale_log2;           // softmax scale * log2(e)
 };
 
