@@ -244,13 +244,20 @@ __device__ __forceinline__ void lds_dma4(uint32_t lds_addr, const void* gbase, u
 }
 
 // Staging ring of the dK/dV kernel: per slot the Q and dO tiles of 32 pairs
-// and, per wave, its own copy of the 32 pairs' (lse * log2 e, dsum).
+// and, per wave, its own copy of the 32 pairs' (lse * log2 e, dsum).  The Q
+// tiles of all slots come first, then the dO tiles, then the metadata, so
+// that every tile byte lies below 64 KiB: with the slot known at compile
+// time, a fragment read is its lane's base register plus an immediate.
 constexpr int kDkdvStages = 4;
-template <int D, int NW>
+template <int D, int NW, int NS>
 struct DkdvRing {
   static constexpr int TB = PairTile<D>::BYTES;
   static constexpr int META = 32 * 8;
-  static constexpr int SLOT = 2 * TB + NW * META;
+  static constexpr int BYTES = 2 * NS * TB + NS * NW * META;
+  static constexpr int q(int slot) { return slot * TB; }
+  static constexpr int o(int slot) { return (NS + slot) * TB; }
+  static constexpr int meta(int slot, int wave) { return 2 * NS * TB + (slot * NW + wave) * META; }
+  static_assert(2 * NS * TB <= 65536, "tile bytes within the immediate offset range");
   // 16-byte copies per tile (Q then dO), split evenly over the NW waves
   static constexpr int INSTR = 2 * 32 * PairTile<D>::CPR / 64;
   static constexpr int PER_WAVE = INSTR / NW;
@@ -266,11 +273,15 @@ void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32, NDT = D / 16;
   constexpr int SEG_ROWS = seg_rows_for(G);
   using PT = PairTile<D>;
-  using RG = DkdvRing<D, NW>;
+  using RG = DkdvRing<D, NW, NS>;
   constexpr int KL = RG::KL;
   static_assert(KL * (NS - 2) <= 63, "vmcnt range");
-  __shared__ __attribute__((aligned(16))) uint8_t ring[NS * RG::SLOT];
+  __shared__ __attribute__((aligned(16))) uint8_t ring[RG::BYTES];
   __shared__ int rows_lds[SEG_ROWS];
+  // row * h_q + g * G (the pair index of the row's head 0), when a segment
+  // has few enough rows that the table costs no occupancy
+  constexpr bool kPbase = SEG_ROWS <= 1024;
+  __shared__ uint32_t pbase_lds[kPbase ? SEG_ROWS : 1];
   __shared__ int scan_lds[NT / 64];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -310,6 +321,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
     n_rows = max(0, hi - lo);
   }
   __syncthreads();
+  if constexpr (kPbase) {
+    for (int i = tid; i < n_rows; i += NT)
+      pbase_lds[i] = (uint32_t)rows_lds[i] * (uint32_t)a.h_q + (uint32_t)(g * G);
+    __syncthreads();
+  }
   const int n_pairs = n_rows * G;
   const int n_tiles = __builtin_amdgcn_readfirstlane((n_pairs + 31) / 32);
   if (n_tiles <= 0) return;
@@ -353,7 +369,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   const uint32_t n_pairs_u = (uint32_t)n_pairs, hq_u = (uint32_t)a.h_q, hg = (uint32_t)(g * G);
   auto pair_index = [&](uint32_t p) -> uint32_t {
     p = min(p, n_pairs_u - 1u);
-    return __umul24((uint32_t)rows_lds[p / G], hq_u) + hg + p % G;
+    if constexpr (kPbase) return pbase_lds[p / G] + p % G;
+    else return __umul24((uint32_t)rows_lds[p / G], hq_u) + hg + p % G;
   };
   // per lane and copy: pair row r and logical chunk c do not depend on the tile
   uint32_t cp_r[RG::PER_WAVE], cp_c16[RG::PER_WAVE];
@@ -365,18 +382,20 @@ void bwd_dkdv_kernel(BwdArgs a) {
     cp_c16[i] = (uint32_t)(16 * (pc ^ PT::f(r)));
   }
   auto issue = [&](int t, int slot) {
-    const uint32_t sb = ring0 + (uint32_t)(slot * RG::SLOT);
     const uint32_t p0 = (uint32_t)t * 32u;
 #pragma unroll
     for (int i = 0; i < RG::PER_WAVE; ++i) {
       const int j = wave_u * RG::PER_WAVE + i;              // copy index in the tile
       // the 64 slots of copy j lie in one tensor (a tensor is 32 CPR slots)
-      const bool is_q = j * 64 < 32 * PT::CPR;
+      constexpr int kPerTensor = 32 * PT::CPR / 64;
+      const bool is_q = j < kPerTensor;
+      const uint32_t dst = ring0 + (uint32_t)(is_q ? RG::q(slot) + j * 1024
+                                                   : RG::o(slot) + (j - kPerTensor) * 1024);
       const uint32_t voff = pair_index(p0 + cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
-      lds_dma16(sb + (uint32_t)(j * 1024), is_q ? (const void*)a.q : (const void*)a.d_out, voff);
+      lds_dma16(dst, is_q ? (const void*)a.q : (const void*)a.d_out, voff);
     }
     const uint32_t moff = pair_index(p0 + (uint32_t)(lane >> 1)) * 8u + 4u * (uint32_t)(lane & 1);
-    lds_dma4(sb + (uint32_t)(2 * RG::TB + wave_u * RG::META), a.meta, moff);
+    lds_dma4(ring0 + (uint32_t)RG::meta(slot, wave_u), a.meta, moff);
   };
 
   // 16-byte row reads: lane (jj, hh) reads pair row 16 pt + jj, logical chunk
@@ -394,11 +413,11 @@ void bwd_dkdv_kernel(BwdArgs a) {
   for (int kt = 0; kt < KT; ++kt) key_lane[kt] = kw0 + 16 * kt + jj;
   const int qoff = (int)(a.n_k - a.n_q);
 
-  auto compute = [&](int t, int slot) {
-    const uint32_t qb = ring0 + (uint32_t)(slot * RG::SLOT);
-    const uint32_t ob = qb + (uint32_t)RG::TB;
-    const float2* meta = reinterpret_cast<const float2*>(&ring[slot * RG::SLOT + 2 * RG::TB +
-                                                               wave * RG::META]);
+  auto compute = [&](int t, auto slot_tag) {
+    constexpr int S = decltype(slot_tag)::value;
+    const uint32_t qb = ring0 + (uint32_t)RG::q(S);
+    const uint32_t ob = ring0 + (uint32_t)RG::o(S);
+    const float2* meta = reinterpret_cast<const float2*>(&ring[RG::meta(S, 0) + wave * RG::META]);
     f32x4 s[2][KT], dp[2][KT];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt)
@@ -420,25 +439,34 @@ void bwd_dkdv_kernel(BwdArgs a) {
           dp[pt][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ao, vf[kt][ks], dp[pt][kt], 0, 0, 0);
         }
       }
-    // P and dS; lane (jj, hh) holds pairs 16 pt + 4 hh + r of key 16 kt + jj
+    // P and dS; lane (jj, hh) holds pairs 16 pt + 4 hh + r of key 16 kt + jj.
+    // Pairs are in ascending row order: when the tile's first row already
+    // sees the wave's last key and every pair is in the segment, no mask.
     bf16x8 pb[KT], sb[KT];
+    const uint32_t tp0 = (uint32_t)(t * 32);
+    const bool whole = tp0 + 31u < n_pairs_u &&
+                       __builtin_amdgcn_readfirstlane(qoff + rows_lds[tp0 / G]) >=
+                           kw0 + 16 * KT - 1;
+    auto p_ds = [&](bool masked) {
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+      for (int pt = 0; pt < 2; ++pt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int pr = 16 * pt + 4 * hh + r;
-        const uint32_t p = (uint32_t)(t * 32 + pr);
-        const float2 m = meta[pr];
-        const int pos = p < n_pairs_u ? qoff + rows_lds[p / G] : -1;
+        for (int r = 0; r < 4; ++r) {
+          const int pr = 16 * pt + 4 * hh + r;
+          const uint32_t p = tp0 + (uint32_t)pr;
+          const float2 m = meta[pr];
+          const int pos = masked ? (p < n_pairs_u ? qoff + rows_lds[p / G] : -1) : 0;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt) {
-          const float pv = key_lane[kt] <= pos
-                               ? fast_exp2(__builtin_fmaf(s[pt][kt][r], a.scale_log2, -m.x))
-                               : 0.0f;
-          pb[kt][4 * pt + r] = (__bf16)pv;
-          sb[kt][4 * pt + r] = (__bf16)(pv * (dp[pt][kt][r] - m.y));
+          for (int kt = 0; kt < KT; ++kt) {
+            const float e = fast_exp2(__builtin_fmaf(s[pt][kt][r], a.scale_log2, -m.x));
+            const float pv = !masked || key_lane[kt] <= pos ? e : 0.0f;
+            pb[kt][4 * pt + r] = (__bf16)pv;
+            sb[kt][4 * pt + r] = (__bf16)(pv * (dp[pt][kt][r] - m.y));
+          }
         }
-      }
+    };
+    if (whole) p_ds(false);
+    else p_ds(true);
     // dV^T += dO^T P, dK^T += Q^T dS: A rows d of d-tile dt, reduction over
     // pairs in the order 4 hh + e (e < 4), 16 + 4 hh + e - 4 (e >= 4)
 #pragma unroll
@@ -464,13 +492,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int j = 0; j + 1 < NS; ++j)
     if (j < n_tiles) issue(j, j);
-  for (int t = 0; t < n_tiles; ++t) {
+  auto step = [&](int t, auto slot_tag) {
+    constexpr int S = decltype(slot_tag)::value;
     const int after = min(NS - 2, n_tiles - 1 - t);
     if (after >= 2) wait_vm_barrier<2 * KL>();
     else if (after == 1) wait_vm_barrier<KL>();
     else wait_vm_barrier<0>();
-    if (t + NS - 1 < n_tiles) issue(t + NS - 1, (t + NS - 1) % NS);
-    compute(t, t % NS);
+    if (t + NS - 1 < n_tiles) issue(t + NS - 1, (S + NS - 1) % NS);
+    compute(t, slot_tag);
+  };
+  static_assert(NS == 4, "the tile loop is unrolled over four slots");
+  for (int t = 0; t < n_tiles; t += NS) {
+    step(t, StageTag<0>());
+    if (t + 1 < n_tiles) step(t + 1, StageTag<1>());
+    if (t + 2 < n_tiles) step(t + 2, StageTag<2>());
+    if (t + 3 < n_tiles) step(t + 3, StageTag<3>());
   }
 
   // ---- accumulate: lane (jj, hh) holds key 16 kt + jj, d = 16 dt + 4 hh + r
