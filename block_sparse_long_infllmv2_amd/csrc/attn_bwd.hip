@@ -381,8 +381,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
     cp_r[i] = (uint32_t)r;
     cp_c16[i] = (uint32_t)(16 * (pc ^ PT::f(r)));
   }
+  // With G >= 16 (and kPbase) a tile's 32 pairs lie in 32 / G rows: both
+  // row bases are read once per tile and each copy picks its own; pairs past
+  // the segment take the last row (finite data, masked by position).
   auto issue = [&](int t, int slot) {
     const uint32_t p0 = (uint32_t)t * 32u;
+    uint32_t pb[G >= 16 ? 32 / G : 1];
+    if constexpr (kPbase && G >= 16) {
+      const int row0 = (int)(p0 / G), last = max(n_rows - 1, 0);
+#pragma unroll
+      for (int k = 0; k < 32 / G; ++k) pb[k] = pbase_lds[min(row0 + k, last)];
+    }
+    auto index_of = [&](uint32_t r) -> uint32_t {   // pair p0 + r
+      if constexpr (kPbase && G >= 16) return pb[r / G] + r % G;
+      else return pair_index(p0 + r);
+    };
 #pragma unroll
     for (int i = 0; i < RG::PER_WAVE; ++i) {
       const int j = wave_u * RG::PER_WAVE + i;              // copy index in the tile
@@ -391,10 +404,10 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const bool is_q = j < kPerTensor;
       const uint32_t dst = ring0 + (uint32_t)(is_q ? RG::q(slot) + j * 1024
                                                    : RG::o(slot) + (j - kPerTensor) * 1024);
-      const uint32_t voff = pair_index(p0 + cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
+      const uint32_t voff = index_of(cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
       lds_dma16(dst, is_q ? (const void*)a.q : (const void*)a.d_out, voff);
     }
-    const uint32_t moff = pair_index(p0 + (uint32_t)(lane >> 1)) * 8u + 4u * (uint32_t)(lane & 1);
+    const uint32_t moff = index_of((uint32_t)(lane >> 1)) * 8u + 4u * (uint32_t)(lane & 1);
     lds_dma4(ring0 + (uint32_t)RG::meta(slot, wave_u), a.meta, moff);
   };
 
