@@ -22,8 +22,9 @@ Prints one JSON line.  Timing: each of the K timed iterations flushes the
 caches (a read-modify-write of 1 GiB, 4x the Infinity Cache) and then replays
 the whole step, captured once as a HIP graph, between two HIP events;
 ms_per_step is the median, with p10 / p90 / mean beside it.  The dominant
-call (the attention call) is timed the same way on its own after the step's
-earlier stages, and its mean duration gives the roofline fraction
+call (the attention call; for decode and tree verification the attention
+call that also makes the top-k selection) is timed the same way on its own
+after the step's earlier stages, and its mean duration gives the roofline fraction
 (algorithmic FLOP or bytes per launch over that time).  Other workloads of
 the metric (--also: ragged decode, 128K decode at batch 1, tree
 verification) are timed the same way and reported in the same line.  The
@@ -284,17 +285,17 @@ class Workload:
         elif self.kind == "decode":
             mark("start")
             pl.select(self.q, self.ck, self.seqlens)
-            mark("scores_topk")
+            mark("block_scores")
             if not skip_dominant:
                 pl.attend(self.q, self.k, self.v, self.seqlens)
-            mark("sparse_attn_decode")
+            mark("sparse_attn_decode_topk")
         else:
             mark("start")
             pl.select(self.q, self.ck)
-            mark("scores_topk")
+            mark("block_scores")
             if not skip_dominant:
                 pl.attend(self.q, self.k, self.v, self.kd, self.vd, self.mask)
-            mark("tree_verify")
+            mark("tree_verify_topk")
 
     def backward(self):
         if self.kind == "prefill_bwd_whole":
@@ -361,8 +362,10 @@ class Workload:
         d = c.q.shape[2]
         h_q = c.q.shape[1]
         if self.kind == "decode":
-            # the attention call's own bytes: K and V of the kept keys, Q and O
-            # (the compressed keys are read by the scoring stage, not here)
+            # the selecting attention call's own bytes: the block scores of
+            # each sparse row's eligible blocks and its selection written, K
+            # and V of the kept keys, Q and O (the compressed keys are read by
+            # the scoring stage, not here)
             total = 0.0
             for L in np.tile(np.asarray(c.seqlens), self.rep):
                 L = int(L)
@@ -371,8 +374,9 @@ class Workload:
                     kv = h_kv * L * d * 2 * 2
                 else:
                     kv = h_kv * _visible_selected_keys(L - 1, p, p.topk) * d * 2 * 2
+                    kv += h_kv * ((L - 1) // p.block_size + 1 + p.topk) * 4
                 total += kv + h_q * d * 2 * 2
-            return {"dominant": "sparse_attn_decode", "bound": "hbm", "bytes": total,
+            return {"dominant": "sparse_attn_decode_topk", "bound": "hbm", "bytes": total,
                     "src": "attn_bf16.hip"}
         # tree: union of kept blocks per KV head + drafts + Q/O + masks
         h_kv, n_ctx, _ = c.k.shape
@@ -381,7 +385,10 @@ class Workload:
         T = c.q.shape[0]
         total = (union * p.block_size * d * 2 * 2 + T * h_q * d * 2 * 2 +
                  2 * h_kv * T * d * 2 + T * 8)
-        return {"dominant": "tree_verify", "bound": "hbm", "bytes": float(total),
+        if not self.plan.dense:
+            # block scores read and selection written by the selecting call
+            total += T * h_kv * ((n_ctx - 1) // p.block_size + 1 + p.topk) * 4
+        return {"dominant": "tree_verify_topk", "bound": "hbm", "bytes": float(total),
                 "union_blocks": int(union), "src": "attn_bf16.hip"}
 
 

@@ -68,8 +68,14 @@ def _load(path=None):
         "infllmv2_sparse_attn_decode_noalloc": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64,
                                                                P, i32, i32, i32, i32, P, P, P,
                                                                PP, P]),
+        "infllmv2_sparse_attn_decode_topk": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, P,
+                                                            i32, i32, i32, i32, P, i64, P, P,
+                                                            P, P, sz, PP, P]),
         "infllmv2_tree_verify": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P,
                                                 i32, i32, i32, P, P, P, P, sz, PP, P]),
+        "infllmv2_tree_verify_topk": (ctypes.c_int, [ctypes.c_int, P, i32, P, P, i64, i64, P, P,
+                                                     P, i32, i32, i32, P, i64, P, P, P, P, sz,
+                                                     PP, P]),
         "infllmv2_sparse_attn_prefill_backward": (ctypes.c_int, [ctypes.c_int, P, i32, P, P,
                                                                  i64, i64, i32, i32, i32, P,
                                                                  P, P, P, P, P, P, P, sz, PP,
@@ -246,6 +252,35 @@ def infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, max_seqlen, block_
            "infllmv2_sparse_attn_decode")
 
 
+def infllmv2_sparse_attn_decode_topk(q, k_cache, v_cache, seqlens, max_seqlen, scores,
+                                     block_idx, out, lse, ws, params):
+    """infllmv2_select_topk (row b = sequence b, at its last position) and
+    infllmv2_sparse_attn_decode in one call: scores [batch][h_kv][nb_cap]
+    float32 in, the selection out in block_idx [batch][h_kv][topk]."""
+    batch, h_q, d = q.shape
+    _, h_kv, cap, _ = k_cache.shape
+    p = to_params(params)
+    _need(k_cache, "k_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (batch, h_kv, cap, d), q.dtype)
+    _need(seqlens, "seqlens", (batch,), torch.int32)
+    _need(out, "out", (batch, h_q, d), q.dtype)
+    _need(lse, "lse", (batch, h_q), torch.float32, optional=True)
+    nb_cap = 0
+    if scores is not None:
+        nb_cap = scores.shape[2]
+        _need(scores, "scores", (batch, h_kv, nb_cap), torch.float32)
+    _need(block_idx, "block_idx", (batch, h_kv, p.topk), torch.int32, optional=True)
+    _need(ws, "ws", (ws.numel(),), torch.uint8)
+    _check(LIB.infllmv2_sparse_attn_decode_topk(_dt(q), _ptr(q), batch, _ptr(k_cache),
+                                                _ptr(v_cache), cap, _i32(seqlens, "seqlens"),
+                                                int(max_seqlen), h_q, h_kv, d, _ptr(scores),
+                                                nb_cap, _i32(block_idx, "block_idx"),
+                                                _ptr(out), _ptr(lse), _ptr(ws),
+                                                ws.numel() * ws.element_size(),
+                                                ctypes.byref(p), _stream()),
+           "infllmv2_sparse_attn_decode_topk")
+
+
 def infllmv2_sparse_attn_decode_noalloc(q, k_cache, v_cache, seqlens, max_seqlen, block_idx,
                                         out, lse, params):
     """infllmv2_sparse_attn_decode with the library's fixed scratch array in
@@ -291,6 +326,38 @@ def infllmv2_tree_verify(q, k_cache, v_cache, n_ctx, k_draft, v_draft, tree_mask
                                     _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                     ctypes.byref(p), _stream()),
            "infllmv2_tree_verify")
+
+
+def infllmv2_tree_verify_topk(q, k_cache, v_cache, n_ctx, k_draft, v_draft, tree_mask, scores,
+                              block_idx, out, lse, ws, params):
+    """infllmv2_select_topk (every draft at position n_ctx - 1) and
+    infllmv2_tree_verify in one call: scores [T][h_kv][nb_cap] float32 in,
+    the selection out in block_idx [T][h_kv][topk]."""
+    T, h_q, d = q.shape
+    h_kv, cap, _ = k_cache.shape
+    p = to_params(params)
+    if tree_mask.dtype not in (torch.int64, torch.uint64):
+        raise TypeError("tree_mask must be a 64-bit integer tensor")
+    _need(tree_mask, "tree_mask", (T,))
+    _need(k_cache, "k_cache", (h_kv, cap, d), q.dtype)
+    _need(v_cache, "v_cache", (h_kv, cap, d), q.dtype)
+    _need(k_draft, "k_draft", (h_kv, T, d), q.dtype)
+    _need(v_draft, "v_draft", (h_kv, T, d), q.dtype)
+    _need(out, "out", (T, h_q, d), q.dtype)
+    _need(lse, "lse", (T, h_q), torch.float32, optional=True)
+    nb_cap = 0
+    if scores is not None:
+        nb_cap = scores.shape[2]
+        _need(scores, "scores", (T, h_kv, nb_cap), torch.float32)
+    _need(block_idx, "block_idx", (T, h_kv, p.topk), torch.int32, optional=True)
+    _need(ws, "ws", (ws.numel(),), torch.uint8)
+    _check(LIB.infllmv2_tree_verify_topk(_dt(q), _ptr(q), T, _ptr(k_cache), _ptr(v_cache), cap,
+                                         int(n_ctx), _ptr(k_draft), _ptr(v_draft),
+                                         _ptr(tree_mask), h_q, h_kv, d, _ptr(scores), nb_cap,
+                                         _i32(block_idx, "block_idx"), _ptr(out), _ptr(lse),
+                                         _ptr(ws), ws.numel() * ws.element_size(),
+                                         ctypes.byref(p), _stream()),
+           "infllmv2_tree_verify_topk")
 
 
 def infllmv2_sparse_attn_prefill_backward(q, k_cache, v_cache, n_k, block_idx, out, lse, d_out,

@@ -34,6 +34,7 @@
 #include <mutex>
 
 #include "lds_tiles.h"
+#include "topk_wave.h"
 
 namespace infllmv2 {
 
@@ -1547,11 +1548,19 @@ __device__ __forceinline__ void wait_vm() {
 // (row = draft, all at context position n_ctx - 1, each with its own kept
 // blocks); every row has one more unit after its context units: the chunk of
 // draft tokens, of which it sees those set in its ancestor mask (and itself).
-template <int D, bool TREE>
+//
+// KPL > 0: the wave selects its row's kept blocks itself from the block
+// scores (the top-k selection of topk_wave.h over rows of up to 64 * KPL
+// blocks, the same result as the top-k kernel), every split redundantly, and
+// split 0 writes the selection out; the wave's staging LDS holds the
+// selection's survivors before the copies start.
+template <int D, bool TREE, int KPL = 0>
 __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   constexpr int NS = 2;
   constexpr int TILE = Swz16<D>::TILE;
   __shared__ __attribute__((aligned(16))) uint16_t stage[NS * TILE];   // K0 K1 V0 V1
+  static_assert(KPL == 0 || (kWaveSurvivors + 64) * 8 + kMaxTopk * 4 <= NS * TILE * 2,
+                "the selection's staging fits the copy staging");
   const int lane = threadIdx.x;
   const int split = blockIdx.x, g = blockIdx.y, seq = blockIdx.z;    // seq: the row
   // The sequence length, the whole kept-block list (topk <= 128: two entries
@@ -1559,8 +1568,9 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   // one memory round trip instead of a chain of dependent ones.
   int Lr = (int)a.n_k;
   if constexpr (!TREE) Lr = a.seqlens[seq];
-  const int32_t* lst =
-      a.block_idx ? a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk : nullptr;
+  const int32_t* lst = KPL == 0 && a.block_idx
+                           ? a.block_idx + ((int64_t)seq * a.h_kv + g) * a.topk
+                           : nullptr;
   int32_t lst0 = -1, lst1 = -1;                 // entries lane and 64 + lane
   if (lst) {
     if (lane < a.topk) lst0 = lst[lane];
@@ -1579,9 +1589,28 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
   }
   // lengths outside [1, max_seqlen] are clamped: wrong input, no fault
   const int L = TREE ? Lr : (Lr < 1 ? 1 : (Lr > (int)a.n_k ? (int)a.n_k : Lr));
-  const bool dense = L < a.dense_len || a.block_idx == nullptr;
+  const bool dense =
+      L < a.dense_len || (KPL > 0 ? a.scores == nullptr : a.block_idx == nullptr);
   const int n_b = (L + a.B - 1) / a.B;
   const int cpb = (a.B + kChunk - 1) / kChunk;
+  if constexpr (KPL > 0) {
+    int32_t* sel = reinterpret_cast<int32_t*>(stage) + 2 * (kWaveSurvivors + 64);
+    if (!dense) {
+      wave_select_row<KPL>(a.scores + ((int64_t)seq * a.h_kv + g) * a.nb_cap, a.nb_cap,
+                           (L - 1) / a.B, a.topk, a.init, a.local,
+                           reinterpret_cast<int2*>(stage), sel, lane);
+      __builtin_amdgcn_wave_barrier();
+      if (lane < a.topk) lst0 = sel[lane];
+      if (64 + lane < a.topk) lst1 = sel[64 + lane];
+    }
+    if (split == 0) {                 // dense rows: nothing selected
+      int32_t* so = a.sel_out + ((int64_t)seq * a.h_kv + g) * a.topk;
+      if (lane < a.topk) so[lane] = lst0;
+      if (64 + lane < a.topk) so[64 + lane] = lst1;
+    }
+    // the staging is free for the copies once the list has been read
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
   int n_entries = n_b;
   if (!dense) {
     // kept blocks = the leading valid entries of the list
@@ -1963,12 +1992,28 @@ int tree_tile_tokens(int G) {
   return 0;
 }
 
-template <int D>
-int dispatch_decode(int G, const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if (G == 16) {
-    hipLaunchKernelGGL((attn16_decode_kernel<D, false>), grid, dim3(64), 0, st, a);
-    return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+// 16-head groups: kpl 0 takes the kept-block lists, 16 / 32 / 64 selects in
+// the kernel from the block scores
+template <int D, bool TREE>
+int launch_decode16(int kpl, const AttnArgs& a, dim3 grid, hipStream_t st) {
+  switch (kpl) {
+    case 0: hipLaunchKernelGGL((attn16_decode_kernel<D, TREE, 0>), grid, dim3(64), 0, st, a);
+      break;
+    case 16: hipLaunchKernelGGL((attn16_decode_kernel<D, TREE, 16>), grid, dim3(64), 0, st, a);
+      break;
+    case 32: hipLaunchKernelGGL((attn16_decode_kernel<D, TREE, 32>), grid, dim3(64), 0, st, a);
+      break;
+    case 64: hipLaunchKernelGGL((attn16_decode_kernel<D, TREE, 64>), grid, dim3(64), 0, st, a);
+      break;
+    default: return INFLLMV2_ERR_UNSUPPORTED;
   }
+  return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+template <int D>
+int dispatch_decode(int G, const AttnArgs& a, dim3 grid, hipStream_t st, int kpl) {
+  if (G == 16) return launch_decode16<D, false>(kpl, a, grid, st);
+  if (kpl != 0) return INFLLMV2_ERR_UNSUPPORTED;
   switch (G) {
     case 1:  return launch_attn<D, 1, 4, kDecode>(a, grid, st);
     case 2:  return launch_attn<D, 2, 4, kDecode>(a, grid, st);
@@ -2086,6 +2131,86 @@ extern "C" int infllmv2_sparse_attn_prefill(int dtype, const void* q, int32_t n_
   return d == 128 ? dispatch_prefill<128>(G, a, grid, st) : dispatch_prefill<64>(G, a, grid, st);
 }
 
+namespace {
+
+// The selection a decode or tree call makes itself from block scores.
+struct SelectIn {
+  const float* scores;        // [rows][h_kv][nb_cap]
+  int64_t nb_cap;
+  int32_t* out;               // [rows][h_kv][topk]
+};
+
+// Rows of up to 64 * KPL blocks select inside the 16-head kernels; 0: longer.
+int select_kpl(int64_t n_blocks) {
+  return n_blocks <= 64 * 16 ? 16 : n_blocks <= 64 * 32 ? 32 : n_blocks <= 64 * 64 ? 64 : 0;
+}
+
+// Decode with kept-block lists (sel NULL) or with its own selection from
+// block scores (sel set): inside the 16-head kernel when the rows fit it,
+// else by the top-k kernel into sel->out first.
+int decode_call(int dtype, const void* q, int32_t batch, const void* k, const void* v,
+                int64_t cap, const int32_t* seqlens, int32_t max_seqlen, int32_t h_q,
+                int32_t h_kv, int32_t d, const int32_t* block_idx, const SelectIn* sel,
+                void* out, float* lse, void* ws, size_t ws_bytes, const Resolved& r,
+                hipStream_t st) {
+  if (!q || !k || !v || !out || !seqlens) return INFLLMV2_ERR_INVALID_ARG;
+  if (batch < 0 || max_seqlen <= 0 || cap < max_seqlen) return INFLLMV2_ERR_INVALID_ARG;
+  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
+  const bool sparse = max_seqlen >= r.dense_len;
+  const int64_t n_blocks = ceil_div((int64_t)max_seqlen, (int64_t)r.B);
+  const bool lists_ok =
+      sel ? sel->scores && sel->out && sel->nb_cap >= n_blocks : block_idx != nullptr;
+  if (sparse && !lists_ok) return INFLLMV2_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return INFLLMV2_ERR_INVALID_ARG;
+  if (batch == 0) return INFLLMV2_OK;
+  if (sel && (int64_t)batch * h_kv >= (1ll << 31)) return INFLLMV2_ERR_UNSUPPORTED;
+  const int64_t n_split = decode_splits(batch, h_kv, max_seqlen, r);
+  if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
+  const size_t need = decode_workspace_bytes(batch, h_q, h_kv, d, max_seqlen, r);
+  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
+  const int G = h_q / h_kv;
+  if (dtype != INFLLMV2_F32 && !group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
+  const int kpl = sel && sparse && dtype != INFLLMV2_F32 && G == 16 ? select_kpl(n_blocks) : 0;
+  if (sel && sparse && kpl == 0) {
+    // the top-k kernel writes the lists the attention then reads
+    TopkArgs t = {};
+    t.scores = sel->scores; t.row_is_seq = 1; t.seqlens = seqlens; t.block_idx = sel->out;
+    t.nb_cap = sel->nb_cap; t.h_kv = h_kv; t.B = r.B; t.topk = r.topk; t.init = r.init;
+    t.local = r.local; t.dense_len = r.dense_len; t.batch = batch;
+    INFLLMV2_TRY(launch_select_topk(t, batch, st));
+    block_idx = sel->out;
+  }
+  AttnArgs a = {};
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.block_idx = kpl ? nullptr : (sparse ? block_idx : nullptr); a.seqlens = seqlens;
+  a.out = (uint16_t*)out; a.lse = lse; a.ws = (float*)ws;
+  a.cap = cap; a.n_k = max_seqlen; a.n_rows = batch; a.h_q = h_q; a.h_kv = h_kv;
+  a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
+  a.n_split = (int)n_split;
+  if (kpl) {
+    a.scores = sel->scores; a.nb_cap = sel->nb_cap; a.sel_out = sel->out;
+    a.init = r.init; a.local = r.local;
+  }
+#ifdef INFLLMV2_DEBUG
+  if (sparse && !kpl)
+    INFLLMV2_TRY(debug_check_rows(block_idx, batch, h_kv, r, max_seqlen, 0, seqlens, 1, st));
+#endif
+  if (dtype == INFLLMV2_F32) return decode_f32(a, d, st);
+  dim3 grid((unsigned)n_split, h_kv, batch);
+  INFLLMV2_TRY(d == 128 ? dispatch_decode<128>(G, a, grid, st, kpl)
+                        : dispatch_decode<64>(G, a, grid, st, kpl));
+  if (d == 128)
+    hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(batch * h_q), dim3(64), 0, st,
+                       a.ws, a.n_split, (uint16_t*)out, lse);
+  else
+    hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(batch * h_q), dim3(64), 0, st,
+                       a.ws, a.n_split, (uint16_t*)out, lse);
+  return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+}  // namespace
+
 extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t batch,
                                            const void* k, const void* v, int64_t cap,
                                            const int32_t* seqlens, int32_t max_seqlen,
@@ -2096,42 +2221,24 @@ extern "C" int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t bat
   INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
   Resolved r;
   INFLLMV2_TRY(check_params(p, d, &r));
-  if (!q || !k || !v || !out || !seqlens) return INFLLMV2_ERR_INVALID_ARG;
-  if (batch < 0 || max_seqlen <= 0 || cap < max_seqlen) return INFLLMV2_ERR_INVALID_ARG;
-  if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
-  if (max_seqlen >= r.dense_len && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return INFLLMV2_ERR_INVALID_ARG;
-  if (batch == 0) return INFLLMV2_OK;
-  const int64_t n_split = decode_splits(batch, h_kv, max_seqlen, r);
-  if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
-  const size_t need = decode_workspace_bytes(batch, h_q, h_kv, d, max_seqlen, r);
-  if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
-  AttnArgs a = {};
-  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.block_idx = block_idx; a.seqlens = seqlens;
-  a.out = (uint16_t*)out; a.lse = lse; a.ws = (float*)ws;
-  a.cap = cap; a.n_k = max_seqlen; a.n_rows = batch; a.h_q = h_q; a.h_kv = h_kv;
-  a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
-  a.n_split = (int)n_split;
-  hipStream_t st = (hipStream_t)stream;
-#ifdef INFLLMV2_DEBUG
-  if (max_seqlen >= r.dense_len)
-    INFLLMV2_TRY(debug_check_rows(block_idx, batch, h_kv, r, max_seqlen, 0, seqlens, 1, st));
-#endif
-  if (dtype == INFLLMV2_F32) return decode_f32(a, d, st);
-  const int G = h_q / h_kv;
-  if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
-  dim3 grid((unsigned)n_split, h_kv, batch);
-  INFLLMV2_TRY(d == 128 ? dispatch_decode<128>(G, a, grid, st)
-                        : dispatch_decode<64>(G, a, grid, st));
-  if (d == 128)
-    hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(batch * h_q), dim3(64), 0, st,
-                       a.ws, a.n_split, (uint16_t*)out, lse);
-  else
-    hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(batch * h_q), dim3(64), 0, st,
-                       a.ws, a.n_split, (uint16_t*)out, lse);
-  return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+  return decode_call(dtype, q, batch, k, v, cap, seqlens, max_seqlen, h_q, h_kv, d, block_idx,
+                     nullptr, out, lse, ws, ws_bytes, r, (hipStream_t)stream);
+}
+
+extern "C" int infllmv2_sparse_attn_decode_topk(int dtype, const void* q, int32_t batch,
+                                                const void* k, const void* v, int64_t cap,
+                                                const int32_t* seqlens, int32_t max_seqlen,
+                                                int32_t h_q, int32_t h_kv, int32_t d,
+                                                const float* scores, int64_t nb_cap,
+                                                int32_t* block_idx, void* out, float* lse,
+                                                void* ws, size_t ws_bytes,
+                                                const infllmv2_params* p, void* stream) {
+  INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
+  Resolved r;
+  INFLLMV2_TRY(check_params(p, d, &r));
+  const SelectIn sel = {scores, nb_cap, block_idx};
+  return decode_call(dtype, q, batch, k, v, cap, seqlens, max_seqlen, h_q, h_kv, d, nullptr,
+                     &sel, out, lse, ws, ws_bytes, r, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -2201,22 +2308,23 @@ size_t decode_workspace_bytes(int batch, int h_q, int h_kv, int d, int64_t max_s
 }
 }  // namespace infllmv2
 
-extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* k,
-                                    const void* v, int64_t cap, int64_t n_ctx,
-                                    const void* k_draft, const void* v_draft,
-                                    const uint64_t* tree_mask, int32_t h_q, int32_t h_kv,
-                                    int32_t d, const int32_t* block_idx, void* out, float* lse,
-                                    void* ws, size_t ws_bytes, const infllmv2_params* p,
-                                    void* stream) {
-  INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
-  Resolved r;
-  INFLLMV2_TRY(check_params(p, d, &r));
+namespace {
+
+// Tree verification with kept-block lists (sel NULL) or with its own
+// selection from block scores (as decode_call).
+int tree_call(int dtype, const void* q, int32_t n_draft, const void* k, const void* v,
+              int64_t cap, int64_t n_ctx, const void* k_draft, const void* v_draft,
+              const uint64_t* tree_mask, int32_t h_q, int32_t h_kv, int32_t d,
+              const int32_t* block_idx, const SelectIn* sel, void* out, float* lse, void* ws,
+              size_t ws_bytes, const Resolved& r, hipStream_t st) {
   if (!q || !k || !v || !k_draft || !v_draft || !tree_mask || !out)
     return INFLLMV2_ERR_INVALID_ARG;
   if (n_draft < 0 || n_draft > 64 || n_ctx <= 0 || cap < n_ctx) return INFLLMV2_ERR_INVALID_ARG;
   if (cap > INT32_MAX) return INFLLMV2_ERR_UNSUPPORTED;
   const bool dense = n_ctx < r.dense_len;
-  if (!dense && !block_idx) return INFLLMV2_ERR_INVALID_ARG;
+  const int64_t n_b = ceil_div(n_ctx, r.B);
+  const bool lists_ok = sel ? sel->scores && sel->out && sel->nb_cap >= n_b : block_idx != nullptr;
+  if (!dense && !lists_ok) return INFLLMV2_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !aligned16(k_draft) || !aligned16(v_draft))
     return INFLLMV2_ERR_INVALID_ARG;
@@ -2225,10 +2333,23 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   if (n_split > kMaxCombineSplits) return INFLLMV2_ERR_UNSUPPORTED;
   const size_t need = tree_workspace_bytes(n_draft, h_q, h_kv, d, n_ctx, r);
   if (!ws || ws_bytes < need || ((uintptr_t)ws & 255u)) return INFLLMV2_ERR_WORKSPACE;
+  const int G = h_q / h_kv;
+  if (dtype != INFLLMV2_F32 && !group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
+  const int kpl = sel && !dense && dtype != INFLLMV2_F32 && G == 16 ? select_kpl(n_b) : 0;
+  if (sel && !dense && kpl == 0) {
+    // the top-k kernel writes the lists the attention then reads: every
+    // draft is a row at the context's last position
+    TopkArgs t = {};
+    t.scores = sel->scores; t.fixed_len = n_ctx; t.block_idx = sel->out;
+    t.nb_cap = sel->nb_cap; t.h_kv = h_kv; t.B = r.B; t.topk = r.topk; t.init = r.init;
+    t.local = r.local; t.dense_len = r.dense_len; t.batch = 1;
+    INFLLMV2_TRY(launch_select_topk(t, n_draft, st));
+    block_idx = sel->out;
+  }
   const int64_t ucap = tree_union_cap(n_draft, n_ctx, r);
   AttnArgs a = {};
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.block_idx = dense ? nullptr : block_idx;
+  a.block_idx = dense || kpl ? nullptr : block_idx;
   a.k_draft = (const uint16_t*)k_draft; a.v_draft = (const uint16_t*)v_draft;
   a.tree_mask = tree_mask;
   a.out = (uint16_t*)out; a.lse = lse; a.ws = (float*)ws;
@@ -2241,21 +2362,21 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   a.cap = cap; a.n_k = n_ctx; a.n_rows = n_draft; a.h_q = h_q; a.h_kv = h_kv;
   a.topk = r.topk; a.B = r.B; a.dense_len = r.dense_len; a.scale_log2 = r.scale * kLog2e;
   a.n_split = (int)n_split;
-  hipStream_t st = (hipStream_t)stream;
+  if (kpl) {
+    a.scores = sel->scores; a.nb_cap = sel->nb_cap; a.sel_out = sel->out;
+    a.init = r.init; a.local = r.local;
+  }
 #ifdef INFLLMV2_DEBUG
   INFLLMV2_TRY(debug_check_masks(tree_mask, n_draft, st));
-  if (!dense)
+  if (!dense && !kpl)
     INFLLMV2_TRY(debug_check_rows(block_idx, n_draft, h_kv, r, n_ctx, 0, nullptr, 2, st));
 #endif
   if (dtype == INFLLMV2_F32) return tree_f32(a, d, st);
-  const int G = h_q / h_kv;
-  if (!group_ok_for_mfma(G)) return INFLLMV2_ERR_UNSUPPORTED;
   if (G == 16) {
     // 16-head groups: each draft is a row of the decode kernel over the
     // shared context (its own kept blocks, then the draft chunk); splits as
     // for decode (one resident round of waves), within the workspace's count
     const int64_t cpb = ceil_div(r.B, kChunk);
-    const int64_t n_b = ceil_div(n_ctx, r.B);
     const int64_t row_units = (dense ? n_b : r.topk) * cpb + 1;
     int64_t ns = ceil_div((int64_t)kDecodeWaves, (int64_t)n_draft * h_kv);
     ns = std::min<int64_t>(ns, n_split);
@@ -2263,11 +2384,8 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
     if (ns > n_split) return INFLLMV2_ERR_UNSUPPORTED;     // cannot happen: see tree_splits
     a.n_split = (int)ns;
     dim3 grid16((unsigned)ns, h_kv, (unsigned)n_draft);
-    if (d == 128)
-      hipLaunchKernelGGL((attn16_decode_kernel<128, true>), grid16, dim3(64), 0, st, a);
-    else
-      hipLaunchKernelGGL((attn16_decode_kernel<64, true>), grid16, dim3(64), 0, st, a);
-    if (hipGetLastError() != hipSuccess) return INFLLMV2_ERR_HIP;
+    INFLLMV2_TRY((d == 128 ? launch_decode16<128, true>(kpl, a, grid16, st)
+                           : launch_decode16<64, true>(kpl, a, grid16, st)));
     if (d == 128)
       hipLaunchKernelGGL((combine_kernel<128, uint16_t>), dim3(n_draft * h_q), dim3(64), 0, st,
                          a.ws, a.n_split, (uint16_t*)out, lse);
@@ -2278,7 +2396,6 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
   }
   const int TT = tree_tile_tokens(G);
   if (!dense) {
-    const int64_t n_b = ceil_div(n_ctx, r.B);
     if (n_b <= kUnionBitmapBlocks)
       hipLaunchKernelGGL(tree_union_bitmap_kernel, dim3(h_kv), dim3(kPlanThreads), 0, st,
                          block_idx, n_draft, h_kv, r.topk, (int)n_b, (int32_t*)a.union_blk,
@@ -2298,4 +2415,37 @@ extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, c
     hipLaunchKernelGGL((combine_kernel<64, uint16_t>), dim3(n_draft * h_q), dim3(64), 0, st,
                        a.ws, a.n_split, (uint16_t*)out, lse);
   return hipGetLastError() == hipSuccess ? INFLLMV2_OK : INFLLMV2_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* k,
+                                    const void* v, int64_t cap, int64_t n_ctx,
+                                    const void* k_draft, const void* v_draft,
+                                    const uint64_t* tree_mask, int32_t h_q, int32_t h_kv,
+                                    int32_t d, const int32_t* block_idx, void* out, float* lse,
+                                    void* ws, size_t ws_bytes, const infllmv2_params* p,
+                                    void* stream) {
+  INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
+  Resolved r;
+  INFLLMV2_TRY(check_params(p, d, &r));
+  return tree_call(dtype, q, n_draft, k, v, cap, n_ctx, k_draft, v_draft, tree_mask, h_q, h_kv,
+                   d, block_idx, nullptr, out, lse, ws, ws_bytes, r, (hipStream_t)stream);
+}
+
+extern "C" int infllmv2_tree_verify_topk(int dtype, const void* q, int32_t n_draft,
+                                         const void* k, const void* v, int64_t cap,
+                                         int64_t n_ctx, const void* k_draft,
+                                         const void* v_draft, const uint64_t* tree_mask,
+                                         int32_t h_q, int32_t h_kv, int32_t d,
+                                         const float* scores, int64_t nb_cap,
+                                         int32_t* block_idx, void* out, float* lse, void* ws,
+                                         size_t ws_bytes, const infllmv2_params* p,
+                                         void* stream) {
+  INFLLMV2_TRY(common_attn_checks(dtype, h_q, h_kv, d));
+  Resolved r;
+  INFLLMV2_TRY(check_params(p, d, &r));
+  const SelectIn sel = {scores, nb_cap, block_idx};
+  return tree_call(dtype, q, n_draft, k, v, cap, n_ctx, k_draft, v_draft, tree_mask, h_q, h_kv,
+                   d, nullptr, &sel, out, lse, ws, ws_bytes, r, (hipStream_t)stream);
 }

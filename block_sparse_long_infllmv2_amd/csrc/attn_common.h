@@ -36,6 +36,11 @@ struct AttnArgs {
                               // many of a tile's tokens go through the shared ring,
                               // the others through each token's own pass (0: all ring)
   float scale_log2;           // softmax scale * log2(e)
+  // decode / tree, 16-head groups, selection inside the attention kernel:
+  const float* scores;        // [rows][h_kv][nb_cap] block scores
+  int32_t* sel_out;           // [rows][h_kv][topk]: the selection, written by split 0
+  int64_t nb_cap;
+  int init, local;            // forced initial / local blocks
 };
 
 

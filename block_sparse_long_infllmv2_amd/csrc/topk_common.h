@@ -14,13 +14,17 @@ constexpr int kTopkThreads = 256;
 
 struct TopkArgs {
   const float* scores;
-  const int32_t* row_seq;
+  const int32_t* row_seq;     // NULL: row r is sequence r if row_is_seq, else 0
   const int32_t* row_pos;
-  const int32_t* seqlens;
+  const int32_t* seqlens;     // NULL: every sequence has length fixed_len
   int32_t* block_idx;
   int64_t nb_cap;
-  int h_kv, B, topk, init, local, dense_len, batch;
+  int64_t fixed_len;
+  int h_kv, B, topk, init, local, dense_len, batch, row_is_seq;
 };
+
+// Queues the selection of rows * h_kv rows (host side, topk.hip).
+int launch_select_topk(const TopkArgs& a, int rows, hipStream_t st);
 
 // Exclusive prefix sum over the 256 threads of the workgroup (thread order).
 __device__ __forceinline__ int block_exclusive_scan(int v, int* total, int* lds4) {

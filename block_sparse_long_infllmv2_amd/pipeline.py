@@ -189,15 +189,21 @@ class ChunkedPrefill:
 class DecodePlan:
     """One new query per sequence of a ragged batch (its K/V already cached).
 
-    Calls: block_scores -> select_topk -> sparse_attn_decode (split-KV +
-    combine).  Compressed keys are assumed current (append windows with
-    compress_keys as the caches grow).
+    Calls: block_scores -> sparse_attn_decode_topk (the top-k selection,
+    split-KV attention and combine; the selection runs inside the attention
+    kernel where it fits).  select_in_attend=False: block_scores ->
+    select_topk -> sparse_attn_decode instead (the same results).  Compressed
+    keys are assumed current (append windows with compress_keys as the caches
+    grow).
     """
 
-    def __init__(self, batch, max_seqlen, h_q, h_kv, d, dtype, params, device="cuda"):
+    def __init__(self, batch, max_seqlen, h_q, h_kv, d, dtype, params, device="cuda",
+                 select_in_attend=True):
         self.p = B.to_params(params)
         self.batch, self.max_seqlen = batch, max_seqlen
         self.h_q, self.h_kv, self.d, self.dtype = h_q, h_kv, d, dtype
+        self.select_in_attend = select_in_attend
+        self.dense = max_seqlen < self.p.dense_len
         dev = torch.device(device)
         self.nb = (max_seqlen + self.p.block_size - 1) // self.p.block_size
         self.row_seq = torch.arange(batch, dtype=torch.int32, device=dev)
@@ -209,16 +215,23 @@ class DecodePlan:
         self.lse = torch.empty((batch, h_q), dtype=torch.float32, device=dev)
 
     def select(self, q, ck_cache, seqlens):
-        if self.max_seqlen < self.p.dense_len:
+        """Block scores (and, unless the attention call selects, the top-k)."""
+        if self.dense:
             return
         B.infllmv2_block_scores(q, self.row_seq, None, ck_cache, seqlens, self.scores,
                                 self.max_seqlen - 1, self.p)
-        B.infllmv2_select_topk(self.scores, self.row_seq, None, seqlens, self.block_idx,
-                               self.p)
+        if not self.select_in_attend:
+            B.infllmv2_select_topk(self.scores, self.row_seq, None, seqlens, self.block_idx,
+                                   self.p)
 
     def attend(self, q, k_cache, v_cache, seqlens):
-        B.infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, self.max_seqlen,
-                                      self.block_idx, self.out, self.lse, self.ws, self.p)
+        if self.select_in_attend and not self.dense:
+            B.infllmv2_sparse_attn_decode_topk(q, k_cache, v_cache, seqlens, self.max_seqlen,
+                                               self.scores, self.block_idx, self.out, self.lse,
+                                               self.ws, self.p)
+        else:
+            B.infllmv2_sparse_attn_decode(q, k_cache, v_cache, seqlens, self.max_seqlen,
+                                          self.block_idx, self.out, self.lse, self.ws, self.p)
 
     def run(self, q, k_cache, v_cache, ck_cache, seqlens):
         self.select(q, ck_cache, seqlens)
@@ -230,13 +243,17 @@ class TreePlan:
     """n_draft tree-shaped draft tokens after an n_ctx-token context.
 
     Calls: block_scores (every draft at the context's last position) ->
-    select_topk -> tree_verify (union planner, split-KV, combine).
+    tree_verify_topk (top-k selection, union planner where used, split-KV,
+    combine).  select_in_attend=False: block_scores -> select_topk ->
+    tree_verify instead (the same results).
     """
 
-    def __init__(self, n_draft, n_ctx, h_q, h_kv, d, dtype, params, device="cuda"):
+    def __init__(self, n_draft, n_ctx, h_q, h_kv, d, dtype, params, device="cuda",
+                 select_in_attend=True):
         self.p = B.to_params(params)
         self.n_draft, self.n_ctx = n_draft, n_ctx
         self.h_q, self.h_kv, self.d, self.dtype = h_q, h_kv, d, dtype
+        self.select_in_attend = select_in_attend
         self.dense = n_ctx < self.p.dense_len
         dev = torch.device(device)
         self.nb = (n_ctx + self.p.block_size - 1) // self.p.block_size
@@ -252,16 +269,23 @@ class TreePlan:
         self.lse = torch.empty((n_draft, h_q), dtype=torch.float32, device=dev)
 
     def select(self, q, ck_cache):
+        """Block scores (and, unless the verification call selects, the top-k)."""
         if self.dense:
             return
         B.infllmv2_block_scores(q, None, self.row_pos, ck_cache.unsqueeze(0), self.seqlens,
                                 self.scores, self.n_ctx - 1, self.p)
-        B.infllmv2_select_topk(self.scores, None, self.row_pos, self.seqlens, self.block_idx,
-                               self.p)
+        if not self.select_in_attend:
+            B.infllmv2_select_topk(self.scores, None, self.row_pos, self.seqlens,
+                                   self.block_idx, self.p)
 
     def attend(self, q, k_cache, v_cache, k_draft, v_draft, tree_mask):
-        B.infllmv2_tree_verify(q, k_cache, v_cache, self.n_ctx, k_draft, v_draft, tree_mask,
-                               self.block_idx, self.out, self.lse, self.ws, self.p)
+        if self.select_in_attend and not self.dense:
+            B.infllmv2_tree_verify_topk(q, k_cache, v_cache, self.n_ctx, k_draft, v_draft,
+                                        tree_mask, self.scores, self.block_idx, self.out,
+                                        self.lse, self.ws, self.p)
+        else:
+            B.infllmv2_tree_verify(q, k_cache, v_cache, self.n_ctx, k_draft, v_draft, tree_mask,
+                                   self.block_idx, self.out, self.lse, self.ws, self.p)
 
     def run(self, q, k_cache, v_cache, ck_cache, k_draft, v_draft, tree_mask):
         self.select(q, ck_cache)

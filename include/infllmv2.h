@@ -219,6 +219,32 @@ int infllmv2_sparse_attn_decode(int dtype, const void* q, int32_t batch,
                                 const infllmv2_params* p, void* stream);
 
 /*
+ * Top-k selection and decode attention in one call (pomoai.com, section 4:
+ * fused kernels to cut launches on the decode path).  The result equals
+ * infllmv2_select_topk(scores, batch, row_seq = {0, 1, .., batch-1},
+ * row_pos = NULL, h_kv, nb_cap, seqlens, batch, block_idx) followed by
+ * infllmv2_sparse_attn_decode(..., block_idx, ...), bit for bit.  For bf16,
+ * 16 query heads per KV head and rows of at most 4096 blocks, each split of
+ * the decode kernel selects its row itself and the first split writes
+ * block_idx (one launch fewer); otherwise the two kernels run in turn.
+ *   scores   float32 [batch][h_kv][nb_cap] from infllmv2_block_scores,
+ *            nb_cap >= ceil(max_seqlen / B)
+ *   block_idx int32 [batch][h_kv][topk], output: the selection, -1 rows for
+ *            dense sequences
+ * Both may be NULL when max_seqlen < dense_len (every row dense; nothing is
+ * selected or written).  The other arguments, the workspace and the errors
+ * are those of infllmv2_sparse_attn_decode.
+ */
+int infllmv2_sparse_attn_decode_topk(int dtype, const void* q, int32_t batch,
+                                     const void* k, const void* v, int64_t cap,
+                                     const int32_t* seqlens, int32_t max_seqlen,
+                                     int32_t h_q, int32_t h_kv, int32_t d,
+                                     const float* scores, int64_t nb_cap,
+                                     int32_t* block_idx, void* out, float* lse,
+                                     void* ws, size_t ws_bytes,
+                                     const infllmv2_params* p, void* stream);
+
+/*
  * Tree speculative verification (pomoai.com, section 2: tree verification in
  * the attention kernel; xugj520.cn, section 1.1: uint64-packed mask for tree
  * speculative decoding).  n_draft draft tokens follow an n_ctx-token context.
@@ -241,6 +267,27 @@ int infllmv2_tree_verify(int dtype, const void* q, int32_t n_draft, const void* 
                          int32_t d, const int32_t* block_idx, void* out, float* lse,
                          void* ws, size_t ws_bytes, const infllmv2_params* p,
                          void* stream);
+
+/*
+ * Top-k selection and tree verification in one call (pomoai.com, sections 2
+ * and 4).  The result equals infllmv2_select_topk(scores, n_draft,
+ * row_seq = NULL, row_pos = {n_ctx-1, ..}, h_kv, nb_cap, {n_ctx}, 1,
+ * block_idx) followed by infllmv2_tree_verify(..., block_idx, ...), bit for
+ * bit.  For bf16, 16 query heads per KV head and contexts of at most 4096
+ * blocks, each split selects its draft's row itself and the first split
+ * writes block_idx; otherwise the two run in turn.
+ *   scores    float32 [n_draft][h_kv][nb_cap], nb_cap >= ceil(n_ctx / B)
+ *   block_idx int32 [n_draft][h_kv][topk], output
+ * Both may be NULL when n_ctx < dense_len.  The other arguments, the
+ * workspace and the errors are those of infllmv2_tree_verify.
+ */
+int infllmv2_tree_verify_topk(int dtype, const void* q, int32_t n_draft, const void* k,
+                              const void* v, int64_t cap, int64_t n_ctx,
+                              const void* k_draft, const void* v_draft,
+                              const uint64_t* tree_mask, int32_t h_q, int32_t h_kv,
+                              int32_t d, const float* scores, int64_t nb_cap,
+                              int32_t* block_idx, void* out, float* lse, void* ws,
+                              size_t ws_bytes, const infllmv2_params* p, void* stream);
 
 /*
  * infllmv2_sparse_attn_decode without a workspace argument, for callers that

@@ -48,6 +48,11 @@ def lib():
                                          ctypes.POINTER(ctypes.c_int), P]
     lib.infllmv2_tree_verify.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P, i32,
                                          i32, i32, P, P, P, P, sz, PP, P]
+    lib.infllmv2_sparse_attn_decode_topk.argtypes = [ctypes.c_int, P, i32, P, P, i64, P, i32,
+                                                     i32, i32, i32, P, i64, P, P, P, P, sz, PP,
+                                                     P]
+    lib.infllmv2_tree_verify_topk.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64, P, P, P,
+                                              i32, i32, i32, P, i64, P, P, P, P, sz, PP, P]
     lib.infllmv2_sparse_attn_prefill_backward.argtypes = [ctypes.c_int, P, i32, P, P, i64, i64,
                                                           i32, i32, i32, P, P, P, P, P, P, P,
                                                           P, sz, PP, P]
@@ -166,6 +171,37 @@ def test_attention_validation(lib):
               FAKE, None, FAKE, tneed - 256, params(lib), None) == WORKSPACE
     assert tv(1, FAKE, 16, FAKE, FAKE, 20000, 20000, FAKE, None, FAKE, 32, 2, 128, FAKE,
               FAKE, None, FAKE, tneed, params(lib), None) == INVALID  # no draft V
+
+
+def test_select_in_attend_validation(lib):
+    """The decode / tree calls that select from block scores check the scores
+    and the selection output on the host (sparse rows need both, and a score
+    row must cover every block of the longest sequence)."""
+    dec = lib.infllmv2_sparse_attn_decode_topk
+    need = lib.infllmv2_workspace_size(0, 2, 32, 2, 128, 20000, params(lib))
+    nb = (20000 + 63) // 64
+
+    def dcall(scores=FAKE, nb_cap=nb, idx=FAKE, ws_bytes=need, batch=2, h_q=32):
+        return dec(1, FAKE, batch, FAKE, FAKE, 20000, FAKE, 20000, h_q, 2, 128, scores, nb_cap,
+                   idx, FAKE, None, FAKE, ws_bytes, params(lib), None)
+    assert dcall(scores=None) == INVALID
+    assert dcall(idx=None) == INVALID
+    assert dcall(nb_cap=nb - 1) == INVALID
+    assert dcall(ws_bytes=need - 1) == WORKSPACE
+    assert dcall(h_q=6) == UNSUPPORTED          # group size 3 (bf16)
+    assert dcall(batch=0) == OK                 # nothing to do
+    tv = lib.infllmv2_tree_verify_topk
+    tneed = lib.infllmv2_workspace_size(1, 16, 32, 2, 128, 20000, params(lib))
+
+    def tcall(scores=FAKE, nb_cap=nb, idx=FAKE, ws_bytes=tneed, n_draft=16):
+        return tv(1, FAKE, n_draft, FAKE, FAKE, 20000, 20000, FAKE, FAKE, FAKE, 32, 2, 128,
+                  scores, nb_cap, idx, FAKE, None, FAKE, ws_bytes, params(lib), None)
+    assert tcall(scores=None) == INVALID
+    assert tcall(idx=None) == INVALID
+    assert tcall(nb_cap=nb - 1) == INVALID
+    assert tcall(ws_bytes=tneed - 256) == WORKSPACE
+    assert tcall(n_draft=65) == INVALID
+    assert tcall(n_draft=0) == OK
 
 
 def test_backward_validation(lib):
