@@ -76,9 +76,11 @@ struct BwdArgs {
 // (row, head) pairs per dK/dV work item: bounds a workgroup's work.  Each
 // item adds its partial dK/dV with float32 atomics, whose write traffic grows
 // with the item count; smaller items balance better.  Measured on the 128K
-// chunk (MI355X): dK/dV 2.49 / 2.17 / 2.40 / 2.55 ms at 2048 / 4096 / 8192 /
-// 16384 pairs.  Rows per item are capped so the row list stays at 8 KB of LDS.
-constexpr int kSegPairs = 4096;
+// chunk (MI355X), first kernel: dK/dV 2.49 / 2.17 / 2.40 / 2.55 ms at 2048 /
+// 4096 / 8192 / 16384 pairs; current kernel (rocprofv3 means, one box): 1.79 /
+// 1.69 / 1.71 / 1.76 ms at 4096 / 5120 / 6144 / 7168 pairs.  Rows per item
+// are capped so the row list stays at 8 KB of LDS.
+constexpr int kSegPairs = 5120;
 constexpr int kMaxSegRows = 2048;
 __host__ __device__ constexpr int seg_rows_for(int G) {
   return kSegPairs / G < kMaxSegRows ? (kSegPairs / G > 0 ? kSegPairs / G : 1) : kMaxSegRows;
