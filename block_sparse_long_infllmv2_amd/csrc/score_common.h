@@ -12,8 +12,11 @@ namespace infllmv2 {
 constexpr int kScoreThreads = 256;
 constexpr int kScoreMaxWindows = 1024;   // window scores held in LDS per chunk
 constexpr int kMfmaMinRows = 64;         // fewer rows: the streaming kernel
-constexpr int kScoreMinWgs = 512;        // streaming kernel: workgroups aimed for
-constexpr int kScoreMinBlocks = 4;       // ... but at least this many blocks each
+// streaming kernel: workgroups aimed for, but at least kScoreMinBlocks blocks
+// each.  Ragged batch of 8 up to 128K (flushed steps): 46.6 / 45.0 / 44.5 us at
+// 512 / 1024 / 2048; 128K batch 1, batch 32 and the 16-draft tree unchanged.
+constexpr int kScoreMinWgs = 2048;
+constexpr int kScoreMinBlocks = 4;
 
 struct ScoreArgs {
   const void* q;
