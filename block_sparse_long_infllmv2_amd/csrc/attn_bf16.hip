@@ -1897,12 +1897,16 @@ namespace {
 
 // Splits per (row, KV head): enough workgroups to cover the GPU for batched
 // decode and tree verification while keeping the float32 partials small.
-// Decode aims at one resident round of kDecodeWaves single-wave workgroups
-// (two per CU, as the 64 KB staging ring allows): a larger batch gets fewer
-// splits, so each wave streams more chunks through its ring and the combine
-// merges fewer partials.
+// Decode aims at kDecodeWaves single-wave workgroups in all (at most two per
+// CU, as the 64 KB staging ring allows): a larger batch gets fewer splits, so
+// each wave streams more chunks through its ring and the combine merges fewer
+// partials.  With the selection inside each wave, 256 beat 512 on a ragged
+// batch of 8 up to 128K (44.6 -> 42.4 us per step) and tied at batch 1 and
+// batch 32.  Tree verification keeps one round of kTreeWaves (16 drafts at
+// 128K: 51.2 us against 55.4 us at 256).
 constexpr int kMaxDecodeSplits = 32;
-constexpr int kDecodeWaves = 512;
+constexpr int kDecodeWaves = 256;
+constexpr int kTreeWaves = 512;
 constexpr int kMaxTreeSplits = 32;
 constexpr int kMaxCombineSplits = 64;      // lanes of the combine kernel
 
@@ -2378,7 +2382,7 @@ int tree_call(int dtype, const void* q, int32_t n_draft, const void* k, const vo
     // for decode (one resident round of waves), within the workspace's count
     const int64_t cpb = ceil_div(r.B, kChunk);
     const int64_t row_units = (dense ? n_b : r.topk) * cpb + 1;
-    int64_t ns = ceil_div((int64_t)kDecodeWaves, (int64_t)n_draft * h_kv);
+    int64_t ns = ceil_div((int64_t)kTreeWaves, (int64_t)n_draft * h_kv);
     ns = std::min<int64_t>(ns, n_split);
     ns = std::max<int64_t>(ns, ceil_div(row_units, (int64_t)(kSplitEntryCap - 1) * cpb));
     if (ns > n_split) return INFLLMV2_ERR_UNSUPPORTED;     // cannot happen: see tree_splits

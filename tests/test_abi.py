@@ -99,8 +99,9 @@ def test_defaults_status_version(lib):
 def test_workspace_sizes(lib):
     ws = lib.infllmv2_workspace_size
     dec = ws(0, 8, 32, 2, 128, 131072, params(lib))
-    # 8 rows x 32 heads x 32 splits x (128 + 2) floats
-    assert dec == 8 * 32 * 32 * 130 * 4
+    # 8 rows x 32 heads x 16 splits (256 waves over 16 (row, KV head) pairs)
+    # x (128 + 2) floats
+    assert dec == 8 * 32 * 16 * 130 * 4
     dec_short = ws(0, 1, 32, 2, 128, 640, params(lib))   # 10 blocks -> 10 splits
     assert dec_short == ((1 * 32 * 10 * 130 * 4 + 255) // 256) * 256
     tree = ws(1, 16, 32, 2, 128, 131072, params(lib))

@@ -403,7 +403,7 @@ def test_decode_blocks_not_multiple_of_64(B, PL, bs, topk):
 
 
 def test_decode_large_batch_fewer_splits(B, PL):
-    # 40 sequences x 2 KV heads: the split count falls to ceil(512 / 80) = 7
+    # 40 sequences x 2 KV heads: the split count falls to ceil(256 / 80) = 4
     _say("decode bf16 batch 40")
     p = Params(dense_len=2048, topk=16)
     lens = [int(x) for x in np.random.default_rng(13).integers(1, 9000, 40)]
