@@ -127,10 +127,17 @@ class ChunkedPrefill:
     are made once; all chunks share one score scratch buffer and write into
     one output.  The chunks share one selection buffer too, unless
     keep_selections is set (training): then every chunk keeps its own rows'
-    selections, which backward() needs."""
+    selections, which backward() needs.
+
+    overlap: each chunk's compress, scores and top-k run on a second stream
+    (default priority) while the previous chunk's attention runs on the
+    caller's stream; chunk i's attention waits for chunk i's selection only.
+    Selections then alternate between two buffers (unless kept), and the
+    selection of chunk i waits for the attention of chunk i - 2, the last
+    reader of the buffer it overwrites.  The results are the same."""
 
     def __init__(self, n, chunk, h_q, h_kv, d, dtype, params, device="cuda",
-                 keep_selections=False):
+                 keep_selections=False, overlap=False):
         self.p = B.to_params(params)
         self.n, self.chunk = n, chunk
         dev = torch.device(device)
@@ -141,29 +148,57 @@ class ChunkedPrefill:
         self.score_buf = torch.empty(chunk * h_kv * nb_max, dtype=torch.float32, device=dev)
         per_row = h_kv * self.p.topk
         self.keep_selections = keep_selections
-        self.idx_buf = torch.empty((n if keep_selections else chunk) * per_row,
-                                   dtype=torch.int32, device=dev)
+        self.overlap = overlap
+        n_sel = n if keep_selections else (2 if overlap else 1) * chunk
+        self.idx_buf = torch.empty(n_sel * per_row, dtype=torch.int32, device=dev)
+
+        def idx_view(i, q0):
+            if keep_selections:
+                return self.idx_buf[q0 * per_row:]
+            return self.idx_buf[(i % 2 if overlap else 0) * chunk * per_row:]
         self.plans = [PrefillPlan(q1 - q0, n_k, h_q, h_kv, d, dtype, params, device=dev,
                                   out=self.out[q0:q1], lse=self.lse[q0:q1],
-                                  score_buf=self.score_buf,
-                                  idx_buf=self.idx_buf[q0 * per_row:] if keep_selections
-                                  else self.idx_buf)
-                      for (q0, q1, n_k, _, _) in self.sched]
+                                  score_buf=self.score_buf, idx_buf=idx_view(i, q0))
+                      for i, (q0, q1, n_k, _, _) in enumerate(self.sched)]
+        self.side = torch.cuda.Stream(device=dev) if overlap else None
         self.bwd_ws = None
+
+    def _select(self, pl, qc, k_cache, ck_cache, m0, m1):
+        # every chunk appends the windows it completes (a dense chunk too:
+        # later sparse chunks score against all of them)
+        if m1 > m0:
+            pl.compress(k_cache, ck_cache, m_begin=m0)
+        if not pl.dense:
+            pl.select(qc, ck_cache)
 
     def run(self, q, k_cache, v_cache, ck_cache, skip_attention=False):
         """q [n][h_q][d]; K/V caches [h_kv][cap >= n][d]; ck_cache
         [h_kv][>= windows(n)][d] (filled here, window by window)."""
-        for (q0, q1, _, m0, m1), pl in zip(self.sched, self.plans):
+        if not self.overlap:
+            for (q0, q1, _, m0, m1), pl in zip(self.sched, self.plans):
+                qc = q[q0:q1]
+                self._select(pl, qc, k_cache, ck_cache, m0, m1)
+                if not skip_attention:
+                    pl.attend(qc, k_cache, v_cache)
+            return self.out
+        main, side = torch.cuda.current_stream(), self.side
+        side.wait_stream(main)                      # the inputs are ready
+        attended = []
+        for i, ((q0, q1, _, m0, m1), pl) in enumerate(zip(self.sched, self.plans)):
             qc = q[q0:q1]
-            # every chunk appends the windows it completes (a dense chunk too:
-            # later sparse chunks score against all of them)
-            if m1 > m0:
-                pl.compress(k_cache, ck_cache, m_begin=m0)
-            if not pl.dense:
-                pl.select(qc, ck_cache)
+            with torch.cuda.stream(side):
+                if i >= 2 and not self.keep_selections:
+                    side.wait_event(attended[i - 2])
+                self._select(pl, qc, k_cache, ck_cache, m0, m1)
+                selected = torch.cuda.Event()
+                selected.record(side)
+            main.wait_event(selected)
             if not skip_attention:
                 pl.attend(qc, k_cache, v_cache)
+            done = torch.cuda.Event()
+            done.record(main)
+            attended.append(done)
+        main.wait_stream(side)
         return self.out
 
     def attend_all(self, q, k_cache, v_cache):

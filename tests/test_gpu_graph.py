@@ -83,6 +83,23 @@ def test_graph_prefill_step(B, PL):
                   lambda: plan.run(q2, k, v, ck))
 
 
+def test_graph_chunked_prefill_overlap(B, PL):
+    """A whole prompt in 4 chunks with the overlapped schedule (two streams)
+    captured as one graph: every replay equals the eager run."""
+    _say("graph: chunked prefill, overlapped schedule")
+    p = Params(topk=8, dense_len=1024)
+    n, chunk = 2048, 512
+    c = make_prefill(33, n_k=n, n_q=n, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=3, alpha=1.5, beta=1.5)
+    q, k, v = up(c.q), up(c.k), up(c.v)
+    q2 = up(np.flip(c.q, axis=0).copy())
+    cp = PL.ChunkedPrefill(n, chunk, 32, 2, 128, torch.bfloat16, p, overlap=True)
+    ck = torch.zeros((2, _nwin(n, p), 128), dtype=torch.bfloat16, device="cuda")
+    _replay_check(lambda: cp.run(q, k, v, ck),
+                  lambda: [cp.out, cp.lse],
+                  lambda: cp.run(q2, k, v, ck))
+
+
 def test_graph_decode_step(B, PL):
     _say("graph: decode step")
     p = Params(dense_len=2048, topk=16)
