@@ -149,3 +149,43 @@ def test_tree_select_in_attend_matches_two_calls(B, PL, n_ctx, T, h_q, h_kv, d, 
     _same(one.block_idx, two.block_idx, "selection")
     _same(one.out, two.out, "out")
     _same(one.lse, two.lse, "lse")
+
+
+def test_select_in_attend_dense_calls_need_no_scores(B, PL):
+    """Below dense_len nothing is selected: the selecting calls accept NULL
+    scores and selection and give the list-taking calls' dense results."""
+    _say("select-in-attend: dense decode and tree without scores")
+    p = Params(dense_len=8192, topk=16)
+    g = torch.Generator(device="cuda").manual_seed(77)
+    lens = [100, 3000, 8191]
+    bsz, cap, d = len(lens), 8192, 128
+    k = torch.randn((bsz, 2, cap, d), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((bsz, 2, cap, d), generator=g, device="cuda").to(torch.bfloat16)
+    q = torch.randn((bsz, 32, d), generator=g, device="cuda").to(torch.bfloat16)
+    seqlens = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    plan = PL.DecodePlan(bsz, max(lens), 32, 2, d, torch.bfloat16, p)
+    out2, lse2 = torch.empty_like(plan.out), torch.empty_like(plan.lse)
+    B.infllmv2_sparse_attn_decode(q, k, v, seqlens, max(lens), None, plan.out, plan.lse,
+                                  plan.ws, p)
+    B.infllmv2_sparse_attn_decode_topk(q, k, v, seqlens, max(lens), None, None, out2, lse2,
+                                       plan.ws, p)
+    torch.cuda.synchronize()
+    _same(out2, plan.out, "decode out")
+    _same(lse2, plan.lse, "decode lse")
+    T, n_ctx = 7, 5000
+    kc = torch.randn((2, n_ctx, d), generator=g, device="cuda").to(torch.bfloat16)
+    vc = torch.randn((2, n_ctx, d), generator=g, device="cuda").to(torch.bfloat16)
+    kd = torch.randn((2, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    vd = torch.randn((2, T, d), generator=g, device="cuda").to(torch.bfloat16)
+    qt = torch.randn((T, 32, d), generator=g, device="cuda").to(torch.bfloat16)
+    mask = torch.tensor([(1 << (i + 1)) - 1 for i in range(T)], dtype=torch.int64,
+                        device="cuda")
+    tp = PL.TreePlan(T, n_ctx, 32, 2, d, torch.bfloat16, p)
+    assert tp.dense
+    out3, lse3 = torch.empty_like(tp.out), torch.empty_like(tp.lse)
+    B.infllmv2_tree_verify(qt, kc, vc, n_ctx, kd, vd, mask, None, tp.out, tp.lse, tp.ws, p)
+    B.infllmv2_tree_verify_topk(qt, kc, vc, n_ctx, kd, vd, mask, None, None, out3, lse3,
+                                tp.ws, p)
+    torch.cuda.synchronize()
+    _same(out3, tp.out, "tree out")
+    _same(lse3, tp.lse, "tree lse")
