@@ -217,12 +217,15 @@ def test_backward_block192(B):
     compare(B, c, sel, "block192")
 
 
-def test_backward_whole_prompt_in_chunks(B):
+@pytest.mark.parametrize("overlap", [False, True])
+def test_backward_whole_prompt_in_chunks(B, overlap):
     """A 2500-token prompt run forward and backward in chunks of 1000 (the
     first chunk dense, the others sparse): every chunk adds its dk/dv into the
     same buffers, and the result equals the oracle's backward of the whole
-    prompt with each row's selection as the forward made it."""
-    _say("chunked backward: 2500 tokens in chunks of 1000, dense_len 1500")
+    prompt with each row's selection as the forward made it.  overlap: the
+    forward's two-stream schedule (selections under the previous chunk's
+    attention) with every chunk's selection kept."""
+    _say(f"chunked backward: 2500 tokens in chunks of 1000, dense_len 1500, overlap={overlap}")
     from block_sparse_long_infllmv2_amd import pipeline as PL
     p = Params(topk=8, dense_len=1500)
     n, chunk, h_q, h_kv, d = 2500, 1000, 16, 1, 64
@@ -231,7 +234,8 @@ def test_backward_whole_prompt_in_chunks(B):
     q, k, v = dev(c.q), dev(c.k), dev(c.v)
     nc = O.num_windows(n, p.kernel_size, p.kernel_stride)
     ck = torch.zeros((h_kv, nc, d), dtype=torch.bfloat16, device="cuda")
-    cp = PL.ChunkedPrefill(n, chunk, h_q, h_kv, d, torch.bfloat16, p, keep_selections=True)
+    cp = PL.ChunkedPrefill(n, chunk, h_q, h_kv, d, torch.bfloat16, p, keep_selections=True,
+                           overlap=overlap)
     cp.run(q, k, v, ck)
     d_out = make_upstream_grad(71, n, h_q, d, "bf16")
     dq = torch.empty_like(q)
