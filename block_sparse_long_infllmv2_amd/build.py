@@ -77,12 +77,23 @@ def build_probes(hipcc: str) -> list:
     return out
 
 
+def _check_loads(path: str) -> None:
+    """Resolve every symbol of the built library now, in a child process (no
+    GPU is touched): a kernel whose host-side launch stub was not emitted
+    links, but leaves an undefined symbol that only loading reveals."""
+    code = "import ctypes, os, sys; ctypes.CDLL(sys.argv[1], mode=os.RTLD_NOW)"
+    r = subprocess.run([sys.executable, "-c", code, path], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"{path} does not load:\n{r.stderr.strip().splitlines()[-1]}")
+
+
 def _link(objs: list, lib: str, hipcc: str) -> None:
     tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    _check_loads(tmp)
     os.replace(tmp, lib)
 
 
