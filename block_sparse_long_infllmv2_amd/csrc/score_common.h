@@ -43,14 +43,14 @@ __device__ __forceinline__ int64_t last_window_of_block(int64_t b, int B, int s)
 
 // Blocks per workgroup of the streaming scorer: as many as keep a chunk's
 // windows within the LDS buffer (a chunk of n blocks spans at most
-// (n*B + ks - 2)/s + 2 windows), at most 32, and for few rows as few as
+// (n*B + ks - 2)/s + 2 windows), at most 64, and for few rows as few as
 // still give about kScoreMinWgs workgroups (a decode row alone would
 // otherwise leave most CUs without loads to issue), but at least
 // kScoreMinBlocks.  0 if not even one block fits.
 inline int stream_blocks_per_wg(int B, int ks, int s, int64_t nb_launch, int64_t rows,
                                 int h_kv) {
   int bpw = (int)(((int64_t)(kScoreMaxWindows - 2) * s - ks + 2) / B);
-  if (bpw > 32) bpw = 32;
+  if (bpw > 64) bpw = 64;
   if (bpw < 1) return 0;
   const int64_t spread = (nb_launch * rows * h_kv + kScoreMinWgs - 1) / kScoreMinWgs;
   const int64_t want = spread < kScoreMinBlocks ? kScoreMinBlocks : spread;
