@@ -12,9 +12,11 @@
 namespace infllmv2 {
 
 // ---------------------------------------------------------------------------
-// One wave per (row, KV head) when the eligible blocks fit in registers
+// One wave selects one (row, KV head) whose eligible blocks fit in registers
 // (64 * KPL of them): lane l holds the scores of blocks b = l + 64 j
-// (coalesced loads; ascending block order is (j, lane) order).
+// (coalesced loads; ascending block order is (j, lane) order).  The top-k
+// kernel runs four such waves per workgroup; the selecting decode kernels run
+// it in each split's wave before its copies start.
 //   1. Non-candidates (forced blocks, blocks past the row) become NaN, which
 //      no comparison admits; only the 64-block pieces that reach them are
 //      touched.
