@@ -1090,14 +1090,40 @@ struct Row16 {
   // (4: a 64-key chunk, 2: a 32-key half) give NKT / 2 B operands.
   template <int NKT>
   struct PFragN { bf16x8 f[NKT / 2]; };
+  template <bool SKIP = true>
   __device__ __forceinline__ PFrag softmax(f32x4 (&s)[4], bool keep, float scale_log2) {
-    const PFragN<4> r = softmax_n<4>(s, keep, scale_log2);
+    const PFragN<4> r = softmax_n<4, SKIP>(s, keep, scale_log2);
     PFrag pf;
     pf.f[0] = r.f[0];
     pf.f[1] = r.f[1];
     return pf;
   }
+  // maximum over a row's four lanes: its other 48 keys sit in lanes j + 16,
+  // j + 32, j + 48
+  __device__ __forceinline__ static float row_max(float mx) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                      false, false);
+    return fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  }
   template <int NKT>
+  __device__ __forceinline__ PFragN<NKT> pack(const f32x4 (&s)[NKT]) const {
+    PFragN<NKT> pf;
+#pragma unroll
+    for (int sidx = 0; sidx < NKT / 2; ++sidx)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pf.f[sidx][e] = (__bf16)s[2 * sidx + (e >> 2)][e & 3];
+    return pf;
+  }
+  // SKIP: the row maximum is only formed when some lane's own maximum clears
+  // the slack.  Otherwise no row's maximum does, so every row keeps m with
+  // alpha = 1 and O untouched, exactly what the full step gives, and the
+  // cross-lane reduction and the rescale exponential are saved.  That pays
+  // on most chunks of the prefill loops; the decode loop, bound by latency,
+  // is faster with the straight-line step (SKIP = false).
+  template <int NKT, bool SKIP = true>
   __device__ __forceinline__ PFragN<NKT> softmax_n(f32x4 (&s)[NKT], bool keep,
                                                    float scale_log2) {
     float mx = -INFINITY;
@@ -1106,37 +1132,51 @@ struct Row16 {
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = keep ? mx * scale_log2 : -INFINITY;
-    // the row's other 48 keys sit in lanes j + 16, j + 32, j + 48
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                      false, false);
-    mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                      false, false);
-    mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
-    const float m_new = mx > m + kRescaleSlack ? mx : m;
-    const float alpha = fast_exp2(m - m_new);
-    const float msub = keep ? m_new : INFINITY;
-    float psum = 0.0f;
+    if constexpr (SKIP) {
+      float alpha = 1.0f;
+      if (__ballot(mx > m + kRescaleSlack)) {
+        mx = row_max(mx);
+        const float m_new = mx > m + kRescaleSlack ? mx : m;
+        alpha = fast_exp2(m - m_new);
+        m = m_new;
+        if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int kt = 0; kt < NKT; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -msub));
-        s[kt][r] = p;
-        psum += p;
+          for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+        }
       }
-    m = m_new;
-    l = l * alpha + psum;
-    if (__ballot(alpha != 1.0f)) {
+      const float msub = keep ? m : INFINITY;
+      float psum = 0.0f;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -msub));
+          s[kt][r] = p;
+          psum += p;
+        }
+      l = l * alpha + psum;
+    } else {
+      mx = row_max(mx);
+      const float m_new = mx > m + kRescaleSlack ? mx : m;
+      const float alpha = fast_exp2(m - m_new);
+      const float msub = keep ? m_new : INFINITY;
+      float psum = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -msub));
+          s[kt][r] = p;
+          psum += p;
+        }
+      m = m_new;
+      l = l * alpha + psum;
+      if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] *= alpha;
+      }
     }
-    PFragN<NKT> pf;
-#pragma unroll
-    for (int sidx = 0; sidx < NKT / 2; ++sidx)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pf.f[sidx][e] = (__bf16)s[2 * sidx + (e >> 2)][e & 3];
-    return pf;
+    return pack(s);
   }
 
   // O^T += V^T P^T for the tile at vb; k-step outer, d-tile inner
@@ -1698,7 +1738,7 @@ __global__ __launch_bounds__(64) void attn16_decode_kernel(AttnArgs a) {
       st.qk(lds0 + S * TILE, sc);
       if (isd) st.mask_bits(sc, dbits);
       else if (lim < kChunk - 1) st.mask(sc, lim);
-      const typename Row16<D>::PFrag pf = st.softmax(sc, true, a.scale_log2);
+      const typename Row16<D>::PFrag pf = st.template softmax<false>(sc, true, a.scale_log2);
       st.pv(lds0 + (NS + S) * TILE, pf);
     }
     if (i + 2 < n) {
