@@ -1145,14 +1145,14 @@ struct Row16 {
         }
       }
       const float msub = keep ? m : INFINITY;
-      float psum = 0.0f;
+      float psum;
 #pragma unroll
       for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const float p = fast_exp2(__builtin_fmaf(s[kt][r], scale_log2, -msub));
           s[kt][r] = p;
-          psum += p;
+          psum = kt == 0 && r == 0 ? p : psum + p;   // p >= 0: the same sum as from 0
         }
       l = l * alpha + psum;
     } else {
@@ -1266,9 +1266,11 @@ void attn16_prefill_kernel(AttnArgs a) {
   const uint32_t full_mask = n_tok >= 32 ? 0xffffffffu : ((1u << n_tok) - 1u);
   const int p0 = (int)a.n_k - a.n_rows + tok0;   // query position of the tile's first token
 
-  // this wave's tokens: TPW consecutive ones
+  // this wave's tokens: TPW consecutive ones (a scalar, so the per-chunk
+  // token tests stay on the scalar unit)
   const int my_head = g * G + (lane & 15);
-  auto tok_of = [&](int j) { return wave * TPW + j; };
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto tok_of = [&](int j) { return wave_u * TPW + j; };
 
   int n_entries;
   if (dense) {
@@ -1382,7 +1384,6 @@ void attn16_prefill_kernel(AttnArgs a) {
   DTV dmav;
   dmak.init(tid);
   dmav.init(tid);
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)stage;
   // Chunk i sits in slot i % NS: K at lds0 + slot TILE, V at lds0 + (NS + slot) TILE.
   // Iteration i: barrier (chunk i landed, iteration i-1 done everywhere, so
