@@ -335,7 +335,8 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // ---- this wave's 16 KT keys of K and V as B operands (key j of tile kt in
   // lane column j, dims 32 ks + 8 h .. +8); keys past n_k repeat the last key
   const int jj = lane & 15, hh = lane >> 4;
-  const int kw0 = key0 + 16 * KT * wave;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);   // the wave index as a scalar
+  const int kw0 = key0 + 16 * KT * wave_u;
   bf16x8 kf[KT][NKS], vf[KT][NKS];
 #pragma unroll
   for (int kt = 0; kt < KT; ++kt) {
@@ -365,7 +366,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // repeat its last pair (finite data, masked by position).  Byte offsets
   // are 32-bit: the host keeps n_q * h_q * D * 2 below 4 GiB.
   const uint32_t ring0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)ring;
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // (row * h_q + head) of pair p (clamped to the segment), 32-bit: the host
   // keeps n_q * h_q * D * 2 below 4 GiB
   const uint32_t n_pairs_u = (uint32_t)n_pairs, hq_u = (uint32_t)a.h_q, hg = (uint32_t)(g * G);
@@ -383,21 +383,33 @@ void bwd_dkdv_kernel(BwdArgs a) {
     cp_r[i] = (uint32_t)r;
     cp_c16[i] = (uint32_t)(16 * (pc ^ PT::f(r)));
   }
-  // With G >= 16 (and kPbase) a tile's 32 pairs lie in 32 / G rows: both
-  // row bases are read once per tile and each copy picks its own; pairs past
-  // the segment take the last row (finite data, masked by position).
+  // With G >= 16 (and kPbase) a tile's 32 pairs lie in 32 / G <= 2 rows: both
+  // row bases are read once per tile into scalars.  A copy instruction
+  // covers 64 / CPR consecutive pair rows, all of one row (G is a multiple
+  // of that count), so each copy takes its row base as a scalar and adds a
+  // tile-independent per-lane part (its pair's head and chunk).  The meta
+  // copy's lanes span both rows: they add the scalar distance between the
+  // bases under a per-lane mask.  Pairs past the segment take the last row
+  // (finite data, masked by position).
+  constexpr bool kTwoRows = kPbase && G >= 16;
+  static_assert(!kTwoRows || (32 / G <= 2 && G % (64 / PT::CPR) == 0),
+                "a tile spans at most two rows; a copy stays in one");
+  uint32_t cp_fix[RG::PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < RG::PER_WAVE; ++i) cp_fix[i] = (cp_r[i] % G) * (uint32_t)(2 * D) + cp_c16[i];
+  const uint32_t m_pair = (uint32_t)(lane >> 1);
+  const uint32_t m_fix = (m_pair % G) * 8u + 4u * (uint32_t)(lane & 1);
+  const uint32_t m_hi = m_pair / G != 0u ? ~0u : 0u;
   auto issue = [&](int t, int slot) {
     const uint32_t p0 = (uint32_t)t * 32u;
-    uint32_t pb[G >= 16 ? 32 / G : 1];
-    if constexpr (kPbase && G >= 16) {
+    uint32_t b0 = 0u, b1 = 0u;
+    if constexpr (kTwoRows) {
       const int row0 = (int)(p0 / G), last = max(n_rows - 1, 0);
-#pragma unroll
-      for (int k = 0; k < 32 / G; ++k) pb[k] = pbase_lds[min(row0 + k, last)];
+      b0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)pbase_lds[min(row0, last)]);
+      b1 = 32 / G > 1
+               ? (uint32_t)__builtin_amdgcn_readfirstlane((int)pbase_lds[min(row0 + 1, last)])
+               : b0;
     }
-    auto index_of = [&](uint32_t r) -> uint32_t {   // pair p0 + r
-      if constexpr (kPbase && G >= 16) return pb[r / G] + r % G;
-      else return pair_index(p0 + r);
-    };
 #pragma unroll
     for (int i = 0; i < RG::PER_WAVE; ++i) {
       const int j = wave_u * RG::PER_WAVE + i;              // copy index in the tile
@@ -406,10 +418,19 @@ void bwd_dkdv_kernel(BwdArgs a) {
       const bool is_q = j < kPerTensor;
       const uint32_t dst = ring0 + (uint32_t)(is_q ? RG::q(slot) + j * 1024
                                                    : RG::o(slot) + (j - kPerTensor) * 1024);
-      const uint32_t voff = index_of(cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
+      uint32_t voff;
+      if constexpr (kTwoRows) {
+        const bool second = ((j * (64 / PT::CPR)) % 32) / G != 0;   // the same in every lane
+        voff = (second ? b1 : b0) * (uint32_t)(2 * D) + cp_fix[i];
+      } else
+        voff = pair_index(p0 + cp_r[i]) * (uint32_t)(2 * D) + cp_c16[i];
       lds_dma16(dst, is_q ? (const void*)a.q : (const void*)a.d_out, voff);
     }
-    const uint32_t moff = index_of((uint32_t)(lane >> 1)) * 8u + 4u * (uint32_t)(lane & 1);
+    uint32_t moff;
+    if constexpr (kTwoRows)
+      moff = b0 * 8u + (m_hi & ((b1 - b0) * 8u)) + m_fix;
+    else
+      moff = pair_index(p0 + m_pair) * 8u + 4u * (uint32_t)(lane & 1);
     lds_dma4(ring0 + (uint32_t)RG::meta(slot, wave_u), a.meta, moff);
   };
 
@@ -561,7 +582,9 @@ void bwd_dq_kernel(BwdArgs a) {
   constexpr int TILE = SW::TILE;
   constexpr int RB = SW::RB;
   constexpr int SORT_N = TT * kSortCap;
-  __shared__ __attribute__((aligned(16))) uint16_t stage[2 * 2 * TILE / 2];   // K[2] V[2]
+  // 256-byte aligned: the fragment addresses below XOR bits 5..7 of ring
+  // addresses (slot bases are multiples of 256)
+  __shared__ __attribute__((aligned(256))) uint16_t stage[2 * 2 * TILE / 2];   // K[2] V[2]
   __shared__ int2 ents[TT * kSortCap];
   __shared__ int scan_lds[NT / 64];
   static_assert(SORT_N * 4 <= (int)sizeof(stage), "sort buffer aliases the staging ring");
@@ -650,12 +673,21 @@ void bwd_dq_kernel(BwdArgs a) {
     dma.issue(lds0 + slot * TILE, kseq + off, un.nv, tid, wave_u);
     dma.issue(lds0 + (2 + slot) * TILE, vseq + off, un.nv, tid, wave_u);
   };
-  // fragment addresses: 16-byte reads, row 16 kt + jj, chunk 4 ks + hh
+  // Fragment addresses.  The swizzle of a row reads only its low four bits,
+  // so rows 16 m + jj share row jj's (16 m RB is an immediate offset), and
+  // the chunk index enters as an XOR: 16-byte row reads (row 16 kt + jj,
+  // chunk 4 ks + hh) are the k-step-0 offset XOR 64 ks; transposing reads
+  // (row 32 sidx + 4 hh + jj / 4, chunk 2 dt + (jj % 4) / 2, half jj % 2)
+  // are the d-tile-0 offset XOR 32 dt.  Slot bases are multiples of 256, so
+  // the XORs hold on the absolute addresses too: one XOR per k-step or d-tile
+  // and chunk, every row and slot offset an immediate.
   auto row_addr = [&](int r, int c) -> uint32_t {
     return (uint32_t)(r * RB + ((c ^ SW::f(r)) * 16));
   };
-
+  static_assert(TILE % 256 == 0, "slot bases keep bits 0..7");
   const int tr_row = 4 * hh + (jj >> 2), tr_q = jj & 3;
+  const uint32_t rd0 = row_addr(jj, hh);
+  const uint32_t tr0 = row_addr(tr_row, tr_q >> 1) + 8u * (uint32_t)(tr_q & 1);
 
   Unit cur = unit_of(0);
   if (n > 0) issue(cur, 0);
@@ -665,7 +697,8 @@ void bwd_dq_kernel(BwdArgs a) {
     const Unit nxt = unit_of(i + 1);
     if (i + 1 < n) issue(nxt, slot ^ 1);
     if (cur.tm & wave_tok_mask) {
-      const uint32_t kb = lds0 + slot * TILE, vb = lds0 + (2 + slot) * TILE;
+      const uint32_t kb = lds0 + slot * TILE;
+      const uint32_t krd = kb + rd0, ktr = kb + tr0;
       int lim = -1;
       if (my_ok && ((cur.tm >> my_t) & 1u)) lim = min(p0 + my_t - cur.key0, cur.nv - 1);
       // per 32-key half sidx: S^T, dP^T of its two key tiles, then dS^T as
@@ -683,11 +716,11 @@ void bwd_dq_kernel(BwdArgs a) {
         for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
           for (int t2 = 0; t2 < 2; ++t2) {
-            const uint32_t ra = row_addr(16 * (2 * sidx + t2) + jj, 4 * ks + hh);
-            s[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(kb + ra), qf[ks], s[t2],
+            const uint32_t ra = (krd ^ (uint32_t)(64 * ks)) + (uint32_t)(16 * (2 * sidx + t2) * RB);
+            s[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(ra), qf[ks], s[t2],
                                                             0, 0, 0);
-            dp[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(vb + ra), of[ks], dp[t2],
-                                                             0, 0, 0);
+            dp[t2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_read16(ra + 2 * TILE), of[ks],
+                                                             dp[t2], 0, 0, 0);
           }
         // lane (jj, hh): pair jj, keys 16 kt + 4 hh + r
         bf16x8 sb;
@@ -703,9 +736,9 @@ void bwd_dq_kernel(BwdArgs a) {
           }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const uint32_t base = row_addr(32 * sidx + tr_row, 2 * dt + (tr_q >> 1)) + 8u * (tr_q & 1);
-          const bf16x4 lo = lds_read_tr8(kb + base);
-          const bf16x4 hi = lds_read_tr8(kb + base + 16u * RB);
+          const uint32_t base = (ktr ^ (uint32_t)(32 * dt)) + (uint32_t)(32 * sidx * RB);
+          const bf16x4 lo = lds_read_tr8(base);
+          const bf16x4 hi = lds_read_tr8(base + 16u * RB);
           const bf16x8 ak = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           dq[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ak, sb, dq[dt], 0, 0, 0);
         }
