@@ -137,6 +137,14 @@ constexpr int kMfmaWaves = 8;            // waves per workgroup, splitting the w
 constexpr int kStageBlocks = 32;
 constexpr int kStageStride = kStageBlocks + 4;   // floats per staged row (16-byte pad)
 
+// Maximum of two window scores for the pooling.  Scores are finite or -inf
+// (windows past a row), so the NaN-propagating maximum gives what fmaxf
+// gives; it is issued as v_maximum3_f32 with no canonicalising v_max of each
+// operand, which fmaxf's NaN-ignoring semantics need on matrix-core results.
+__device__ __forceinline__ float pool_max(float x, float y) {
+  return __builtin_elementwise_maximum(x, y);
+}
+
 // WPB = windows per block (B / s): 4 or 8.
 template <int D, int WPB>
 __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(ScoreArgs a, int n_row_tiles) {
@@ -264,7 +272,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
   // the halo of a tile's first block is the previous tile's last window,
   // carried in registers (computed directly only for the range's first tile)
   const int per_wave = (n_tiles + kMfmaWaves - 1) / kMfmaWaves;
-  const int t_begin = wave * per_wave;
+  const int t_begin = __builtin_amdgcn_readfirstlane(wave) * per_wave;   // a scalar tile loop
   const int t_end = min(n_tiles, t_begin + per_wave);
   float carry[RG];
 #pragma unroll
@@ -348,8 +356,8 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
       if (full_vis) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          own[q] = fmaxf(fmaxf(acc[rg][4 * q], acc[rg][4 * q + 1]),
-                         fmaxf(acc[rg][4 * q + 2], acc[rg][4 * q + 3]));
+          own[q] = pool_max(pool_max(acc[rg][4 * q], acc[rg][4 * q + 1]),
+                         pool_max(acc[rg][4 * q + 2], acc[rg][4 * q + 3]));
           last[q] = acc[rg][4 * q + 3];
         }
       } else {
@@ -360,7 +368,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
           for (int e = 0; e < 4; ++e) {
             const int m = mt + 8 * q + 4 * half + e;
             const float x = m < n_vis[rg] ? acc[rg][4 * q + e] : -INFINITY;
-            mx = fmaxf(mx, x);
+            mx = pool_max(mx, x);
             if (e == 3) last[q] = x;
           }
           own[q] = mx;
@@ -377,7 +385,7 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const float halo = half ? other[q] : (q > 0 ? other[q - 1] : carry[rg]);
-          bs[q] = fmaxf(own[q], halo);
+          bs[q] = pool_max(own[q], halo);
         }
         carry[rg] = other[3];     // for half-0 lanes: last window of block 7
         // regroup: half 0 -> blocks 0..3 of the tile, half 1 -> 4..7
@@ -396,9 +404,9 @@ __global__ __launch_bounds__(kMfmaWaves * 64) void block_scores_mfma_kernel(Scor
         float bs[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float both = fmaxf(own[q], swap_halves(own[q]));
+          const float both = pool_max(own[q], swap_halves(own[q]));
           const float halo = q > 0 ? (half ? last[q - 1] : other[q - 1]) : carry[rg];
-          bs[q] = fmaxf(both, halo);
+          bs[q] = pool_max(both, halo);
         }
         carry[rg] = half ? last[3] : other[3];     // window 31 of the tile
         if (half == 0) {
