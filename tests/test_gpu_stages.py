@@ -279,6 +279,29 @@ def test_prefill_bf16_block128(B, PL):
     _check_prefill(plan, ck, c, rows=list(range(0, 120, 4)) + [119])
 
 
+@pytest.mark.parametrize("bs,topk,rising", [
+    (64, 32, True),      # the ring loop; later blocks score up to 16x higher
+    (64, 32, False),     # the first blocks score highest: the running max never moves
+    (128, 6, True),      # small top-k: ring and each token's own pass
+])
+def test_prefill_running_max_moves(B, PL, bs, topk, rising):
+    """Keys scaled by powers of two per fifth of the context (exact in bf16),
+    so that the kept blocks' scores rise by more than the softmax's rescale
+    slack several times along a row (or only fall): the loop's full step
+    with the row maximum and the O rescale, and its step that keeps the
+    running maximum, both against the oracle."""
+    _say(f"prefill bf16 running max moves: block={bs} topk={topk} rising={rising}")
+    p = Params(block_size=bs, topk=topk, dense_len=0)
+    n_k, n_q = 4096, 100
+    c = make_prefill(23, n_k=n_k, n_q=n_q, h_q=32, h_kv=2, d=128, params=p, dtype="bf16",
+                     n_planted=2, alpha=1.5, beta=1.5)
+    level = np.minimum(np.arange(n_k) * 5 // n_k, 4)
+    f = 2.0 ** (level if rising else 4 - level)
+    c.k *= f[None, :, None]
+    plan, ck = _run_prefill(B, PL, c)
+    _check_prefill(plan, ck, c, rows=sorted(set(list(range(0, n_q, 3)) + [n_q - 1])))
+
+
 @pytest.mark.parametrize("bs,n_k,n_q,h_q,h_kv,d,topk,dtype", [
     (96, 5000, 150, 32, 2, 128, 8, "bf16"),   # 16-head groups; last block 8 keys
     (96, 3030, 100, 8, 2, 64, 8, "bf16"),     # G = 4 (32-row tiles); last block 54 keys
