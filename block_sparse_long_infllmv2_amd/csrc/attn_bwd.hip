@@ -545,21 +545,48 @@ void bwd_dkdv_kernel(BwdArgs a) {
     if (t + 3 < n_tiles) step(t + 3, StageTag<3>());
   }
 
-  // ---- accumulate: lane (jj, hh) holds key 16 kt + jj, d = 16 dt + 4 hh + r
+  // ---- accumulate.  Lane (jj, hh) holds key 16 kt + jj, d = 16 dt + 4 hh + r:
+  // added as they are, an atomic instruction would touch 16 lines with 4
+  // scattered floats each.  The wave's tile goes through LDS instead (the
+  // ring is free once every wave has left the tile loop), so that each
+  // atomic instruction covers whole 64-byte lines: 16 lanes per key row,
+  // 4 rows per instruction.  dK, then dV, through the same staging, whose
+  // rows are padded to D + 16 floats so the 4 rows of a read fall in
+  // disjoint banks.  LDS operations of one wave complete in order.
+  constexpr int kRowF = D + 16;
+  static_assert(NW * 16 * KT * kRowF * 4 <= RG::BYTES, "the staging fits in the ring");
+  __syncthreads();
+  float* stg = reinterpret_cast<float*>(ring) + wave_u * (16 * KT * kRowF);
+  auto put = [&](const f32x4 (&acc)[KT][NDT], float mul) {
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt) {
-    const int key = key_lane[kt];
-    if (key >= a.n_k) continue;
-    float* dkr = a.dk + ((int64_t)g * a.cap + key) * D + 4 * hh;
-    float* dvr = a.dv + ((int64_t)g * a.cap + key) * D + 4 * hh;
+    for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4*>(&stg[(16 * kt + jj) * kRowF + 16 * dt + 4 * hh]) =
+            acc[kt][dt] * mul;
+    __builtin_amdgcn_wave_barrier();
+  };
+  auto add_to = [&](float* dst) {
+    const int rl = lane >> 4, dl = lane & 15;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        unsafeAtomicAdd(dkr + 16 * dt + r, a.scale * dk[kt][dt][r]);
-        unsafeAtomicAdd(dvr + 16 * dt + r, dv[kt][dt][r]);
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = 16 * kt + 4 * it + rl;
+        const int key = kw0 + row;
+        float* o = dst + ((int64_t)g * a.cap + (key < a.n_k ? key : 0)) * D + dl;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) {
+          const float x = stg[row * kRowF + 16 * i + dl];
+          if (key < a.n_k) unsafeAtomicAdd(o + 16 * i, x);
+        }
       }
-  }
+    __builtin_amdgcn_wave_barrier();
+  };
+  put(dk, a.scale);
+  add_to(a.dk);
+  put(dv, 1.0f);
+  add_to(a.dv);
 }
 
 // ---------------------------------------------------------------------------
