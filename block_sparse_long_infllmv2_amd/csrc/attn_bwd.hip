@@ -78,8 +78,10 @@ struct BwdArgs {
 // with the item count; smaller items balance better.  Measured on the 128K
 // chunk (MI355X), first kernel: dK/dV 2.49 / 2.17 / 2.40 / 2.55 ms at 2048 /
 // 4096 / 8192 / 16384 pairs; current kernel (rocprofv3 means, one box): 1.79 /
-// 1.69 / 1.71 / 1.76 ms at 4096 / 5120 / 6144 / 7168 pairs.  Rows per item
-// are capped so the row list stays at 8 KB of LDS.
+// 1.69 / 1.71 / 1.76 ms at 4096 / 5120 / 6144 / 7168 pairs; with whole-line
+// atomics, 3072 / 4096 / 6144 pairs stayed within the run-to-run spread of
+// 5120 (backward call 2.54-2.86 ms on one box).  Rows per item are capped so
+// the row list stays at 8 KB of LDS.
 constexpr int kSegPairs = 5120;
 constexpr int kMaxSegRows = 2048;
 __host__ __device__ constexpr int seg_rows_for(int G) {
